@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the RVQ hot path on one MI355X.
+
+One step = the whole path on one ragged batch of native-resolution image
+features (16 images, H and W in patches uniform on 14..84, D=1152 bf16,
+L=8 levels of K=8192 fp32 codewords):
+  codebook preparation -> multi-level encode -> decode to bf16 ->
+  per-level usage counts and mean squared residual.
+Inputs are resident in HBM before the timed region.  `value` is encoded
+vectors per second for the whole step.  The distance kernel (the dense
+contraction with its top-2 epilogue) is timed per launch with HIP events
+recorded on the library's stream, and reported against the bf16 MFMA peak.
+The fp64 oracle is timed on the host's cores on a bounded row sample.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RVQ-encoded vectors/sec (all levels) at D=1152,K=8192,L=8; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+class HipEvents:
+    """hipEvent_t pairs via the HIP runtime (the library records them)."""
+
+    def __init__(self, count: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * count)()
+        for i in range(count):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.ev[i] = h
+
+    def slice(self, start: int, count: int):
+        return (ctypes.c_void_p * count).from_address(ctypes.addressof(self.ev) + start * ctypes.sizeof(ctypes.c_void_p))
+
+    def record(self, i: int, stream) -> None:
+        rc = self.hip.hipEventRecord(self.ev[i], stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(out.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def cpu_baseline(w, target_s: float = 15.0) -> dict:
+    """The fp64 oracle (encode + decode + counts + msr) on a seeded row sample."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    env_threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, env_threads) if env_threads > 0 else cores
+    rng = np.random.default_rng(12345)
+
+    def run(rows):
+        sub = w.rows(np.sort(rng.choice(w.N, rows, replace=False)))
+        t0 = time.perf_counter()
+        ref = oracle.encode(sub.x, sub.codebooks, x_dtype=sub.x_dtype, threads=threads)
+        oracle.decode(ref["ids"], sub.codebooks, threads=threads)
+        oracle.hist(ref["ids"], sub.K)
+        oracle.msr(sub.x, ref["ids"], sub.codebooks, x_dtype=sub.x_dtype, threads=threads)
+        return time.perf_counter() - t0
+
+    probe_rows = threads
+    t_probe = run(probe_rows)
+    rows = int(max(threads, min(4096, probe_rows * target_s / max(t_probe, 1e-3))))
+    rows = max(threads, rows // threads * threads)
+    t = run(rows)
+    return {"value": rows / t, "unit": "vectors/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} seeded rows of the {w.N}-row native-resolution batch "
+                      f"(D={w.D}, K={w.K}, L={w.L}); fp64 encode+decode+counts+msr, {t:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the RVQ path runs on a single MI355X and has no "
+              "multi-GPU mode (rows would shard independently; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import residual_vector_quantization_rvq_amd as rvq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.native_batch()
+    N, D, L, K = w.N, w.D, w.L, w.K
+    x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prepared = torch.empty(rvq.rvq_prepared_size(L, K, D), dtype=torch.uint8, device=dev)
+    ws = torch.empty(rvq.rvq_encode_workspace_size(N, D, L, K), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(rvq.rvq_level_stats_workspace_size(N, L, K, D, True), dtype=torch.uint8,
+                      device=dev)
+    ids = torch.empty((N, L), dtype=torch.int32, device=dev)
+    out = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    total_steps = args.warmup + args.steps
+    per_step = 2 * L + 5
+    ev = HipEvents(per_step * total_steps)
+
+    def step(k: int):
+        base = k * per_step
+        m = base + 2 * L
+        ev.record(m, sptr)
+        rvq.rvq_prepare_codebooks(cb, out=prepared)
+        ev.record(m + 1, sptr)
+        rvq.rvq_encode(x, cb, prepared, workspace=ws, ids_out=ids, events=ev.slice(base, 2 * L))
+        ev.record(m + 2, sptr)
+        rvq.rvq_decode(ids, cb, torch.bfloat16, out=out)
+        ev.record(m + 3, sptr)
+        rvq.rvq_level_stats(ids, K, x, cb, workspace=ws2)
+        ev.record(m + 4, sptr)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(args.warmup, total_steps):
+        step(k)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    dist_ms, prep_ms, enc_ms, dec_ms, st_ms = [], [], [], [], []
+    for k in range(args.warmup, total_steps):
+        b = k * per_step
+        m = b + 2 * L
+        dist_ms += [ev.elapsed_ms(b + 2 * l, b + 2 * l + 1) for l in range(L)]
+        prep_ms.append(ev.elapsed_ms(m, m + 1))
+        enc_ms.append(ev.elapsed_ms(m + 1, m + 2))
+        dec_ms.append(ev.elapsed_ms(m + 2, m + 3))
+        st_ms.append(ev.elapsed_ms(m + 3, m + 4))
+    ev.close()
+    dist_avg = float(np.mean(dist_ms))
+    flops_per_launch = 2.0 * N * K * D
+    achieved = flops_per_launch / (dist_avg * 1e-3) / 1e12
+    value = N / (ms_per_step * 1e-3)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "native_batch", "images": 16, "N": N, "D": D, "K": K, "L": L,
+                   "x_dtype": "bf16", "codebooks": "fp32",
+                   "step": "prepare+encode+decode(bf16)+level_stats(counts+msr)"},
+        "roofline": {"bound": "mfma", "kernel": "distance_top2_kernel",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "launch_ms": round(dist_avg, 4),
+                     "flops_per_launch": flops_per_launch},
+        "mfma_pct": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "prepare_ms": round(float(np.median(prep_ms)), 4),
+        "encode_ms": round(float(np.median(enc_ms)), 4),
+        "encode_vectors_per_s": round(N / (float(np.median(enc_ms)) * 1e-3), 1),
+        "decode_ms": round(float(np.median(dec_ms)), 4),
+        "level_stats_ms": round(float(np.median(st_ms)), 4),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

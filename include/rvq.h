@@ -1,0 +1,188 @@
+/*
+ * rvq.h -- C ABI of the MI355X (gfx950) residual vector quantization library.
+ *
+ * What the library computes.  Visual feature vectors become multi-level
+ * discrete token IDs by residual vector quantization (RVQ): at each level
+ * the nearest codeword of that level's codebook is chosen, its index is
+ * recorded, and it is subtracted so the residual passes on to the next
+ * level ("LongCat-2.5 Native Multimodality for Agentic Tasks", section
+ * "Visual Primitive Modeling", paragraph "Discrete Native Resolution Vision
+ * Transformer"; "LongCat-2.5 Open Source Release ...", section "02 Visual
+ * Coding and 3D": detail is added level by level).  Token IDs are turned
+ * back into vectors by summing the chosen codewords (same blog, Figure 1:
+ * the token sequences are reconstructed).  The tokenizer is fixed and its
+ * IDs are precomputed offline (same blog, paragraph "Offline Visual
+ * Preprocessing"), so encoding here is a deterministic, batch-invariant
+ * function of (row, codebooks): a row's IDs do not depend on the other rows
+ * in the call or on its position.
+ *
+ * Readings taken where the pages are silent: the distance is the squared
+ * Euclidean distance; there is one [K][d] codebook per level; search is
+ * greedy level by level; exact ties go to the lowest codeword index.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers are device memory owned by the
+ *     caller (any allocator).  The library allocates no memory and keeps no
+ *     global mutable state; scratch memory is a caller-provided workspace.
+ *   - All arrays are dense and row-major.  Codebooks are [L][K][d] fp32;
+ *     token IDs are [n][L] int32 (level-minor); rows are [n][d].
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     Concurrent calls on different streams must use different workspaces.
+ *   - Arguments are validated on the host before any HIP call; a non-OK
+ *     status means nothing was enqueued, except RVQ_ERR_HIP, which reports
+ *     a failed launch (the stream may then hold part of the work).
+ *   - n == 0 is a valid no-op (outputs of size zero; hist and msr are still
+ *     written for level statistics).
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified
+ *     but every memory access stays in bounds.
+ */
+#ifndef RVQ_H
+#define RVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rvq_status {
+    RVQ_OK = 0,
+    RVQ_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misaligned pointer */
+    RVQ_ERR_UNSUPPORTED = 2,        /* valid request outside what this build supports */
+    RVQ_ERR_WORKSPACE_TOO_SMALL = 3,
+    RVQ_ERR_HIP = 4                 /* a HIP launch failed */
+} rvq_status;
+
+typedef enum rvq_dtype {
+    RVQ_F32 = 0,
+    RVQ_BF16 = 1
+} rvq_dtype;
+
+/* Static text for a status code. */
+const char *rvq_status_string(rvq_status s);
+
+/* Detail of the last non-OK status returned on the calling host thread
+ * (thread-local, overwritten by the next failing call). */
+const char *rvq_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Codebook preparation (once per fixed codebook set).
+ *
+ * The tokenizer is fixed ("Offline Visual Preprocessing"), so per-codeword
+ * data derived from the codebooks is computed once and reused by every
+ * encode call: the squared norms ||c||^2 in fp32 and a bf16 copy of the
+ * codewords in the layout the distance kernel reads.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of the prepared buffer for L levels of K codewords of dimension d. */
+rvq_status rvq_prepared_size(int32_t L, int32_t K, int32_t d, size_t *bytes);
+
+/*
+ * codebooks : device, [L][K][d] fp32, 16-byte aligned.
+ * prepared  : device, >= rvq_prepared_size bytes, 256-byte aligned; fully
+ *             overwritten.  Owned by the caller; pass it to rvq_encode with
+ *             the same codebooks, L, K and d (not checked: a buffer prepared
+ *             from other codebooks gives wrong IDs, never a fault).
+ */
+rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, int32_t d,
+                                 void *prepared, size_t prepared_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Encode: greedy multi-level nearest-codeword search with residual update.
+ *
+ * Per level l and row r: the squared distance ||r - c||^2 =
+ * ||r||^2 - 2 r.c + ||c||^2 is ranked over all K codewords by the score
+ * ||c||^2 - 2 r.c (||r||^2 is the same for every codeword), with the dot
+ * products taken on the matrix cores from bf16 copies of r and c with fp32
+ * accumulation; the two best-scoring codewords are then rescored exactly in
+ * fp32 as sum_i (r_i - c_i)^2 and the smaller wins (lower index on a tie).
+ * The chosen codeword is subtracted from the fp32 residual, which feeds the
+ * next level.
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes needed by rvq_encode for n rows. */
+rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K, size_t *bytes);
+
+/*
+ * x            : device, [n][d] rows in x_dtype (fp32 or bf16), 16-byte aligned.
+ * codebooks    : device, [L][K][d] fp32 (the exact values used for rescoring
+ *                and for the residual update), 16-byte aligned.
+ * prepared     : device, filled by rvq_prepare_codebooks for these codebooks.
+ * ids          : device, [n][L] int32 output; ids[row*L + l] in [0, K).
+ * residual_out : device, [n][d] fp32 output x - sum_l codebooks[l][ids[l]],
+ *                or NULL when not wanted.  16-byte aligned.
+ * workspace    : device, >= rvq_encode_workspace_size bytes, 256-byte
+ *                aligned; contents on entry are ignored.
+ */
+rvq_status rvq_encode(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
+                      const float *codebooks, const void *prepared, int32_t L, int32_t K,
+                      int32_t *ids, float *residual_out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Same as rvq_encode, and additionally records events[2*l] on `stream`
+ * immediately before and events[2*l + 1] immediately after the distance
+ * kernel of level l (the dense contraction with its top-2 epilogue), for
+ * l = 0..L-1.  `events` is a host array of 2*L events created by the caller
+ * (hipEventCreate); pass NULL to record nothing.  Used to time the distance
+ * stage alone without a profiler.
+ */
+rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
+                               const float *codebooks, const void *prepared, int32_t L, int32_t K,
+                               int32_t *ids, float *residual_out,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream,
+                               hipEvent_t *events);
+
+/* ------------------------------------------------------------------------
+ * Decode: out[row] = sum_{l < levels} codebooks[l][ids[row*L + l]], summed in
+ * fp32 in level order, then stored as fp32 or rounded to nearest-even bf16.
+ * `levels` in [0, L] reconstructs from the first `levels` levels only
+ * (coarse-to-fine; levels == L is the full reconstruction).
+ *
+ * ids       : device, [n][L] int32.  An ID outside [0, K) contributes
+ *             nothing and is counted in *bad_ids.
+ * codebooks : device, [L][K][d] fp32, 16-byte aligned.
+ * out       : device, [n][d] in out_dtype, 16-byte aligned.
+ * bad_ids   : device uint32 counter incremented by the number of out-of-range
+ *             IDs seen, or NULL.  The caller zeroes it.
+ * ---------------------------------------------------------------------- */
+rvq_status rvq_decode(const int32_t *ids, int64_t n, const float *codebooks,
+                      int32_t L, int32_t K, int32_t d, int32_t levels,
+                      void *out, rvq_dtype out_dtype, uint32_t *bad_ids, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Level statistics.
+ *   hist[l][k] = number of rows whose level-l ID is k (exact integer count;
+ *                out-of-range IDs are not counted and go to *bad_ids).
+ *   msr[l]     = mean over rows of ||x_row - sum_{j <= l} codebooks[j][ids[row][j]]||^2,
+ *                the mean squared residual left after levels 0..l.  Per-row
+ *                residuals are fp32, squared norms and the mean are fp64,
+ *                reduced in a fixed order (bitwise reproducible).
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes needed by rvq_level_stats (x given or not). */
+rvq_status rvq_level_stats_workspace_size(int64_t n, int32_t L, int32_t K, int32_t d,
+                                          int32_t with_msr, size_t *bytes);
+
+/*
+ * ids       : device, [n][L] int32.
+ * hist      : device, [L][K] int64 output, fully overwritten.  Required.
+ * x         : device, [n][d] rows (x_dtype), or NULL to skip msr.
+ * codebooks : device, [L][K][d] fp32; required when x is given.
+ * msr       : device, [L] fp64 output; required when x is given, else ignored.
+ *             With n == 0 it is all zeros.
+ * bad_ids   : as for rvq_decode.
+ * workspace : device, >= rvq_level_stats_workspace_size bytes, 256-byte aligned.
+ */
+rvq_status rvq_level_stats(const int32_t *ids, int64_t n, int32_t L, int32_t K, int64_t *hist,
+                           const void *x, rvq_dtype x_dtype, int32_t d, const float *codebooks,
+                           double *msr, uint32_t *bad_ids,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RVQ_H */

@@ -1,0 +1,222 @@
+"""Residual vector quantization (RVQ) on MI355X (gfx950).
+
+Thin Python binding of ``librvq.so`` (the C ABI in ``include/rvq.h``).  It
+only marshals arguments: torch allocates device memory (outputs and
+workspaces) and supplies the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, importing this package raises.
+
+Functions keep the C names:
+  rvq_prepare_codebooks(codebooks)            -> prepared buffer (uint8 tensor)
+  rvq_encode(x, codebooks, prepared)          -> ids [n, L] int32 (, residual)
+  rvq_decode(ids, codebooks, out_dtype, ...)  -> reconstruction [n, d]
+  rvq_level_stats(ids, K, x, codebooks)       -> (hist [L, K] int64, msr [L] fp64)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "RVQError", "library_path", "exported_symbols", "RVQ_F32", "RVQ_BF16",
+    "rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size", "rvq_encode",
+    "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_status_string",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "librvq.so")
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "rvq.h")
+
+RVQ_OK, RVQ_ERR_INVALID_ARGUMENT, RVQ_ERR_UNSUPPORTED, RVQ_ERR_WORKSPACE_TOO_SMALL, RVQ_ERR_HIP = range(5)
+RVQ_F32, RVQ_BF16 = 0, 1
+
+
+class RVQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+_i32, _i64, _sz, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+_psz = ctypes.POINTER(ctypes.c_size_t)
+
+_lib.rvq_status_string.argtypes = [ctypes.c_int]
+_lib.rvq_status_string.restype = ctypes.c_char_p
+_lib.rvq_last_error.argtypes = []
+_lib.rvq_last_error.restype = ctypes.c_char_p
+_lib.rvq_prepared_size.argtypes = [_i32, _i32, _i32, _psz]
+_lib.rvq_prepare_codebooks.argtypes = [_p, _i32, _i32, _i32, _p, _sz, _p]
+_lib.rvq_encode_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _psz]
+_lib.rvq_encode.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _sz, _p]
+_lib.rvq_encode_profiled.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p,
+                                     _sz, _p, _p]
+_lib.rvq_decode.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _i32, _p, ctypes.c_int, _p, _p]
+_lib.rvq_level_stats_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _psz]
+_lib.rvq_level_stats.argtypes = [_p, _i64, _i32, _i32, _p, _p, ctypes.c_int, _i32, _p, _p, _p,
+                                 _p, _sz, _p]
+for _f in ("rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size",
+           "rvq_encode", "rvq_encode_profiled", "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded ctypes library (for callers passing raw pointers)."""
+    return _lib
+
+
+def exported_symbols() -> list:
+    """Function names declared in include/rvq.h."""
+    with open(_HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(rvq_\w+)\s*\(", text, re.M)))
+
+
+def rvq_status_string(status: int) -> str:
+    return _lib.rvq_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != RVQ_OK:
+        raise RVQError(status, f"{rvq_status_string(status)}: {_lib.rvq_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return RVQ_F32
+    if dt == torch.bfloat16:
+        return RVQ_BF16
+    raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def _need_cuda(name: str, t: torch.Tensor) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def rvq_prepared_size(L: int, K: int, d: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.rvq_prepared_size(L, K, d, ctypes.byref(out)))
+    return out.value
+
+
+def rvq_prepare_codebooks(codebooks: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Norms and bf16 copy of a fixed [L, K, d] fp32 codebook set."""
+    _need_cuda("codebooks", codebooks)
+    L, K, d = codebooks.shape
+    nbytes = rvq_prepared_size(L, K, d)
+    prepared = out if out is not None else torch.empty(nbytes, dtype=torch.uint8,
+                                                       device=codebooks.device)
+    _check(_lib.rvq_prepare_codebooks(_ptr(codebooks), L, K, d, _ptr(prepared), prepared.numel(),
+                                      _stream(codebooks.device)))
+    return prepared
+
+
+def rvq_encode_workspace_size(n: int, d: int, L: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.rvq_encode_workspace_size(n, d, L, K, ctypes.byref(out)))
+    return out.value
+
+
+def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, prepared: Optional[torch.Tensor] = None,
+               residual: bool = False, workspace: Optional[torch.Tensor] = None,
+               ids_out: Optional[torch.Tensor] = None, events=None):
+    """Greedy RVQ encode of rows x [n, d] (fp32 or bf16).  Returns ids [n, L]
+    int32, and the fp32 final residual [n, d] when ``residual`` is true.
+    ``events``: optional ctypes array of 2*L hipEvent_t recorded around each
+    level's distance kernel (rvq_encode_profiled)."""
+    _need_cuda("x", x)
+    _need_cuda("codebooks", codebooks)
+    L, K, d = codebooks.shape
+    n = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError("x must be [n, d] with the codebooks' d")
+    if prepared is None:
+        prepared = rvq_prepare_codebooks(codebooks)
+    dev = x.device
+    ids = ids_out if ids_out is not None else torch.empty((n, L), dtype=torch.int32, device=dev)
+    res = torch.empty((n, d), dtype=torch.float32, device=dev) if residual else None
+    wbytes = rvq_encode_workspace_size(n, d, L, K)
+    if workspace is None or workspace.numel() < wbytes:
+        workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    _check(_lib.rvq_encode_profiled(_ptr(x), _dtype_code(x.dtype), n, d, _ptr(codebooks),
+                                    _ptr(prepared), L, K, _ptr(ids), _ptr(res), _ptr(workspace),
+                                    workspace.numel(), _stream(dev), events))
+    return (ids, res) if residual else ids
+
+
+def rvq_decode(ids: torch.Tensor, codebooks: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+               levels: Optional[int] = None, bad_ids: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sum of the chosen codewords of the first ``levels`` levels (default all)."""
+    _need_cuda("ids", ids)
+    _need_cuda("codebooks", codebooks)
+    L, K, d = codebooks.shape
+    n = ids.shape[0]
+    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[1] != L:
+        raise ValueError("ids must be int32 [n, L]")
+    levels = L if levels is None else int(levels)
+    if out is None:
+        out = torch.empty((n, d), dtype=out_dtype, device=ids.device)
+    _check(_lib.rvq_decode(_ptr(ids), n, _ptr(codebooks), L, K, d, levels, _ptr(out),
+                           _dtype_code(out.dtype), _ptr(bad_ids), _stream(ids.device)))
+    return out
+
+
+def rvq_level_stats_workspace_size(n: int, L: int, K: int, d: int, with_msr: bool) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.rvq_level_stats_workspace_size(n, L, K, d, 1 if with_msr else 0, ctypes.byref(out)))
+    return out.value
+
+
+def rvq_level_stats(ids: torch.Tensor, K: int, x: Optional[torch.Tensor] = None,
+                    codebooks: Optional[torch.Tensor] = None,
+                    bad_ids: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Per-level usage counts [L, K] int64 and, when x is given, the per-level
+    mean squared residual [L] fp64."""
+    _need_cuda("ids", ids)
+    n, L = ids.shape
+    dev = ids.device
+    hist = torch.empty((L, K), dtype=torch.int64, device=dev)
+    msr = None
+    d = 1
+    xdt = RVQ_F32
+    if x is not None:
+        _need_cuda("x", x)
+        if codebooks is None:
+            raise ValueError("codebooks are required with x")
+        _need_cuda("codebooks", codebooks)
+        d = x.shape[1]
+        xdt = _dtype_code(x.dtype)
+        msr = torch.empty((L,), dtype=torch.float64, device=dev)
+    wbytes = rvq_level_stats_workspace_size(n, L, K, d, x is not None)
+    if workspace is None or workspace.numel() < wbytes:
+        workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    _check(_lib.rvq_level_stats(_ptr(ids), n, L, K, _ptr(hist), _ptr(x), xdt, d, _ptr(codebooks),
+                                _ptr(msr), _ptr(bad_ids), _ptr(workspace), workspace.numel(),
+                                _stream(dev)))
+    return hist, msr

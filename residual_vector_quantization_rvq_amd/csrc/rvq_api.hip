@@ -1,0 +1,285 @@
+// rvq_api.hip -- the C ABI declared in include/rvq.h.
+//
+// Host side only: argument validation (before any HIP call), workspace
+// layout, kernel planning and the per-level launch sequence of the encoder.
+// Everything is enqueued on the caller's stream; nothing is allocated.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/rvq.h"
+#include "common.h"
+
+using namespace rvq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rvq_status fail(rvq_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+rvq_status fail(rvq_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+rvq_status hip_fail(hipError_t e, const char *what) {
+  return fail(RVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 25;  // one wave per row: grid work-items < 2^32
+constexpr int kMaxLevelsGather = 64;            // decode / statistics: IDs of a row in one wave
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+rvq_status check_shape(int64_t n, int32_t d, int32_t L, int32_t K) {
+  if (n < 0) return fail(RVQ_ERR_INVALID_ARGUMENT, "n must be >= 0 (got %lld)", (long long)n);
+  if (d < 1) return fail(RVQ_ERR_INVALID_ARGUMENT, "d must be >= 1 (got %d)", d);
+  if (L < 1) return fail(RVQ_ERR_INVALID_ARGUMENT, "L must be >= 1 (got %d)", L);
+  if (K < 1) return fail(RVQ_ERR_INVALID_ARGUMENT, "K must be >= 1 (got %d)", K);
+  if (K > INT32_MAX - kTileCodewords)
+    return fail(RVQ_ERR_UNSUPPORTED, "K too large (got %d)", K);
+  if (n > kMaxRows)
+    return fail(RVQ_ERR_UNSUPPORTED, "n above %lld rows per call (got %lld)", (long long)kMaxRows,
+                (long long)n);
+  if ((int64_t)L * padded_k(K) * padded_d(d) > ((int64_t)1 << 40))
+    return fail(RVQ_ERR_UNSUPPORTED, "codebook too large");
+  return RVQ_OK;
+}
+
+rvq_status need(const void *p, const char *name, size_t align) {
+  if (!p) return fail(RVQ_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);
+  if (!aligned(p, align))
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "%s must be %zu-byte aligned", name, align);
+  return RVQ_OK;
+}
+
+#define RVQ_TRY(expr)                     \
+  do {                                    \
+    rvq_status _st = (expr);              \
+    if (_st != RVQ_OK) return _st;        \
+  } while (0)
+
+#define HIP_TRY(expr, what)               \
+  do {                                    \
+    hipError_t _e = (expr);               \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+struct PreparedLayout {
+  size_t norms_off, cbh_off, total;
+};
+PreparedLayout prepared_layout(int32_t L, int32_t K, int32_t d) {
+  PreparedLayout p;
+  const size_t Kp = (size_t)padded_k(K), Dp = (size_t)padded_d(d);
+  p.norms_off = 0;
+  p.cbh_off = align256((size_t)L * Kp * sizeof(float));
+  p.total = p.cbh_off + align256((size_t)L * Kp * Dp * sizeof(uint16_t));
+  return p;
+}
+
+struct EncodeLayout {
+  size_t r32_off, r16_off, part_off, total;
+};
+EncodeLayout encode_layout(int64_t n, int32_t d, int32_t K) {
+  EncodeLayout w;
+  const size_t Dp = (size_t)padded_d(d);
+  const size_t ktiles = (size_t)ceil_div(K, kTileCodewords);
+  w.r32_off = 0;
+  w.r16_off = align256((size_t)n * d * sizeof(float));
+  w.part_off = w.r16_off + align256((size_t)n * Dp * sizeof(uint16_t));
+  w.total = w.part_off + align256((size_t)n * ktiles * sizeof(float4));
+  if (w.total == 0) w.total = 256;
+  return w;
+}
+
+int num_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus > 0 ? cus : 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rvq_status_string(rvq_status s) {
+  switch (s) {
+    case RVQ_OK: return "RVQ_OK";
+    case RVQ_ERR_INVALID_ARGUMENT: return "RVQ_ERR_INVALID_ARGUMENT";
+    case RVQ_ERR_UNSUPPORTED: return "RVQ_ERR_UNSUPPORTED";
+    case RVQ_ERR_WORKSPACE_TOO_SMALL: return "RVQ_ERR_WORKSPACE_TOO_SMALL";
+    case RVQ_ERR_HIP: return "RVQ_ERR_HIP";
+  }
+  return "RVQ_ERR_UNKNOWN";
+}
+
+const char *rvq_last_error(void) { return g_err; }
+
+rvq_status rvq_prepared_size(int32_t L, int32_t K, int32_t d, size_t *bytes) {
+  RVQ_TRY(check_shape(0, d, L, K));
+  if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+  *bytes = prepared_layout(L, K, d).total;
+  return RVQ_OK;
+}
+
+rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, int32_t d,
+                                 void *prepared, size_t prepared_bytes, hipStream_t stream) {
+  RVQ_TRY(check_shape(0, d, L, K));
+  RVQ_TRY(need(codebooks, "codebooks", 16));
+  RVQ_TRY(need(prepared, "prepared", 256));
+  const PreparedLayout pl = prepared_layout(L, K, d);
+  if (prepared_bytes < pl.total)
+    return fail(RVQ_ERR_WORKSPACE_TOO_SMALL, "prepared buffer needs %zu bytes (got %zu)", pl.total,
+                prepared_bytes);
+  char *base = (char *)prepared;
+  HIP_TRY(launch_prepare(codebooks, L, K, d, (float *)(base + pl.norms_off),
+                         (uint16_t *)(base + pl.cbh_off), stream),
+          "prepare_kernel launch");
+  return RVQ_OK;
+}
+
+rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K, size_t *bytes) {
+  RVQ_TRY(check_shape(n, d, L, K));
+  if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+  *bytes = encode_layout(n, d, K).total;
+  return RVQ_OK;
+}
+
+rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
+                               const float *codebooks, const void *prepared, int32_t L, int32_t K,
+                               int32_t *ids, float *residual_out, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream, hipEvent_t *events) {
+  RVQ_TRY(check_shape(n, d, L, K));
+  if (x_dtype != RVQ_F32 && x_dtype != RVQ_BF16)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown x_dtype %d", (int)x_dtype);
+  RVQ_TRY(need(codebooks, "codebooks", 16));
+  RVQ_TRY(need(prepared, "prepared", 256));
+  if (n > 0) {
+    RVQ_TRY(need(x, "x", 16));
+    RVQ_TRY(need(ids, "ids", 4));
+    if (residual_out && !aligned(residual_out, 16))
+      return fail(RVQ_ERR_INVALID_ARGUMENT, "residual_out must be 16-byte aligned");
+  }
+  const EncodeLayout wl = encode_layout(n, d, K);
+  RVQ_TRY(need(workspace, "workspace", 256));
+  if (workspace_bytes < wl.total)
+    return fail(RVQ_ERR_WORKSPACE_TOO_SMALL, "encode workspace needs %zu bytes (got %zu)",
+                wl.total, workspace_bytes);
+  if (n == 0) return RVQ_OK;
+
+  const int Dp = (int)padded_d(d);
+  const int64_t Kp = padded_k(K);
+  const PreparedLayout pl = prepared_layout(L, K, d);
+  const float *norms = (const float *)((const char *)prepared + pl.norms_off);
+  const uint16_t *cbh = (const uint16_t *)((const char *)prepared + pl.cbh_off);
+  char *ws = (char *)workspace;
+  float *r32 = (float *)(ws + wl.r32_off);
+  uint16_t *r16 = (uint16_t *)(ws + wl.r16_off);
+  float4 *part = (float4 *)(ws + wl.part_off);
+
+  const DistPlan plan = plan_distance(n, K, num_cus());
+  HIP_TRY(launch_init_residual(x, x_dtype == RVQ_BF16, n, d, Dp, r32, r16, stream),
+          "init_residual_kernel launch");
+  for (int l = 0; l < L; ++l) {
+    if (events) HIP_TRY(hipEventRecord(events[2 * l], stream), "hipEventRecord");
+    HIP_TRY(launch_distance_top2(plan, r16, n, Dp, cbh + (int64_t)l * Kp * Dp, norms + l * Kp,
+                                 part, stream),
+            "distance_top2_kernel launch");
+    if (events) HIP_TRY(hipEventRecord(events[2 * l + 1], stream), "hipEventRecord");
+    const bool last = l == L - 1;
+    float *r_out = (last && residual_out) ? residual_out : r32;
+    HIP_TRY(launch_rescore_update(part, plan.splits, n, d, Dp, K, L, l,
+                                  codebooks + (int64_t)l * K * d, r32, r_out, r16, !last, ids,
+                                  stream),
+            "rescore_update_kernel launch");
+  }
+  return RVQ_OK;
+}
+
+rvq_status rvq_encode(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
+                      const float *codebooks, const void *prepared, int32_t L, int32_t K,
+                      int32_t *ids, float *residual_out, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return rvq_encode_profiled(x, x_dtype, n, d, codebooks, prepared, L, K, ids, residual_out,
+                             workspace, workspace_bytes, stream, nullptr);
+}
+
+rvq_status rvq_decode(const int32_t *ids, int64_t n, const float *codebooks, int32_t L, int32_t K,
+                      int32_t d, int32_t levels, void *out, rvq_dtype out_dtype, uint32_t *bad_ids,
+                      hipStream_t stream) {
+  RVQ_TRY(check_shape(n, d, L, K));
+  if (L > kMaxLevelsGather)
+    return fail(RVQ_ERR_UNSUPPORTED, "decode supports L <= %d (got %d)", kMaxLevelsGather, L);
+  if (levels < 0 || levels > L)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "levels must be in [0, L] (got %d)", levels);
+  if (out_dtype != RVQ_F32 && out_dtype != RVQ_BF16)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", (int)out_dtype);
+  RVQ_TRY(need(codebooks, "codebooks", 16));
+  if (n > 0) {
+    RVQ_TRY(need(ids, "ids", 4));
+    RVQ_TRY(need(out, "out", 16));
+  }
+  if (bad_ids && !aligned(bad_ids, 4))
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "bad_ids must be 4-byte aligned");
+  if (n == 0) return RVQ_OK;
+  HIP_TRY(launch_decode(ids, n, codebooks, L, K, d, levels, out, out_dtype == RVQ_BF16, bad_ids,
+                        stream),
+          "decode_kernel launch");
+  return RVQ_OK;
+}
+
+rvq_status rvq_level_stats_workspace_size(int64_t n, int32_t L, int32_t K, int32_t d,
+                                          int32_t with_msr, size_t *bytes) {
+  RVQ_TRY(check_shape(n, with_msr ? d : 1, L, K));
+  if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+  size_t total = align256(hist_partial_bytes(n, L, K));
+  if (with_msr) total += align256(msr_partial_bytes(n, L));
+  *bytes = total > 0 ? total : 256;
+  return RVQ_OK;
+}
+
+rvq_status rvq_level_stats(const int32_t *ids, int64_t n, int32_t L, int32_t K, int64_t *hist,
+                           const void *x, rvq_dtype x_dtype, int32_t d, const float *codebooks,
+                           double *msr, uint32_t *bad_ids, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const bool with_msr = x != nullptr;
+  RVQ_TRY(check_shape(n, with_msr ? d : 1, L, K));
+  if (L > kMaxLevelsGather)
+    return fail(RVQ_ERR_UNSUPPORTED, "level statistics support L <= %d (got %d)",
+                kMaxLevelsGather, L);
+  RVQ_TRY(need(hist, "hist", 8));
+  if (n > 0) RVQ_TRY(need(ids, "ids", 4));
+  if (with_msr) {
+    if (x_dtype != RVQ_F32 && x_dtype != RVQ_BF16)
+      return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown x_dtype %d", (int)x_dtype);
+    RVQ_TRY(need(codebooks, "codebooks", 16));
+    RVQ_TRY(need(msr, "msr", 8));
+    if (n > 0) RVQ_TRY(need(x, "x", 16));
+  }
+  if (bad_ids && !aligned(bad_ids, 4))
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "bad_ids must be 4-byte aligned");
+  size_t need_bytes = 0;
+  RVQ_TRY(rvq_level_stats_workspace_size(n, L, K, d, with_msr ? 1 : 0, &need_bytes));
+  RVQ_TRY(need(workspace, "workspace", 256));
+  if (workspace_bytes < need_bytes)
+    return fail(RVQ_ERR_WORKSPACE_TOO_SMALL, "level-stats workspace needs %zu bytes (got %zu)",
+                need_bytes, workspace_bytes);
+  char *ws = (char *)workspace;
+  uint32_t *hpart = (uint32_t *)ws;
+  double *mpart = (double *)(ws + align256(hist_partial_bytes(n, L, K)));
+  HIP_TRY(launch_hist(ids, n, L, K, hist, hpart, bad_ids, stream), "histogram launch");
+  if (with_msr)
+    HIP_TRY(launch_msr(x, x_dtype == RVQ_BF16, ids, n, d, codebooks, L, K, msr, mpart, bad_ids,
+                       stream),
+            "msr launch");
+  return RVQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/rvq.h, sizes workspaces as documented and rejects bad
+arguments on the host before any HIP call."""
+import ctypes
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "residual_vector_quantization_rvq_amd", "librvq.so")
+
+
+@pytest.fixture(scope="module")
+def rvq():
+    if not os.path.exists(LIB):
+        from residual_vector_quantization_rvq_amd import _build
+        _build.build()
+    import residual_vector_quantization_rvq_amd as m
+    return m
+
+
+def test_exports_every_declared_symbol(rvq):
+    names = rvq.exported_symbols()
+    assert {"rvq_encode", "rvq_decode", "rvq_level_stats", "rvq_prepare_codebooks",
+            "rvq_status_string", "rvq_last_error"} <= set(names)
+    lib = ctypes.CDLL(rvq.library_path())
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in rvq.h but not exported"
+
+
+def test_status_strings(rvq):
+    assert rvq.rvq_status_string(0) == "RVQ_OK"
+    assert rvq.rvq_status_string(3) == "RVQ_ERR_WORKSPACE_TOO_SMALL"
+    assert rvq.rvq_status_string(99) == "RVQ_ERR_UNKNOWN"
+
+
+def test_prepared_size_layout(rvq):
+    # norms [L][Kp] fp32 then bf16 [L][Kp][Dp], each rounded up to 256 bytes
+    L, K, d = 8, 8192, 1152
+    assert rvq.rvq_prepared_size(L, K, d) == L * K * 4 + L * K * d * 2
+    # padding: K -> multiple of 256, d -> multiple of 32
+    L, K, d = 3, 300, 70
+    Kp, Dp = 512, 96
+    norms = (L * Kp * 4 + 255) // 256 * 256
+    cbh = (L * Kp * Dp * 2 + 255) // 256 * 256
+    assert rvq.rvq_prepared_size(L, K, d) == norms + cbh
+
+
+def test_encode_workspace_size(rvq):
+    n, d, L, K = 1000, 64, 4, 256
+    r32 = n * d * 4
+    r16 = n * d * 2
+    part = n * 1 * 16
+    al = lambda v: (v + 255) // 256 * 256
+    assert rvq.rvq_encode_workspace_size(n, d, L, K) == al(r32) + al(r16) + al(part)
+    assert rvq.rvq_encode_workspace_size(0, d, L, K) == 256
+
+
+@pytest.mark.parametrize("n,d,L,K,err", [
+    (-1, 4, 1, 1, 1), (1, 0, 1, 1, 1), (1, 4, 0, 1, 1), (1, 4, 1, 0, 1),
+    (1 << 26, 4, 1, 1, 2),
+])
+def test_shape_validation(rvq, n, d, L, K, err):
+    with pytest.raises(rvq.RVQError) as e:
+        rvq.rvq_encode_workspace_size(n, d, L, K)
+    assert e.value.status == err
+
+
+def _call_encode(rvq, **kw):
+    lib = rvq.raw_library()
+    a = dict(x=256, x_dtype=0, n=10, d=4, cb=256, prep=256, L=2, K=3, ids=256, res=None,
+             ws=256, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    p = ctypes.c_void_p
+    return lib.rvq_encode(p(a["x"]), a["x_dtype"], a["n"], a["d"], p(a["cb"]), p(a["prep"]),
+                          a["L"], a["K"], p(a["ids"]), p(a["res"]) if a["res"] else None,
+                          p(a["ws"]), a["ws_bytes"], p(a["stream"]) if a["stream"] else None)
+
+
+def test_encode_rejects_bad_arguments_before_any_hip_call(rvq):
+    # fake, never-dereferenced addresses: validation must fail first
+    assert _call_encode(rvq, x_dtype=7) == 1
+    assert _call_encode(rvq, x=0) == 1
+    assert _call_encode(rvq, x=8) == 1          # misaligned
+    assert _call_encode(rvq, cb=0) == 1
+    assert _call_encode(rvq, prep=128) == 1     # prepared must be 256-byte aligned
+    assert _call_encode(rvq, ids=0) == 1
+    assert _call_encode(rvq, res=260) == 1      # residual_out misaligned
+    assert _call_encode(rvq, ws=0) == 1
+    assert _call_encode(rvq, ws_bytes=10) == 3
+    assert "workspace" in rvq.raw_library().rvq_last_error().decode()
+    # n == 0 is a no-op once the arguments are valid (no HIP call made)
+    assert _call_encode(rvq, n=0, x=0, ids=0) == 0
+
+
+def test_decode_and_stats_reject_bad_arguments(rvq):
+    lib = rvq.raw_library()
+    p = ctypes.c_void_p
+    # levels out of range, bad dtype, L above the gather limit, null out
+    assert lib.rvq_decode(p(256), 4, p(256), 2, 3, 4, 3, p(256), 1, None, None) == 1
+    assert lib.rvq_decode(p(256), 4, p(256), 2, 3, 4, 2, p(256), 5, None, None) == 1
+    assert lib.rvq_decode(p(256), 4, p(256), 65, 3, 4, 2, p(256), 1, None, None) == 2
+    assert lib.rvq_decode(p(256), 4, p(256), 2, 3, 4, 2, None, 1, None, None) == 1
+    assert lib.rvq_decode(None, 0, p(256), 2, 3, 4, 2, None, 1, None, None) == 0
+    # level stats: hist required; x without codebooks; short workspace
+    assert lib.rvq_level_stats(p(256), 4, 2, 3, None, None, 0, 1, None, None, None,
+                               p(256), 1 << 20, None) == 1
+    assert lib.rvq_level_stats(p(256), 4, 2, 3, p(256), p(256), 0, 4, None, p(256), None,
+                               p(256), 1 << 20, None) == 1
+    assert lib.rvq_level_stats(p(256), 4, 2, 3, p(256), None, 0, 1, None, None, None,
+                               p(256), 1, None) == 3
+
+
+def test_prepare_rejects_small_buffer(rvq):
+    lib = rvq.raw_library()
+    p = ctypes.c_void_p
+    assert lib.rvq_prepare_codebooks(p(256), 2, 3, 4, p(256), 16, None) == 3
+    assert lib.rvq_prepare_codebooks(None, 2, 3, 4, p(256), 1 << 20, None) == 1

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rvq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import residual_vector_quantization_rvq_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def _encode(rvq, w, dev, residual=True):
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prepared = rvq.rvq_prepare_codebooks(cb)
+    ids, res = rvq.rvq_encode(x, cb, prepared, residual=True)
+    torch.cuda.synchronize()
+    return ids, res, x, cb, prepared
+
+
+def _full_parity(rvq, w, dev, tag):
+    ids, res, x, cb, prepared = _encode(rvq, w, dev)
+    ids_h = ids.cpu().numpy()
+    ref = oracle.encode(w.x, w.codebooks, x_dtype=w.x_dtype)
+    stats = parity.check_strict_prefix(ids_h, ref)
+    parity.check_teacher_forced(w.x, w.x_dtype, ids_h, w.codebooks)
+    parity.check_residual(res.cpu().numpy(), w.x, w.x_dtype, ids_h, w.codebooks)
+    out32 = rvq.rvq_decode(ids, cb, torch.float32)
+    out16 = rvq.rvq_decode(ids, cb, torch.bfloat16)
+    hist, msr = rvq.rvq_level_stats(ids, w.K, x, cb)
+    torch.cuda.synchronize()
+    parity.check_decode_f32(out32.cpu().numpy(), ids_h, w.codebooks)
+    parity.check_decode_bf16(parity.bf16_tensor_bits(out16), ids_h, w.codebooks)
+    np.testing.assert_array_equal(hist.cpu().numpy(), oracle.hist(ids_h, w.K))
+    parity.check_msr(msr.cpu().numpy(), w.x, w.x_dtype, ids_h, w.codebooks)
+    print(f"[{tag}] {stats}")
+    return ids_h, ref
+
+
+def test_tiny_structured_full(rvq, dev):
+    w = workloads.tiny_structured()
+    ids_h, ref = _full_parity(rvq, w, dev, "tiny_structured")
+    half = w.N // 2
+    np.testing.assert_array_equal(ids_h[half:], w.gen_ids[half:])
+
+
+RAGGED = [
+    # seed, n, d, L, K, dtype: several row blocks with a ragged tail, several
+    # feature stages, several codeword tiles with a ragged tail
+    (31, 300, 96, 3, 600, "f32"),
+    (32, 257, 70, 2, 513, "bf16"),
+    (33, 129, 32, 4, 256, "f32"),
+    (34, 1, 1152, 8, 300, "f32"),
+    (35, 64, 48, 1, 1, "f32"),
+    (36, 200, 64, 5, 2, "bf16"),
+    (37, 1000, 128, 4, 2048, "bf16"),
+    (38, 77, 1280, 3, 700, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: f"s{c[0]}_n{c[1]}_d{c[2]}_L{c[3]}_K{c[4]}_{c[5]}")
+def test_random_shapes_full(rvq, dev, case):
+    seed, n, d, L, K, dt = case
+    w = workloads.random_problem(seed, n, d, L, K, x_dtype=dt)
+    _full_parity(rvq, w, dev, w.name)
+
+
+def test_single_image(rvq, dev):
+    w = workloads.single_image()
+    ids, res, x, cb, _ = _encode(rvq, w, dev)
+    ids_h = ids.cpu().numpy()
+    sel = np.random.default_rng(0).choice(w.N, 96, replace=False)
+    sel.sort()
+    sub = w.rows(sel)
+    ref = oracle.encode(sub.x, sub.codebooks)
+    print("[single_image]", parity.check_strict_prefix(ids_h[sel], ref))
+    parity.check_teacher_forced(sub.x, "f32", ids_h[sel], w.codebooks)
+    parity.check_residual(res.cpu().numpy(), w.x, "f32", ids_h, w.codebooks)
+    out = rvq.rvq_decode(ids, cb, torch.float32)
+    torch.cuda.synchronize()
+    parity.check_decode_f32(out.cpu().numpy(), ids_h, w.codebooks)
+
+
+def test_native_batch(rvq, dev):
+    w = workloads.native_batch()
+    ids, res, x, cb, prepared = _encode(rvq, w, dev)
+    ids_h = ids.cpu().numpy()
+    # oracle on sampled rows: 3 per image (first, middle, last) incl. the batch tail
+    off = w.offsets
+    sel = np.unique(np.concatenate([[off[i], (off[i] + off[i + 1]) // 2, off[i + 1] - 1]
+                                    for i in range(16)]))
+    sub = w.rows(sel)
+    ref = oracle.encode(sub.x, sub.codebooks, x_dtype="bf16")
+    print("[native_batch]", parity.check_strict_prefix(ids_h[sel], ref))
+    parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
+    parity.check_residual(res[torch.from_numpy(sel).to(dev)].cpu().numpy(), sub.x, "bf16",
+                          ids_h[sel], w.codebooks)
+    out16 = rvq.rvq_decode(ids, cb, torch.bfloat16)
+    out32 = rvq.rvq_decode(ids, cb, torch.float32)
+    hist, _ = rvq.rvq_level_stats(ids, w.K)
+    torch.cuda.synchronize()
+    parity.check_decode_bf16(parity.bf16_tensor_bits(out16), ids_h, w.codebooks)
+    parity.check_decode_f32(out32.cpu().numpy(), ids_h, w.codebooks)
+    np.testing.assert_array_equal(hist.cpu().numpy(), oracle.hist(ids_h, w.K))
+    # batch invariance: one image encoded alone gives the same bits
+    a, b = int(off[5]), int(off[6])
+    ids5, res5 = rvq.rvq_encode(x[a:b].contiguous(), cb, prepared, residual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ids5, ids[a:b])
+    assert torch.equal(res5.view(torch.int32), res[a:b].view(torch.int32))
+
+
+def test_bulk_tokenisation_sampled(rvq, dev):
+    w = workloads.bulk_tokenisation()
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prepared = rvq.rvq_prepare_codebooks(cb)
+    ids = rvq.rvq_encode(x, cb, prepared)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    assert ids_h.min() >= 0 and ids_h.max() < w.K
+    sel = np.concatenate([[0, w.N - 1], np.random.default_rng(1).choice(w.N, 6, replace=False)])
+    sel.sort()
+    sub = w.rows(sel)
+    ref = oracle.encode(sub.x, sub.codebooks, x_dtype="bf16")
+    print("[bulk_tokenisation]", parity.check_strict_prefix(ids_h[sel], ref))
+    parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
+
+
+def test_decode_heavy(rvq, dev):
+    w = workloads.decode_heavy()
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids = torch.from_numpy(w.ids).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = rvq.rvq_decode(ids, cb, torch.bfloat16, bad_ids=bad)
+    hist, _ = rvq.rvq_level_stats(ids, w.K, bad_ids=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    np.testing.assert_array_equal(hist.cpu().numpy(), oracle.hist(w.ids, w.K))
+    hot = np.where((w.ids == 0).all(axis=1))[0][:64]
+    sel = np.unique(np.concatenate([hot, np.random.default_rng(2).choice(len(w.ids), 4000, replace=False),
+                                    [len(w.ids) - 1]]))
+    got = parity.bf16_tensor_bits(out[torch.from_numpy(sel).to(dev)])
+    parity.check_decode_bf16(got, w.ids[sel], w.codebooks)
+    # statistics subset: encode at L=8, then msr along the GPU's IDs
+    x = parity.x_to_device(w, dev)
+    sids = rvq.rvq_encode(x, cb)
+    h2, msr = rvq.rvq_level_stats(sids, w.K, x, cb)
+    torch.cuda.synchronize()
+    sids_h = sids.cpu().numpy()
+    np.testing.assert_array_equal(h2.cpu().numpy(), oracle.hist(sids_h, w.K))
+    parity.check_msr(msr.cpu().numpy(), w.x, "f32", sids_h, w.codebooks)
+    sel2 = np.random.default_rng(3).choice(w.N, 48, replace=False)
+    sel2.sort()
+    sub = w.rows(sel2)
+    ref = oracle.encode(sub.x, sub.codebooks)
+    print("[decode_heavy msr subset]", parity.check_strict_prefix(sids_h[sel2], ref))
+    parity.check_teacher_forced(sub.x, "f32", sids_h[sel2], w.codebooks)
+
+
+def test_empty_batch(rvq, dev):
+    w = workloads.random_problem(40, 0, 64, 3, 300)
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids, res = rvq.rvq_encode(x, cb, residual=True)
+    out = rvq.rvq_decode(ids, cb, torch.bfloat16)
+    hist, msr = rvq.rvq_level_stats(ids, w.K, x, cb)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, 3) and res.shape == (0, 64) and out.shape == (0, 64)
+    assert int(hist.abs().sum()) == 0 and hist.shape == (3, 300)
+    assert torch.all(msr == 0)
+
+
+def test_duplicate_codewords_tie_to_lowest_index(rvq, dev):
+    rng = np.random.default_rng(41)
+    L, K, d = 2, 600, 64
+    cb = rng.standard_normal((L, K, d)).astype(np.float32)
+    cb[0, 10] = cb[0, 300]   # exact duplicates in different codeword tiles
+    cb[0, 599] = cb[0, 300]
+    cb[1, 5] = cb[1, 7]
+    x = np.stack([cb[0, 300] + 0.01 * rng.standard_normal(d).astype(np.float32) for _ in range(40)])
+    x = x.astype(np.float32)
+    w = workloads.Workload("dups", cb, x, "f32")
+    ids, res, *_ = _encode(rvq, w, dev)
+    ids_h = ids.cpu().numpy()
+    ref = oracle.encode(x, cb)
+    assert np.all(ref["ids"][:, 0] == 10)
+    assert np.all(ids_h[:, 0] == 10)
+    parity.check_teacher_forced(x, "f32", ids_h, cb)
+
+
+def test_invalid_ids_are_counted_and_skipped(rvq, dev):
+    w = workloads.random_problem(42, 50, 40, 3, 100)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids_h = np.random.default_rng(5).integers(0, w.K, size=(50, 3)).astype(np.int32)
+    ids_h[3, 1] = -1
+    ids_h[7, 2] = w.K
+    ids_h[9, 0] = 1 << 30
+    ids = torch.from_numpy(ids_h).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = rvq.rvq_decode(ids, cb, torch.float32, bad_ids=bad)
+    hist, _ = rvq.rvq_level_stats(ids, w.K, bad_ids=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 6  # 3 from decode, 3 from statistics
+    valid = ids_h.copy()
+    cleaned = oracle.decode(np.where((valid >= 0) & (valid < w.K), valid, 0), w.codebooks)
+    for (r, l) in [(3, 1), (7, 2), (9, 0)]:
+        cleaned[r] -= w.codebooks[l, 0].astype(np.float64)  # skipped level adds nothing
+    np.testing.assert_allclose(out.cpu().numpy(), cleaned, rtol=1e-5, atol=1e-5)
+    ok = (ids_h >= 0) & (ids_h < w.K)
+    want = np.zeros((3, w.K), dtype=np.int64)
+    for l in range(3):
+        want[l] = np.bincount(ids_h[ok[:, l], l], minlength=w.K)
+    np.testing.assert_array_equal(hist.cpu().numpy(), want)
+
+
+def test_prefix_decode_levels(rvq, dev):
+    w = workloads.random_problem(43, 90, 72, 5, 64)
+    ids_h = np.random.default_rng(6).integers(0, w.K, size=(90, 5)).astype(np.int32)
+    ids = torch.from_numpy(ids_h).to(dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    for levels in (0, 1, 3, 5):
+        out = rvq.rvq_decode(ids, cb, torch.float32, levels=levels)
+        o16 = rvq.rvq_decode(ids, cb, torch.bfloat16, levels=levels)
+        torch.cuda.synchronize()
+        if levels == 0:
+            assert torch.all(out == 0)
+        else:
+            parity.check_decode_f32(out.cpu().numpy(), ids_h, w.codebooks, levels=levels)
+            parity.check_decode_bf16(parity.bf16_tensor_bits(o16), ids_h, w.codebooks, levels=levels)
+
+
+def test_determinism_and_batch_invariance(rvq, dev):
+    w = workloads.random_problem(44, 700, 256, 4, 1500, x_dtype="bf16")
+    ids1, res1, x, cb, prepared = _encode(rvq, w, dev)
+    ids2, res2 = rvq.rvq_encode(x, cb, prepared, residual=True)
+    ids3, res3 = rvq.rvq_encode(x[37:420].contiguous(), cb, prepared, residual=True)
+    ids4, res4 = rvq.rvq_encode(x[699:700].contiguous(), cb, prepared, residual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2) and torch.equal(res1.view(torch.int32), res2.view(torch.int32))
+    assert torch.equal(ids3, ids1[37:420])
+    assert torch.equal(res3.view(torch.int32), res1[37:420].view(torch.int32))
+    assert torch.equal(ids4, ids1[699:700])
