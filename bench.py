@@ -134,13 +134,16 @@ def main() -> int:
     per_step = 2 * L + 5
     ev = HipEvents(per_step * total_steps)
 
+    launches = ctypes.c_int32(0)
+
     def step(k: int):
         base = k * per_step
         m = base + 2 * L
         ev.record(m, sptr)
         rvq.rvq_prepare_codebooks(cb, out=prepared)
         ev.record(m + 1, sptr)
-        rvq.rvq_encode(x, cb, prepared, workspace=ws, ids_out=ids, events=ev.slice(base, 2 * L))
+        rvq.rvq_encode(x, cb, prepared, workspace=ws, ids_out=ids, events=ev.slice(base, 2 * L),
+                       launches=launches)
         ev.record(m + 2, sptr)
         rvq.rvq_decode(ids, cb, torch.bfloat16, out=out)
         ev.record(m + 3, sptr)
@@ -161,14 +164,16 @@ def main() -> int:
     for k in range(args.warmup, total_steps):
         b = k * per_step
         m = b + 2 * L
-        dist_ms += [ev.elapsed_ms(b + 2 * l, b + 2 * l + 1) for l in range(L)]
+        dist_ms += [ev.elapsed_ms(b + 2 * i, b + 2 * i + 1) for i in range(launches.value)]
         prep_ms.append(ev.elapsed_ms(m, m + 1))
         enc_ms.append(ev.elapsed_ms(m + 1, m + 2))
         dec_ms.append(ev.elapsed_ms(m + 2, m + 3))
         st_ms.append(ev.elapsed_ms(m + 3, m + 4))
     ev.close()
     dist_avg = float(np.mean(dist_ms))
-    flops_per_launch = 2.0 * N * K * D
+    # one launch covers all levels when the encoder runs fused, else one level
+    levels_per_launch = L if launches.value == 1 else 1
+    flops_per_launch = 2.0 * N * K * D * levels_per_launch
     achieved = flops_per_launch / (dist_avg * 1e-3) / 1e12
     value = N / (ms_per_step * 1e-3)
 
@@ -188,7 +193,8 @@ def main() -> int:
         "config": {"workload": "native_batch", "images": 16, "N": N, "D": D, "K": K, "L": L,
                    "x_dtype": "bf16", "codebooks": "fp32",
                    "step": "prepare+encode+decode(bf16)+level_stats(counts+msr)"},
-        "roofline": {"bound": "mfma", "kernel": "distance_top2_kernel",
+        "roofline": {"bound": "mfma",
+                     "kernel": "sweep_kernel" + ("<fused: all levels>" if launches.value == 1 else "<one level>"),
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "launch_ms": round(dist_avg, 4),

@@ -18,7 +18,10 @@
  *
  * Readings taken where the pages are silent: the distance is the squared
  * Euclidean distance; there is one [K][d] codebook per level; search is
- * greedy level by level; exact ties go to the lowest codeword index.
+ * greedy level by level.  On an exact tie (e.g. duplicated codewords) the
+ * encoder returns one of the tied codewords: the lower index when two tie,
+ * and a fixed (input-determined, batch-independent) one of them when more
+ * than two tie.
  *
  * Conventions for every entry point:
  *   - Pointers named as device pointers are device memory owned by the
@@ -98,6 +101,8 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
  * products taken on the matrix cores from bf16 copies of r and c with fp32
  * accumulation; the two best-scoring codewords are then rescored exactly in
  * fp32 as sum_i (r_i - c_i)^2 and the smaller wins (lower index on a tie).
+ * The screening keeps each score to 2^-19 relative precision, so which two
+ * codewords are rescored is decided at that precision.
  * The chosen codeword is subtracted from the fp32 residual, which feeds the
  * next level.
  * ---------------------------------------------------------------------- */
@@ -113,6 +118,8 @@ rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K,
  * ids          : device, [n][L] int32 output; ids[row*L + l] in [0, K).
  * residual_out : device, [n][d] fp32 output x - sum_l codebooks[l][ids[l]],
  *                or NULL when not wanted.  16-byte aligned.
+ * d            : 1..1280 (RVQ_ERR_UNSUPPORTED above: a row's features stay
+ *                resident in registers during the sweep).
  * workspace    : device, >= rvq_encode_workspace_size bytes, 256-byte
  *                aligned; contents on entry are ignored.
  */
@@ -122,18 +129,20 @@ rvq_status rvq_encode(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Same as rvq_encode, and additionally records events[2*l] on `stream`
- * immediately before and events[2*l + 1] immediately after the distance
- * kernel of level l (the dense contraction with its top-2 epilogue), for
- * l = 0..L-1.  `events` is a host array of 2*L events created by the caller
- * (hipEventCreate); pass NULL to record nothing.  Used to time the distance
- * stage alone without a profiler.
+ * Same as rvq_encode, and additionally times the distance stage with
+ * caller-created events (hipEventCreate).  The encoder runs either one
+ * launch for all levels (enough rows to fill the GPU: the launch includes
+ * each level's rescoring and residual update) or one distance launch per
+ * level (few rows).  events[2*i] is recorded on `stream` immediately before
+ * and events[2*i + 1] immediately after distance launch i; `events` must
+ * hold 2*L events, or be NULL to record nothing.  *launches (may be NULL)
+ * receives the number of launches recorded (1 or L; 0 when n == 0).
  */
 rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
                                const float *codebooks, const void *prepared, int32_t L, int32_t K,
                                int32_t *ids, float *residual_out,
                                void *workspace, size_t workspace_bytes, hipStream_t stream,
-                               hipEvent_t *events);
+                               hipEvent_t *events, int32_t *launches);
 
 /* ------------------------------------------------------------------------
  * Decode: out[row] = sum_{l < levels} codebooks[l][ids[row*L + l]], summed in
@@ -162,17 +171,18 @@ rvq_status rvq_decode(const int32_t *ids, int64_t n, const float *codebooks,
  *                reduced in a fixed order (bitwise reproducible).
  * ---------------------------------------------------------------------- */
 
-/* Workspace bytes needed by rvq_level_stats (x given or not). */
+/* Workspace bytes needed by rvq_level_stats (with_msr != 0 when msr is requested). */
 rvq_status rvq_level_stats_workspace_size(int64_t n, int32_t L, int32_t K, int32_t d,
                                           int32_t with_msr, size_t *bytes);
 
 /*
  * ids       : device, [n][L] int32.
  * hist      : device, [L][K] int64 output, fully overwritten.  Required.
- * x         : device, [n][d] rows (x_dtype), or NULL to skip msr.
- * codebooks : device, [L][K][d] fp32; required when x is given.
- * msr       : device, [L] fp64 output; required when x is given, else ignored.
+ * msr       : device, [L] fp64 output, or NULL to compute the counts only.
  *             With n == 0 it is all zeros.
+ * x         : device, [n][d] rows (x_dtype); required when msr is non-NULL
+ *             and n > 0, ignored otherwise.
+ * codebooks : device, [L][K][d] fp32; required when msr is non-NULL.
  * bad_ids   : as for rvq_decode.
  * workspace : device, >= rvq_level_stats_workspace_size bytes, 256-byte aligned.
  */

@@ -63,7 +63,7 @@ _lib.rvq_prepare_codebooks.argtypes = [_p, _i32, _i32, _i32, _p, _sz, _p]
 _lib.rvq_encode_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _psz]
 _lib.rvq_encode.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _sz, _p]
 _lib.rvq_encode_profiled.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p,
-                                     _sz, _p, _p]
+                                     _sz, _p, _p, ctypes.POINTER(ctypes.c_int32)]
 _lib.rvq_decode.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _i32, _p, ctypes.c_int, _p, _p]
 _lib.rvq_level_stats_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _psz]
 _lib.rvq_level_stats.argtypes = [_p, _i64, _i32, _i32, _p, _p, ctypes.c_int, _i32, _p, _p, _p,
@@ -143,11 +143,12 @@ def rvq_encode_workspace_size(n: int, d: int, L: int, K: int) -> int:
 
 def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, prepared: Optional[torch.Tensor] = None,
                residual: bool = False, workspace: Optional[torch.Tensor] = None,
-               ids_out: Optional[torch.Tensor] = None, events=None):
+               ids_out: Optional[torch.Tensor] = None, events=None, launches=None):
     """Greedy RVQ encode of rows x [n, d] (fp32 or bf16).  Returns ids [n, L]
     int32, and the fp32 final residual [n, d] when ``residual`` is true.
     ``events``: optional ctypes array of 2*L hipEvent_t recorded around each
-    level's distance kernel (rvq_encode_profiled)."""
+    distance launch; ``launches``: optional ctypes.c_int32 receiving the
+    number of launches recorded (rvq_encode_profiled)."""
     _need_cuda("x", x)
     _need_cuda("codebooks", codebooks)
     L, K, d = codebooks.shape
@@ -164,7 +165,8 @@ def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, prepared: Optional[torc
         workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
     _check(_lib.rvq_encode_profiled(_ptr(x), _dtype_code(x.dtype), n, d, _ptr(codebooks),
                                     _ptr(prepared), L, K, _ptr(ids), _ptr(res), _ptr(workspace),
-                                    workspace.numel(), _stream(dev), events))
+                                    workspace.numel(), _stream(dev), events,
+                                    None if launches is None else ctypes.byref(launches)))
     return (ids, res) if residual else ids
 
 

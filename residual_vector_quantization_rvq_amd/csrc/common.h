@@ -56,42 +56,82 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// ---- tiling constants of the distance kernel (shared with host sizing) ----
-constexpr int kTileCodewords = 256;  // codewords per tile (MFMA M side)
-constexpr int kTileRows = 128;       // rows per tile (MFMA N side)
-constexpr int kStageCols = 32;       // feature columns per LDS stage
-constexpr int kNumXcd = 8;           // workgroups are dispatched round-robin over 8 XCDs
+// ---- prepared codebook stream (shared by every encode kernel) ----
+// Codewords are grouped in tiles of 128 and features in stages of 64.  For
+// level l and tile t the stream holds
+//   [norm k-step: 4 blocks][stage 0: 16 blocks] ... [stage S-1: 16 blocks]
+// where a block is 1 KB = one MFMA A-fragment of v_mfma_f32_32x32x16_bf16
+// for a sub-tile j (32 codewords) and a k-step ks (16 features):
+//   lane L holds 8 bf16 values -2*c[t*128 + j*32 + L%32][s*64 + ks*16 + (L/32)*8 + e].
+// Stage blocks are ordered (j, ks).  Norm block j: lanes L < 32 hold
+// [hi, lo, 0 x 6] with hi = bf16(||c||^2), lo = bf16(||c||^2 - hi) for
+// codeword t*128 + j*32 + L; lanes >= 32 hold zeros.  Multiplied by a
+// B-fragment of ones in the same two positions, the norm k-step adds
+// ||c||^2 to the accumulator, so a sweep accumulates the score
+// ||c||^2 - 2 r.c directly.  Padded codewords (index >= K) are zero
+// vectors with norm kPadNorm, so their score is huge and finite.
+constexpr int kTileCw = 128;
+constexpr int kStageCols = 64;
+constexpr int kBlockBytes = 1024;
+constexpr int kStageBytes = 16 * kBlockBytes;
+constexpr int kNormBytes = 4 * kBlockBytes;
+constexpr int kRowsPerWG = 128;      // 4 waves x 32 rows
+constexpr int kMaxStages = 20;       // features <= 1280
+constexpr float kPadNorm = 3.0e38f;
 
-// Padded sizes of the prepared codebook.
-inline int64_t padded_k(int64_t K) { return round_up(K, kTileCodewords); }
-inline int64_t padded_d(int64_t d) { return round_up(d, kStageCols); }
+// Stage counts (features / 64) with an instantiated encoder; a width is
+// padded with zeros up to the next one (zero features change no distance).
+#define RVQ_FOR_EACH_STAGE_COUNT(X) X(1) X(2) X(4) X(8) X(12) X(16) X(18) X(20)
+__host__ __device__ inline int stages_for(int64_t d) {
+  const int s = (int)ceil_div(d, kStageCols);
+  const int counts[] = {1, 2, 4, 8, 12, 16, 18, 20};
+  for (int c : counts)
+    if (c >= s) return c;
+  return 0;
+}
+__host__ __device__ inline int64_t padded_k(int64_t K) { return round_up(K, kTileCw); }
+__host__ __device__ inline int64_t padded_d(int64_t d) { return (int64_t)stages_for(d) * kStageCols; }
+__host__ __device__ inline int64_t tile_bytes(int stages) { return kNormBytes + (int64_t)stages * kStageBytes; }
+__host__ __device__ inline int64_t stream_bytes(int L, int64_t K, int64_t d) {
+  return (int64_t)L * (padded_k(K) / kTileCw) * tile_bytes((int)(padded_d(d) / kStageCols));
+}
 
 // ---- host-side launchers (return hipGetLastError of their launches) ----
-hipError_t launch_prepare(const float *cb, int L, int K, int d, float *norms, uint16_t *cbh,
-                          hipStream_t s);
-hipError_t launch_init_residual(const void *x, bool x_bf16, int64_t n, int d, int Dp, float *r32,
-                                uint16_t *r16, hipStream_t s);
+hipError_t launch_prepare(const float *cb, int L, int K, int d, float *norms, uint8_t *stream,
+                          float *cbpad, int dp, hipStream_t s);
 
-struct DistPlan {
-  int ktiles;      // codeword tiles per level
-  int tiles_per_wg;
-  int splits;      // partial top-2 lists per row = ceil(ktiles / tiles_per_wg)
+struct EncodePlan {
+  bool fused;          // all levels in one launch
+  int stages;          // feature stages (d padded to 64)
+  int tiles;           // codeword tiles per level
   int row_blocks;
-  int group;       // row blocks per L2-sharing group
-  int per_xcd;     // workgroups per XCD
-  int grid;
+  int splits;          // split mode: workgroups per row block per level
+  int tiles_per_split;
 };
-DistPlan plan_distance(int64_t n, int K, int num_cus);
-hipError_t launch_distance_top2(const DistPlan &p, const uint16_t *r16, int64_t n, int Dp,
-                                const uint16_t *cbh_l, const float *norms_l, float4 *part,
-                                hipStream_t s);
-hipError_t launch_rescore_update(const float4 *part, int splits, int64_t n, int d, int Dp, int K,
-                                 int L, int level, const float *cb_l, const float *r_in,
-                                 float *r_out, uint16_t *r16, bool write_r16, int32_t *ids,
-                                 hipStream_t s);
+EncodePlan plan_encode(int64_t n, int d, int K, int num_cus);
+struct EncodeArgs {
+  const void *x;        // caller's rows [n][d], fp32 or bf16
+  int x_bf16;
+  int64_t n;
+  int d;                // true width
+  int dp;               // row stride seen by the sweep: d rounded up to 16
+  const uint8_t *stream;
+  int L, K;
+  const float *cb;      // fp32 codebooks with row stride dp
+  float *r32;           // fp32 residual [n][dp]
+  float *residual_out;  // caller's [n][d] output or null
+  int32_t *ids;
+  float4 *part;
+  // set by launch_encode
+  const float *src0;    // level-0 rows, fp32 stride dp (x itself or a staged copy)
+  float *res_final;     // where the last level writes its residual (or null)
+};
+hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a, hipEvent_t *events,
+                         hipStream_t s);
+
 hipError_t launch_decode(const int32_t *ids, int64_t n, const float *cb, int L, int K, int d,
                          int levels, void *out, bool out_bf16, uint32_t *bad, hipStream_t s);
 size_t hist_partial_bytes(int64_t n, int L, int K);

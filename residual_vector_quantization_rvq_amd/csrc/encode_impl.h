@@ -1,0 +1,450 @@
+// encode_impl.h -- the encoder kernels (templates instantiated per stage count
+// in the encode_s*.hip units).
+#pragma once
+//
+// Method: "LongCat-2.5 Native Multimodality for Agentic Tasks", section
+// "Visual Primitive Modeling", paragraph "Discrete Native Resolution Vision
+// Transformer" (RVQ on native-resolution features), and "LongCat-2.5 Open
+// Source Release ...", section "02 Visual Coding and 3D" (detail added level
+// by level).  Per level and row r the nearest codeword under the squared
+// Euclidean distance ||r||^2 - 2 r.c + ||c||^2 is chosen; ||r||^2 is the
+// same for every codeword, so codewords are ranked by the score
+// ||c||^2 - 2 r.c.
+//
+// Design (one workgroup = 4 waves = 128 rows, one workgroup per CU):
+//  * Each wave keeps its 32 rows resident in VGPRs as bf16 B-fragments of
+//    v_mfma_f32_32x32x16_bf16 covering the whole feature dimension, so rows
+//    are read from memory once per level, never once per codeword tile.
+//  * The prepared codebook (common.h) is one contiguous stream of A-fragments
+//    per level.  All workgroups sweep it in the same order, so the 32 CUs of
+//    an XCD share every line in L2.  Each 16 KB stage is staged through a
+//    double-buffered LDS ring with register prefetch two stages ahead, and
+//    every wave reads all A-fragments of a stage from LDS (no bank
+//    conflicts: lane L reads bytes 16L..16L+15 of a 1 KB fragment).
+//  * A per-tile norm k-step folds ||c||^2 into the accumulator, so the
+//    accumulator holds the score.  The epilogue packs each score with a
+//    5-bit lane-local codeword tag into a key (score bits 0..4 replaced) and
+//    keeps the two smallest keys per 64-codeword block with v_min / v_med3
+//    (3 VALU ops per score); block winners are merged exactly under the
+//    (key, index) order.
+//  * Fused mode (enough rows to fill the GPU): all levels run in one launch;
+//    after a level's sweep, lanes L and L+32 of a wave rescore their row's
+//    two candidates exactly in fp32 (sum of squared differences, each lane
+//    one half of the features in a fixed order), pick the smaller (lower
+//    index on a tie), subtract it from the fp32 residual and rebuild the
+//    B-fragments for the next level in registers.
+//  * Split mode (few rows): a level's codeword tiles are split over
+//    several workgroups per row block, each writing its top-2 list; a second
+//    kernel merges the lists and runs the same rescoring and update.
+// Every score depends only on (row, codeword): one MFMA shape, one k-step
+// order, one key rule and a total order for merging, so the IDs and
+// residuals are bitwise independent of batch size, row position and mode.
+#include <type_traits>
+
+#include "common.h"
+
+namespace rvq {
+
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ float pack_key(float score, uint32_t tag) {
+  return __uint_as_float((__float_as_uint(score) & ~31u) | tag);
+}
+
+// The row fragments do not fit in the 256 arch VGPRs next to everything
+// else, so the first kFragsInAgpr k-steps live in AGPRs (next to the 64
+// accumulator AGPRs) and feed the MFMA B operand from there; the compiler
+// only emits the VGPR form, hence the MFMAs below are written out.  Each
+// starts with s_nop 3 (covers a VALU write of an operand just before; free
+// while the matrix pipe is busy), and mfma_drain orders the epilogue's
+// reads of the accumulators after the last MFMA's result latency.
+constexpr int kFragsInAgpr = 48;
+
+__device__ __forceinline__ void mfma_first(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+  asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_bv(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+  asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_ba(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+  asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_drain(f32x16 (&acc)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+}
+
+// Row fragments split over AGPRs (k-steps < NA) and VGPRs (the rest).
+template <int KS>
+struct RowFrags {
+  static constexpr int NA = KS < kFragsInAgpr ? KS : kFragsInAgpr;
+  static constexpr int NV = KS - NA;
+  bf16x8 fa[NA];
+  bf16x8 fv[NV > 0 ? NV : 1];
+  template <int k>
+  __device__ __forceinline__ void set(const bf16x8 &v) {
+    if constexpr (k < NA) fa[k] = v;
+    else fv[k - NA] = v;
+  }
+  template <int k>
+  __device__ __forceinline__ void mfma(f32x16 &acc, const bf16x8 &a) {
+    if constexpr (k < NA) mfma_acc_ba(acc, a, fa[k]);
+    else mfma_acc_bv(acc, a, fv[k - NA]);
+  }
+};
+
+// Compile-time loop: f(integral_constant<int, i>) for i in [0, N).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Rows seen by the sweep are fp32 with a stride dp that is a multiple of 16
+// and zero padding past the true width, so a k-step (16 features) is either
+// wholly inside the row or wholly past it -- the same for every lane of a
+// wave -- and every access is an aligned 32-byte vector access.  Reads past
+// the row use a clamped address and select zero, so no lane branches.
+__device__ __forceinline__ void read8(const float *base, int64_t row, int dp, int i0, bool active,
+                                      float (&v)[8]) {
+  const float *p = base + row * dp + (active ? i0 : 0);
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  v[0] = active ? a.x : 0.f; v[1] = active ? a.y : 0.f;
+  v[2] = active ? a.z : 0.f; v[3] = active ? a.w : 0.f;
+  v[4] = active ? b.x : 0.f; v[5] = active ? b.y : 0.f;
+  v[6] = active ? b.z : 0.f; v[7] = active ? b.w : 0.f;
+}
+
+__device__ __forceinline__ void write8(float *base, int64_t row, int dp, int i0,
+                                       const float (&v)[8]) {
+  *reinterpret_cast<float4 *>(base + row * dp + i0) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4 *>(base + row * dp + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&v)[8]) {
+  bf16x8 b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = (__bf16)v[e];
+  return b;
+}
+
+// B-fragments of one row half: lane half h holds features ks*16 + h*8 + e.
+template <int KS>
+__device__ __forceinline__ void build_bfrags(RowFrags<KS> &bfr, const float *src, int64_t row,
+                                             int dp, int h) {
+  static_for<0, KS>([&](auto K_) {
+    constexpr int ks = decltype(K_)::value;
+    float v[8];
+    read8(src, row, dp, ks * 16 + h * 8, ks * 16 < dp, v);
+    bfr.template set<ks>(to_bf16x8(v));
+    // bound the loads the scheduler hoists ahead (register pressure)
+    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Exact fp32 rescoring of the two candidates and residual update for one
+// row; lanes L and L+32 (h = 0, 1) each take features ks*16 + h*8 + e in
+// order ks, e, accumulating (r - c)^2 with fmaf, and the row's distance is
+// (half 0) + (half 1).  Returns the chosen index.  dst (if store) receives
+// r - c_id; with `frags` the next level's B-fragments are rebuilt.
+template <int KS>
+__device__ __forceinline__ int rescore_update(RowFrags<KS> &bfr, bool frags, const float *src,
+                                              float *dst, bool store, int64_t row, int dp,
+                                              const float *cb_l, int c1, int c2, bool v2, int h) {
+  float p1 = 0.f, p2 = 0.f;
+  const int kend = dp >> 4;
+  for (int ks = 0; ks < kend; ++ks) {
+    const int i0 = ks * 16 + h * 8;
+    float r[8], a[8], b[8];
+    read8(src, row, dp, i0, true, r);
+    read8(cb_l, c1, dp, i0, true, a);
+    read8(cb_l, c2, dp, i0, true, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = r[e] - a[e];
+      const float u = r[e] - b[e];
+      p1 = fmaf(t, t, p1);
+      p2 = fmaf(u, u, p2);
+    }
+  }
+  const float q1 = __shfl_xor(p1, 32, 64);
+  const float q2 = __shfl_xor(p2, 32, 64);
+  const float d1 = h ? q1 + p1 : p1 + q1;
+  const float d2 = h ? q2 + p2 : p2 + q2;
+  const int id = (v2 && (d2 < d1 || (d2 == d1 && c2 < c1))) ? c2 : c1;
+  static_for<0, KS>([&](auto K_) {
+    constexpr int ks = decltype(K_)::value;
+    const int i0 = ks * 16 + h * 8;
+    const bool active = ks * 16 < dp;
+    float r[8], c[8], v[8];
+    read8(src, row, dp, i0, active, r);
+    read8(cb_l, id, dp, i0, active, c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = r[e] - c[e];
+    if (store && active) write8(dst, row, dp, i0, v);
+    if (frags) bfr.template set<ks>(to_bf16x8(v));
+    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+  });
+  return id;
+}
+
+// First two candidates of a row's top-2 list as valid codeword indices.
+__device__ __forceinline__ void candidates(int i1, int i2, int K, int &c1, int &c2, bool &v2) {
+  c1 = (i1 >= 0 && i1 < K) ? i1 : 0;  // finite inputs always give a valid first candidate
+  v2 = i2 >= 0 && i2 < K && i2 != i1;
+  c2 = v2 ? i2 : c1;
+}
+
+// ---- LDS ring of codebook stages fed by direct global->LDS loads ----
+// A slot holds one stage (16 KB of A-fragments) after a 4 KB area that
+// receives the tile's norm k-step when the stage starts a tile.  The loads
+// (global_load_lds_dwordx4: lane i's 16 bytes land at M0 + 16*i) are
+// written out because the compiler, unable to tell the slots apart, would
+// otherwise wait for every outstanding load before each LDS read; the
+// waits below are exact per-wave counts instead.
+constexpr int kSlots = 7;                  // stages resident in LDS
+constexpr int kAhead = kSlots - 1;         // stages loaded ahead of the one in use
+constexpr int kSlotBytes = kNormBytes + kStageBytes;
+
+__device__ __forceinline__ void dma16(const uint4 *src, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
+}
+
+// Load instructions one wave issues for a stage: 4 x 1 KB blocks, plus its
+// norm block when the stage starts a tile.
+__host__ __device__ constexpr int dma_count(int s) { return s == 0 ? 5 : 4; }
+
+// Loads issued after stage s's, for the stages s+1 .. s+kAhead-1.
+template <int S>
+__host__ __device__ constexpr int dma_after(int s) {
+  int c = 0;
+  for (int k = 1; k < kAhead; ++k) c += dma_count((s + k) % S);
+  return c;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Issue this wave's loads of stream stage (tt, s) into ring slot `slot`.
+__device__ __forceinline__ void issue_stage(const uint4 *ls, int64_t tile_u4, int tt, int s,
+                                            int slot, uint32_t ring_lds, int wave, int lane) {
+  const uint4 *tp = ls + (int64_t)tt * tile_u4;
+  const uint4 *sp = tp + 256 + (int64_t)s * 1024 + wave * 256 + lane;
+  const uint32_t base = ring_lds + (uint32_t)slot * kSlotBytes;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    dma16(sp + q * 64, base + kNormBytes + (uint32_t)(wave * 4 + q) * kBlockBytes);
+  if (s == 0) dma16(tp + wave * 64 + lane, base + (uint32_t)wave * kBlockBytes);
+}
+
+}  // namespace
+
+template <int S, bool FUSED>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void sweep_kernel(
+    EncodeArgs a, int T, int level, int splits, int tiles_per_split) {
+  constexpr int KS = 4 * S;
+  __shared__ uint4 ring[kSlots * (kSlotBytes / 16)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int rb, sp;
+  if (FUSED) {
+    rb = blockIdx.x;
+    sp = 0;
+  } else {
+    rb = blockIdx.x / splits;
+    sp = blockIdx.x % splits;
+  }
+  const int64_t row = (int64_t)rb * kRowsPerWG + wave * 32 + (lane & 31);
+  const bool live = row < a.n;
+  const int64_t rowc = live ? row : a.n - 1;
+  const int t0 = FUSED ? 0 : sp * tiles_per_split;
+  const int t1 = FUSED ? T : min(T, t0 + tiles_per_split);
+  const int ntiles = t1 - t0;
+  const int nst = ntiles * S;
+  const int l_begin = FUSED ? 0 : level;
+  const int l_end = FUSED ? a.L : level + 1;
+  const int64_t tile_u4 = tile_bytes(S) / 16;
+  const uint32_t ring_lds = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4 *)ring);
+
+  RowFrags<KS> bfr;
+  build_bfrags<KS>(bfr, l_begin == 0 ? a.src0 : a.r32, rowc, a.dp, h);
+  bf16x8 bnorm;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bnorm[e] = (__bf16)((h == 0 && e < 2) ? 1.0f : 0.0f);
+
+  const uint4 *ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l_begin * T + t0) * tile_u4;
+  // prologue of the first level: stages 0 .. kAhead-1
+  static_for<0, kAhead>([&](auto K_) {
+    constexpr int k = decltype(K_)::value;
+    if (k < nst) issue_stage(ls, tile_u4, k / S, k % S, k, ring_lds, wave, lane);
+  });
+
+  for (int l = l_begin; l < l_end; ++l) {
+    ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l * T + t0) * tile_u4;
+    float S1 = __builtin_inff(), S2 = __builtin_inff();
+    int I1 = kNoIndex, I2 = kNoIndex;
+
+    int slot_t = 0;  // ring slot of the current tile's stage 0
+    for (int tt = 0; tt < ntiles; ++tt) {
+      f32x16 acc[4];
+      static_for<0, S>([&](auto S_) {
+        constexpr int s = decltype(S_)::value;
+        const int g = tt * S + s;
+        // this wave's loads of stage g are done once at most dma_after<S>(s)
+        // newer ones are outstanding; at the start of a level (update-phase
+        // accesses may be interleaved) and near the end wait for all
+        if (g == 0 || g + kAhead - 1 >= nst) wait_vmcnt<0>();
+        else wait_vmcnt<dma_after<S>(s)>();
+        barrier_only();
+        int slot = slot_t + s % kSlots;
+        slot = slot >= kSlots ? slot - kSlots : slot;
+        const uint4 *st = ring + slot * (kSlotBytes / 16);
+        if constexpr (s == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            mfma_first(acc[j], __builtin_bit_cast(bf16x8, st[j * 64 + lane]), bnorm);
+        }
+        static_for<0, 4>([&](auto KS_) {
+          constexpr int ks = decltype(KS_)::value;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            bfr.template mfma<s * 4 + ks>(
+                acc[j], __builtin_bit_cast(bf16x8, st[256 + (j * 4 + ks) * 64 + lane]));
+        });
+        // refill the slot freed by stage g-1 with stage g + kAhead
+        if (g + kAhead < nst) {
+          int nslot = slot + kAhead;
+          nslot = nslot >= kSlots ? nslot - kSlots : nslot;
+          issue_stage(ls, tile_u4, tt + (s + kAhead) / S, (s + kAhead) % S, nslot, ring_lds,
+                      wave, lane);
+        }
+      });
+      slot_t += S % kSlots;
+      slot_t = slot_t >= kSlots ? slot_t - kSlots : slot_t;
+      mfma_drain(acc);
+
+      // Epilogue: accumulator element i of sub-tile j is codeword
+      // j*32 + (i/4)*8 + h*4 + i%4 of the tile for this lane's row.  Per
+      // 64-codeword block p (sub-tiles 2p, 2p+1) the tag jj*16 + i is unique.
+      const int tbase = (t0 + tt) * kTileCw;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float k1 = __builtin_inff(), k2 = __builtin_inff();
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float key = pack_key(acc[2 * p + jj][i], (uint32_t)(jj * 16 + i));
+            k2 = __builtin_amdgcn_fmed3f(k1, k2, key);
+            k1 = fminf(k1, key);
+          }
+        }
+        const uint32_t g1 = __float_as_uint(k1) & 31u, g2 = __float_as_uint(k2) & 31u;
+        const int bb = tbase + p * 64 + h * 4;
+        const int j1 = bb + (int)((g1 >> 4) * 32 + ((g1 >> 2) & 3) * 8 + (g1 & 3));
+        const int j2 = bb + (int)((g2 >> 4) * 32 + ((g2 >> 2) & 3) * 8 + (g2 & 3));
+        merge_top2(S1, I1, S2, I2, k1, j1, k2, j2);
+      }
+    }
+
+    // Lanes L and L+32 hold the same row over disjoint codewords.
+    {
+      const float t1 = __shfl_xor(S1, 32, 64), t2 = __shfl_xor(S2, 32, 64);
+      const int j1 = __shfl_xor(I1, 32, 64), j2 = __shfl_xor(I2, 32, 64);
+      merge_top2(S1, I1, S2, I2, t1, j1, t2, j2);
+    }
+
+    if (FUSED && l + 1 < l_end) {
+      // every wave is done with the ring; start streaming the next level
+      // while this level's rescoring and update run
+      barrier_only();
+      const uint4 *ln = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)(l + 1) * T + t0) * tile_u4;
+      static_for<0, kAhead>([&](auto K_) {
+        constexpr int k = decltype(K_)::value;
+        if (k < nst) issue_stage(ln, tile_u4, k / S, k % S, k, ring_lds, wave, lane);
+      });
+    }
+    if (FUSED) {
+      int c1, c2;
+      bool v2;
+      candidates(I1, I2, a.K, c1, c2, v2);
+      const bool last = l == a.L - 1;
+      float *dst = last ? a.res_final : a.r32;
+      const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
+      const int id = rescore_update<KS>(bfr, !last, l == 0 ? a.src0 : a.r32, dst,
+                                        live && dst != nullptr, rowc, a.dp, cb_l, c1, c2, v2, h);
+      if (live && h == 0) a.ids[row * a.L + l] = id;
+    } else {
+      if (live && h == 0)
+        a.part[row * splits + sp] = make_float4(S1, __int_as_float(I1), S2, __int_as_float(I2));
+    }
+  }
+}
+
+// Split mode, after every split of a level wrote its list: merge the lists
+// (a total order, so any merge order gives the same result) and run the
+// same rescoring and update as the fused kernel.
+template <int S>
+__global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int level, int splits) {
+  constexpr int KS = 4 * S;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWG + wave * 32 + (lane & 31);
+  const bool live = row < a.n;
+  const int64_t rowc = live ? row : a.n - 1;
+  float S1 = __builtin_inff(), S2 = __builtin_inff();
+  int I1 = kNoIndex, I2 = kNoIndex;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float4 p = a.part[rowc * splits + sp];
+    merge_top2(S1, I1, S2, I2, p.x, __float_as_int(p.y), p.z, __float_as_int(p.w));
+  }
+  int c1, c2;
+  bool v2;
+  candidates(I1, I2, a.K, c1, c2, v2);
+  const bool last = level == a.L - 1;
+  float *dst = last ? a.res_final : a.r32;
+  const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
+  RowFrags<KS> unused;
+  const int id = rescore_update<KS>(unused, false, level == 0 ? a.src0 : a.r32, dst,
+                                    live && dst != nullptr, rowc, a.dp, cb_l, c1, c2, v2, h);
+  if (live && h == 0) a.ids[row * a.L + level] = id;
+}
+
+template <int S>
+hipError_t launch_stage_count(const EncodePlan &p, const EncodeArgs &a, hipEvent_t *ev, hipStream_t s) {
+  hipError_t e;
+  if (p.fused) {
+    if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
+    sweep_kernel<S, true><<<dim3(p.row_blocks), dim3(NT), 0, s>>>(a, p.tiles, 0, 1, p.tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
+    return hipSuccess;
+  }
+  for (int l = 0; l < a.L; ++l) {
+    if (ev && (e = hipEventRecord(ev[2 * l], s)) != hipSuccess) return e;
+    sweep_kernel<S, false><<<dim3(p.row_blocks * p.splits), dim3(NT), 0, s>>>(
+        a, p.tiles, l, p.splits, p.tiles_per_split);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[2 * l + 1], s)) != hipSuccess) return e;
+    split_update_kernel<S><<<dim3(p.row_blocks), dim3(NT), 0, s>>>(a, l, p.splits);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+
+}  // namespace rvq

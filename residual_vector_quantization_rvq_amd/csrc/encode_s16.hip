@@ -1,0 +1,7 @@
+// encode_s16.hip -- encoder instantiations for stage counts 16 (one unit per group so they compile in parallel).
+#include "encode_impl.h"
+
+namespace rvq {
+template hipError_t launch_stage_count<16>(const EncodePlan &, const EncodeArgs &, hipEvent_t *,
+                                            hipStream_t);
+}  // namespace rvq

@@ -41,12 +41,12 @@ rvq_status check_shape(int64_t n, int32_t d, int32_t L, int32_t K) {
   if (d < 1) return fail(RVQ_ERR_INVALID_ARGUMENT, "d must be >= 1 (got %d)", d);
   if (L < 1) return fail(RVQ_ERR_INVALID_ARGUMENT, "L must be >= 1 (got %d)", L);
   if (K < 1) return fail(RVQ_ERR_INVALID_ARGUMENT, "K must be >= 1 (got %d)", K);
-  if (K > INT32_MAX - kTileCodewords)
+  if (K > INT32_MAX - kTileCw)
     return fail(RVQ_ERR_UNSUPPORTED, "K too large (got %d)", K);
   if (n > kMaxRows)
     return fail(RVQ_ERR_UNSUPPORTED, "n above %lld rows per call (got %lld)", (long long)kMaxRows,
                 (long long)n);
-  if ((int64_t)L * padded_k(K) * padded_d(d) > ((int64_t)1 << 40))
+  if (stream_bytes(L, K, d) > ((int64_t)1 << 40))
     return fail(RVQ_ERR_UNSUPPORTED, "codebook too large");
   return RVQ_OK;
 }
@@ -70,29 +70,35 @@ rvq_status need(const void *p, const char *name, size_t align) {
     if (_e != hipSuccess) return hip_fail(_e, what); \
   } while (0)
 
+// Row stride of the fp32 rows and codewords the encoder reads.
+int32_t row_stride(int32_t d) { return (int32_t)round_up(d, 16); }
+
+// Prepared buffer: norms [L][Kp] fp32, the fragment stream, and (only when
+// d is not a multiple of 16) an fp32 copy of the codebooks with stride dp.
 struct PreparedLayout {
-  size_t norms_off, cbh_off, total;
+  size_t norms_off, stream_off, cbpad_off, total;
 };
 PreparedLayout prepared_layout(int32_t L, int32_t K, int32_t d) {
   PreparedLayout p;
-  const size_t Kp = (size_t)padded_k(K), Dp = (size_t)padded_d(d);
   p.norms_off = 0;
-  p.cbh_off = align256((size_t)L * Kp * sizeof(float));
-  p.total = p.cbh_off + align256((size_t)L * Kp * Dp * sizeof(uint16_t));
+  p.stream_off = align256((size_t)L * (size_t)padded_k(K) * sizeof(float));
+  p.cbpad_off = p.stream_off + align256((size_t)stream_bytes(L, K, d));
+  const int32_t dp = row_stride(d);
+  p.total = p.cbpad_off + (dp != d ? align256((size_t)L * K * dp * sizeof(float)) : 0);
   return p;
 }
 
 struct EncodeLayout {
-  size_t r32_off, r16_off, part_off, total;
+  size_t r32_off, part_off, total;
 };
+// Workspace: the fp32 residual [n][d] and, for the split plan, one top-2
+// list per row and codeword tile [n][tiles] (the largest split count).
 EncodeLayout encode_layout(int64_t n, int32_t d, int32_t K) {
   EncodeLayout w;
-  const size_t Dp = (size_t)padded_d(d);
-  const size_t ktiles = (size_t)ceil_div(K, kTileCodewords);
+  const size_t tiles = (size_t)(padded_k(K) / kTileCw);
   w.r32_off = 0;
-  w.r16_off = align256((size_t)n * d * sizeof(float));
-  w.part_off = w.r16_off + align256((size_t)n * Dp * sizeof(uint16_t));
-  w.total = w.part_off + align256((size_t)n * ktiles * sizeof(float4));
+  w.part_off = align256((size_t)n * row_stride(d) * sizeof(float));
+  w.total = w.part_off + align256((size_t)n * tiles * sizeof(float4));
   if (w.total == 0) w.total = 256;
   return w;
 }
@@ -104,6 +110,8 @@ int num_cus() {
     return 256;
   return cus > 0 ? cus : 256;
 }
+
+rvq_status check_encode_width(int32_t d);
 
 }  // namespace
 
@@ -122,8 +130,18 @@ const char *rvq_status_string(rvq_status s) {
 
 const char *rvq_last_error(void) { return g_err; }
 
+namespace {
+rvq_status check_encode_width(int32_t d) {
+  if (stages_for(d) == 0)
+    return fail(RVQ_ERR_UNSUPPORTED, "encode supports d <= %d (got %d)", kMaxStages * kStageCols,
+                d);
+  return RVQ_OK;
+}
+}  // namespace
+
 rvq_status rvq_prepared_size(int32_t L, int32_t K, int32_t d, size_t *bytes) {
   RVQ_TRY(check_shape(0, d, L, K));
+  RVQ_TRY(check_encode_width(d));
   if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
   *bytes = prepared_layout(L, K, d).total;
   return RVQ_OK;
@@ -132,6 +150,7 @@ rvq_status rvq_prepared_size(int32_t L, int32_t K, int32_t d, size_t *bytes) {
 rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, int32_t d,
                                  void *prepared, size_t prepared_bytes, hipStream_t stream) {
   RVQ_TRY(check_shape(0, d, L, K));
+  RVQ_TRY(check_encode_width(d));
   RVQ_TRY(need(codebooks, "codebooks", 16));
   RVQ_TRY(need(prepared, "prepared", 256));
   const PreparedLayout pl = prepared_layout(L, K, d);
@@ -139,14 +158,17 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
     return fail(RVQ_ERR_WORKSPACE_TOO_SMALL, "prepared buffer needs %zu bytes (got %zu)", pl.total,
                 prepared_bytes);
   char *base = (char *)prepared;
+  const int32_t dp = row_stride(d);
   HIP_TRY(launch_prepare(codebooks, L, K, d, (float *)(base + pl.norms_off),
-                         (uint16_t *)(base + pl.cbh_off), stream),
-          "prepare_kernel launch");
+                         (uint8_t *)(base + pl.stream_off),
+                         dp != d ? (float *)(base + pl.cbpad_off) : nullptr, dp, stream),
+          "codebook preparation launch");
   return RVQ_OK;
 }
 
 rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K, size_t *bytes) {
   RVQ_TRY(check_shape(n, d, L, K));
+  RVQ_TRY(check_encode_width(d));
   if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
   *bytes = encode_layout(n, d, K).total;
   return RVQ_OK;
@@ -155,8 +177,10 @@ rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K,
 rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
                                const float *codebooks, const void *prepared, int32_t L, int32_t K,
                                int32_t *ids, float *residual_out, void *workspace,
-                               size_t workspace_bytes, hipStream_t stream, hipEvent_t *events) {
+                               size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
+                               int32_t *launches) {
   RVQ_TRY(check_shape(n, d, L, K));
+  RVQ_TRY(check_encode_width(d));
   if (x_dtype != RVQ_F32 && x_dtype != RVQ_BF16)
     return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown x_dtype %d", (int)x_dtype);
   RVQ_TRY(need(codebooks, "codebooks", 16));
@@ -172,34 +196,28 @@ rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int3
   if (workspace_bytes < wl.total)
     return fail(RVQ_ERR_WORKSPACE_TOO_SMALL, "encode workspace needs %zu bytes (got %zu)",
                 wl.total, workspace_bytes);
+  if (launches) *launches = 0;
   if (n == 0) return RVQ_OK;
 
-  const int Dp = (int)padded_d(d);
-  const int64_t Kp = padded_k(K);
   const PreparedLayout pl = prepared_layout(L, K, d);
-  const float *norms = (const float *)((const char *)prepared + pl.norms_off);
-  const uint16_t *cbh = (const uint16_t *)((const char *)prepared + pl.cbh_off);
   char *ws = (char *)workspace;
-  float *r32 = (float *)(ws + wl.r32_off);
-  uint16_t *r16 = (uint16_t *)(ws + wl.r16_off);
-  float4 *part = (float4 *)(ws + wl.part_off);
-
-  const DistPlan plan = plan_distance(n, K, num_cus());
-  HIP_TRY(launch_init_residual(x, x_dtype == RVQ_BF16, n, d, Dp, r32, r16, stream),
-          "init_residual_kernel launch");
-  for (int l = 0; l < L; ++l) {
-    if (events) HIP_TRY(hipEventRecord(events[2 * l], stream), "hipEventRecord");
-    HIP_TRY(launch_distance_top2(plan, r16, n, Dp, cbh + (int64_t)l * Kp * Dp, norms + l * Kp,
-                                 part, stream),
-            "distance_top2_kernel launch");
-    if (events) HIP_TRY(hipEventRecord(events[2 * l + 1], stream), "hipEventRecord");
-    const bool last = l == L - 1;
-    float *r_out = (last && residual_out) ? residual_out : r32;
-    HIP_TRY(launch_rescore_update(part, plan.splits, n, d, Dp, K, L, l,
-                                  codebooks + (int64_t)l * K * d, r32, r_out, r16, !last, ids,
-                                  stream),
-            "rescore_update_kernel launch");
-  }
+  EncodeArgs a;
+  a.x = x;
+  a.x_bf16 = x_dtype == RVQ_BF16 ? 1 : 0;
+  a.n = n;
+  a.d = d;
+  a.dp = row_stride(d);
+  a.stream = (const uint8_t *)prepared + pl.stream_off;
+  a.L = L;
+  a.K = K;
+  a.cb = a.dp != d ? (const float *)((const char *)prepared + pl.cbpad_off) : codebooks;
+  a.r32 = (float *)(ws + wl.r32_off);
+  a.residual_out = residual_out;
+  a.ids = ids;
+  a.part = (float4 *)(ws + wl.part_off);
+  const EncodePlan plan = plan_encode(n, d, K, num_cus());
+  HIP_TRY(launch_encode(plan, a, events, stream), "encode launch");
+  if (launches) *launches = plan.fused ? 1 : L;
   return RVQ_OK;
 }
 
@@ -208,7 +226,7 @@ rvq_status rvq_encode(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
                       int32_t *ids, float *residual_out, void *workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   return rvq_encode_profiled(x, x_dtype, n, d, codebooks, prepared, L, K, ids, residual_out,
-                             workspace, workspace_bytes, stream, nullptr);
+                             workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 rvq_status rvq_decode(const int32_t *ids, int64_t n, const float *codebooks, int32_t L, int32_t K,
@@ -249,7 +267,7 @@ rvq_status rvq_level_stats(const int32_t *ids, int64_t n, int32_t L, int32_t K, 
                            const void *x, rvq_dtype x_dtype, int32_t d, const float *codebooks,
                            double *msr, uint32_t *bad_ids, void *workspace, size_t workspace_bytes,
                            hipStream_t stream) {
-  const bool with_msr = x != nullptr;
+  const bool with_msr = msr != nullptr;
   RVQ_TRY(check_shape(n, with_msr ? d : 1, L, K));
   if (L > kMaxLevelsGather)
     return fail(RVQ_ERR_UNSUPPORTED, "level statistics support L <= %d (got %d)",

@@ -35,24 +35,31 @@ def test_status_strings(rvq):
 
 
 def test_prepared_size_layout(rvq):
-    # norms [L][Kp] fp32 then bf16 [L][Kp][Dp], each rounded up to 256 bytes
+    # norms [L][K rounded up to 128] fp32, then per level and 128-codeword
+    # tile a 4 KB norm k-step and one 16 KB stage per 64 features (stage
+    # counts 1, 2, 4, 8, 12, 16, 18, 20), each part rounded up to 256 bytes
+    al = lambda v: (v + 255) // 256 * 256
     L, K, d = 8, 8192, 1152
-    assert rvq.rvq_prepared_size(L, K, d) == L * K * 4 + L * K * d * 2
-    # padding: K -> multiple of 256, d -> multiple of 32
+    assert rvq.rvq_prepared_size(L, K, d) == L * K * 4 + L * (K // 128) * (4096 + 18 * 16384)
+    # d = 70: 2 stages; rows not a multiple of 16 wide also get an fp32
+    # codebook copy with row stride 80
     L, K, d = 3, 300, 70
-    Kp, Dp = 512, 96
-    norms = (L * Kp * 4 + 255) // 256 * 256
-    cbh = (L * Kp * Dp * 2 + 255) // 256 * 256
-    assert rvq.rvq_prepared_size(L, K, d) == norms + cbh
+    assert rvq.rvq_prepared_size(L, K, d) == (al(L * 384 * 4) + al(L * 3 * (4096 + 2 * 16384))
+                                              + al(L * K * 80 * 4))
+    # d = 640 needs 10 stages, padded to the next instantiated count (12)
+    assert rvq.rvq_prepared_size(1, 128, 640) == al(128 * 4) + al(4096 + 12 * 16384)
+    with pytest.raises(rvq.RVQError) as e:
+        rvq.rvq_prepared_size(1, 128, 1281)
+    assert e.value.status == 2
 
 
 def test_encode_workspace_size(rvq):
-    n, d, L, K = 1000, 64, 4, 256
-    r32 = n * d * 4
-    r16 = n * d * 2
-    part = n * 1 * 16
+    # fp32 residual [n][d rounded up to 16] and one top-2 list per row and
+    # 128-codeword tile
     al = lambda v: (v + 255) // 256 * 256
-    assert rvq.rvq_encode_workspace_size(n, d, L, K) == al(r32) + al(r16) + al(part)
+    n, d, L, K = 1000, 64, 4, 256
+    assert rvq.rvq_encode_workspace_size(n, d, L, K) == al(n * 64 * 4) + al(n * 2 * 16)
+    assert rvq.rvq_encode_workspace_size(10, 70, 2, 300) == al(10 * 80 * 4) + al(10 * 3 * 16)
     assert rvq.rvq_encode_workspace_size(0, d, L, K) == 256
 
 
