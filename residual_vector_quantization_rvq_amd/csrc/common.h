@@ -121,7 +121,7 @@ struct EncodeArgs {
   const uint8_t *stream;
   int L, K;
   const float *cb;      // fp32 codebooks with row stride dp
-  float *r32;           // fp32 residual [n][dp]
+  float *rbuf[2];       // fp32 residuals [n][dp]: level l reads rbuf[l & 1], writes rbuf[(l+1) & 1]
   float *residual_out;  // caller's [n][d] output or null
   int32_t *ids;
   float4 *part;

@@ -73,18 +73,23 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   EncodeArgs a = a_in;
   const unsigned row_waves = (unsigned)ceil_div(a.n, 4);
   if (a.x_bf16 || a.dp != a.d) {
-    stage_input_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(a.x, a.x_bf16, a.n, a.d, a.dp, a.r32);
-    a.src0 = a.r32;
+    stage_input_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(a.x, a.x_bf16, a.n, a.d, a.dp,
+                                                           a.rbuf[0]);
+    a.src0 = a.rbuf[0];
   } else {
     a.src0 = (const float *)a.x;
   }
+  // the last level reads rbuf[(L-1) & 1] and writes the final residual to
+  // the caller's buffer, or (padded width) to the other buffer first
   const bool unpad = a.residual_out && a.dp != a.d;
-  a.res_final = unpad ? a.r32 : a.residual_out;
+  float *padded_final = a.rbuf[a.L & 1];
+  a.res_final = unpad ? padded_final : a.residual_out;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_stages(p, a, events, s);
   if (e != hipSuccess || !unpad) return e;
-  unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(a.r32, a.n, a.d, a.dp, a.residual_out);
+  unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(padded_final, a.n, a.d, a.dp,
+                                                     a.residual_out);
   return hipGetLastError();
 }
 

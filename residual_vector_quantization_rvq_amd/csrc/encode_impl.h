@@ -56,42 +56,127 @@ __device__ __forceinline__ float pack_key(float score, uint32_t tag) {
 // The row fragments do not fit in the 256 arch VGPRs next to everything
 // else, so the first kFragsInAgpr k-steps live in AGPRs (next to the 64
 // accumulator AGPRs) and feed the MFMA B operand from there; the compiler
-// only emits the VGPR form, hence the MFMAs below are written out.  Each
-// starts with s_nop 3 (covers a VALU write of an operand just before; free
-// while the matrix pipe is busy), and mfma_drain orders the epilogue's
-// reads of the accumulators after the last MFMA's result latency.
+// only emits the VGPR form, so a stage's MFMAs are written out below.  A
+// fragment is one 128-bit value (8 bf16 packed in 4 words).
 constexpr int kFragsInAgpr = 48;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void mfma_first(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-  asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "v"(b));
+// One stage (4 k-steps x 4 sub-tiles) for this lane: A-fragments are read
+// from the ring slot at addr (slot base + 16*lane) with 8 LDS reads in
+// flight in two alternating sets, so the next k-step's reads overlap the
+// current k-step's 4 MFMAs; every read has completed when the block ends.
+#define RVQ_STAGE_ASM                                                                  \
+      "ds_read_b128 %[t0], %[addr] offset:4096\n\t" \
+      "ds_read_b128 %[t1], %[addr] offset:8192\n\t" \
+      "ds_read_b128 %[t2], %[addr] offset:12288\n\t" \
+      "ds_read_b128 %[t3], %[addr] offset:16384\n\t" \
+      "ds_read_b128 %[t4], %[addr] offset:5120\n\t" \
+      "ds_read_b128 %[t5], %[addr] offset:9216\n\t" \
+      "ds_read_b128 %[t6], %[addr] offset:13312\n\t" \
+      "ds_read_b128 %[t7], %[addr] offset:17408\n\t" \
+      "s_waitcnt lgkmcnt(4)\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c0], %[t0], %[b0], %[c0]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c1], %[t1], %[b0], %[c1]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c2], %[t2], %[b0], %[c2]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c3], %[t3], %[b0], %[c3]\n\t" \
+      "ds_read_b128 %[t0], %[addr] offset:6144\n\t" \
+      "ds_read_b128 %[t1], %[addr] offset:10240\n\t" \
+      "ds_read_b128 %[t2], %[addr] offset:14336\n\t" \
+      "ds_read_b128 %[t3], %[addr] offset:18432\n\t" \
+      "s_waitcnt lgkmcnt(4)\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c0], %[t4], %[b1], %[c0]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c1], %[t5], %[b1], %[c1]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c2], %[t6], %[b1], %[c2]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c3], %[t7], %[b1], %[c3]\n\t" \
+      "ds_read_b128 %[t4], %[addr] offset:7168\n\t" \
+      "ds_read_b128 %[t5], %[addr] offset:11264\n\t" \
+      "ds_read_b128 %[t6], %[addr] offset:15360\n\t" \
+      "ds_read_b128 %[t7], %[addr] offset:19456\n\t" \
+      "s_waitcnt lgkmcnt(4)\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c0], %[t0], %[b2], %[c0]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c1], %[t1], %[b2], %[c1]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c2], %[t2], %[b2], %[c2]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c3], %[t3], %[b2], %[c3]\n\t" \
+      "s_waitcnt lgkmcnt(0)\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c0], %[t4], %[b3], %[c0]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c1], %[t5], %[b3], %[c1]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c2], %[t6], %[b3], %[c2]\n\t" \
+      "v_mfma_f32_32x32x16_bf16 %[c3], %[t7], %[b3], %[c3]\n\t"
+
+#define RVQ_STAGE_OUTS(c)                                                               \
+  [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]),                \
+      [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]),         \
+      [t4] "=&v"(t[4]), [t5] "=&v"(t[5]), [t6] "=&v"(t[6]), [t7] "=&v"(t[7])
+
+template <bool B_IN_AGPR>
+__device__ __forceinline__ void stage_mfma(f32x16 (&c)[4], uint32_t addr, const u32x4 &b0,
+                                           const u32x4 &b1, const u32x4 &b2, const u32x4 &b3) {
+  u32x4 t[8];
+  if constexpr (B_IN_AGPR)
+    asm volatile(RVQ_STAGE_ASM
+                 : RVQ_STAGE_OUTS(c)
+                 : [addr] "v"(addr), [b0] "a"(b0), [b1] "a"(b1), [b2] "a"(b2), [b3] "a"(b3));
+  else
+    asm volatile(RVQ_STAGE_ASM
+                 : RVQ_STAGE_OUTS(c)
+                 : [addr] "v"(addr), [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3));
 }
-__device__ __forceinline__ void mfma_acc_bv(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-  asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+
+// The norm k-step opening a tile: accumulators start from ||c||^2.
+__device__ __forceinline__ void norm_mfma(f32x16 (&c)[4], uint32_t addr, const u32x4 &bn) {
+  u32x4 t[4];
+  asm volatile("ds_read_b128 %[t0], %[addr] offset:0\n\t"
+               "ds_read_b128 %[t1], %[addr] offset:1024\n\t"
+               "ds_read_b128 %[t2], %[addr] offset:2048\n\t"
+               "ds_read_b128 %[t3], %[addr] offset:3072\n\t"
+               "s_waitcnt lgkmcnt(0)\n\t"
+               "v_mfma_f32_32x32x16_bf16 %[c0], %[t0], %[bn], 0\n\t"
+               "v_mfma_f32_32x32x16_bf16 %[c1], %[t1], %[bn], 0\n\t"
+               "v_mfma_f32_32x32x16_bf16 %[c2], %[t2], %[bn], 0\n\t"
+               "v_mfma_f32_32x32x16_bf16 %[c3], %[t3], %[bn], 0\n\t"
+               : [c0] "=&a"(c[0]), [c1] "=&a"(c[1]), [c2] "=&a"(c[2]), [c3] "=&a"(c[3]),
+                 [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3])
+               : [addr] "v"(addr), [bn] "v"(bn));
 }
-__device__ __forceinline__ void mfma_acc_ba(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-  asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "a"(b));
-}
+
+// Orders the epilogue's accumulator reads after the last MFMA's result
+// latency (the compiler does not see the MFMAs above).
 __device__ __forceinline__ void mfma_drain(f32x16 (&acc)[4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
 }
 
-// Row fragments split over AGPRs (k-steps < NA) and VGPRs (the rest).
+// Row fragments split over AGPRs (k-steps < NA) and VGPRs (the rest); NA
+// is a multiple of 4 so a stage's four k-steps sit in one register file.
 template <int KS>
 struct RowFrags {
   static constexpr int NA = KS < kFragsInAgpr ? KS : kFragsInAgpr;
   static constexpr int NV = KS - NA;
-  bf16x8 fa[NA];
-  bf16x8 fv[NV > 0 ? NV : 1];
+  u32x4 fa[NA];
+  u32x4 fv[NV > 0 ? NV : 1];
+  // The empty asm pins a new fragment to its register file from the start
+  // (an AGPR-class value never needs copying before an MFMA that reads it).
   template <int k>
-  __device__ __forceinline__ void set(const bf16x8 &v) {
-    if constexpr (k < NA) fa[k] = v;
-    else fv[k - NA] = v;
+  __device__ __forceinline__ void set(const u32x4 &v) {
+    u32x4 t = v;
+    if constexpr (k < NA) {
+      asm volatile("" : "+a"(t));
+      fa[k] = t;
+    } else {
+      asm volatile("" : "+v"(t));
+      fv[k - NA] = t;
+    }
   }
   template <int k>
-  __device__ __forceinline__ void mfma(f32x16 &acc, const bf16x8 &a) {
-    if constexpr (k < NA) mfma_acc_ba(acc, a, fa[k]);
-    else mfma_acc_bv(acc, a, fv[k - NA]);
+  __device__ __forceinline__ const u32x4 &get() const {
+    if constexpr (k < NA) return fa[k];
+    else return fv[k - NA];
+  }
+  template <int s>
+  __device__ __forceinline__ void stage(f32x16 (&c)[4], uint32_t addr) const {
+    static_assert(NA % 4 == 0, "a stage's k-steps must share a register file");
+    stage_mfma<(s * 4 < NA)>(c, addr, get<s * 4>(), get<s * 4 + 1>(), get<s * 4 + 2>(),
+                             get<s * 4 + 3>());
   }
 };
 
@@ -126,11 +211,15 @@ __device__ __forceinline__ void write8(float *base, int64_t row, int dp, int i0,
   *reinterpret_cast<float4 *>(base + row * dp + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const float (&v)[8]) {
-  bf16x8 b;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 to_bf16x8(const float (&v)[8]) {
+  u32x4 q;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) b[e] = (__bf16)v[e];
-  return b;
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 p = {(__bf16)v[2 * e], (__bf16)v[2 * e + 1]};
+    q[e] = __builtin_bit_cast(uint32_t, p);
+  }
+  return q;
 }
 
 // B-fragments of one row half: lane half h holds features ks*16 + h*8 + e.
@@ -150,17 +239,19 @@ __device__ __forceinline__ void build_bfrags(RowFrags<KS> &bfr, const float *src
 // Exact fp32 rescoring of the two candidates and residual update for one
 // row; lanes L and L+32 (h = 0, 1) each take features ks*16 + h*8 + e in
 // order ks, e, accumulating (r - c)^2 with fmaf, and the row's distance is
-// (half 0) + (half 1).  Returns the chosen index.  dst (if store) receives
-// r - c_id; with `frags` the next level's B-fragments are rebuilt.
-template <int KS>
-__device__ __forceinline__ int rescore_update(RowFrags<KS> &bfr, bool frags, const float *src,
-                                              float *dst, bool store, int64_t row, int dp,
-                                              const float *cb_l, int c1, int c2, bool v2, int h) {
+// (half 0) + (half 1).  Returns the chosen index.  One pass over the row:
+// r - c1 is written to dst as it goes (the screening's best is almost
+// always the winner), and rows where c2 wins are rewritten with r - c2.
+// dst must not alias src.
+__device__ __forceinline__ int rescore_update(const float *src, float *dst, bool store,
+                                              int64_t row, int dp, const float *cb_l, int c1,
+                                              int c2, bool v2, int h) {
   float p1 = 0.f, p2 = 0.f;
   const int kend = dp >> 4;
+#pragma unroll 4
   for (int ks = 0; ks < kend; ++ks) {
     const int i0 = ks * 16 + h * 8;
-    float r[8], a[8], b[8];
+    float r[8], a[8], b[8], v[8];
     read8(src, row, dp, i0, true, r);
     read8(cb_l, c1, dp, i0, true, a);
     read8(cb_l, c2, dp, i0, true, b);
@@ -170,27 +261,30 @@ __device__ __forceinline__ int rescore_update(RowFrags<KS> &bfr, bool frags, con
       const float u = r[e] - b[e];
       p1 = fmaf(t, t, p1);
       p2 = fmaf(u, u, p2);
+      v[e] = t;
     }
+    if (store) write8(dst, row, dp, i0, v);
   }
   const float q1 = __shfl_xor(p1, 32, 64);
   const float q2 = __shfl_xor(p2, 32, 64);
   const float d1 = h ? q1 + p1 : p1 + q1;
   const float d2 = h ? q2 + p2 : p2 + q2;
-  const int id = (v2 && (d2 < d1 || (d2 == d1 && c2 < c1))) ? c2 : c1;
-  static_for<0, KS>([&](auto K_) {
-    constexpr int ks = decltype(K_)::value;
-    const int i0 = ks * 16 + h * 8;
-    const bool active = ks * 16 < dp;
-    float r[8], c[8], v[8];
-    read8(src, row, dp, i0, active, r);
-    read8(cb_l, id, dp, i0, active, c);
+  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
+  if (store && __ballot(take2)) {
+    if (take2) {
+#pragma unroll 4
+      for (int ks = 0; ks < kend; ++ks) {
+        const int i0 = ks * 16 + h * 8;
+        float r[8], b[8], v[8];
+        read8(src, row, dp, i0, true, r);
+        read8(cb_l, c2, dp, i0, true, b);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = r[e] - c[e];
-    if (store && active) write8(dst, row, dp, i0, v);
-    if (frags) bfr.template set<ks>(to_bf16x8(v));
-    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-  });
-  return id;
+        for (int e = 0; e < 8; ++e) v[e] = r[e] - b[e];
+        write8(dst, row, dp, i0, v);
+      }
+    }
+  }
+  return take2 ? c2 : c1;
 }
 
 // First two candidates of a row's top-2 list as valid codeword indices.
@@ -280,10 +374,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const uint32_t ring_lds = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4 *)ring);
 
   RowFrags<KS> bfr;
-  build_bfrags<KS>(bfr, l_begin == 0 ? a.src0 : a.r32, rowc, a.dp, h);
-  bf16x8 bnorm;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) bnorm[e] = (__bf16)((h == 0 && e < 2) ? 1.0f : 0.0f);
+  build_bfrags<KS>(bfr, l_begin == 0 ? a.src0 : a.rbuf[l_begin & 1], rowc, a.dp, h);
+  // B-fragment of the norm k-step: ones at k = 0, 1 (lanes of half 0)
+  u32x4 bnorm = {0u, 0u, 0u, 0u};
+  if (h == 0) bnorm[0] = 0x3F803F80u;  // two bf16 ones
 
   const uint4 *ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l_begin * T + t0) * tile_u4;
   // prologue of the first level: stages 0 .. kAhead-1
@@ -311,19 +405,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         barrier_only();
         int slot = slot_t + s % kSlots;
         slot = slot >= kSlots ? slot - kSlots : slot;
-        const uint4 *st = ring + slot * (kSlotBytes / 16);
-        if constexpr (s == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            mfma_first(acc[j], __builtin_bit_cast(bf16x8, st[j * 64 + lane]), bnorm);
-        }
-        static_for<0, 4>([&](auto KS_) {
-          constexpr int ks = decltype(KS_)::value;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            bfr.template mfma<s * 4 + ks>(
-                acc[j], __builtin_bit_cast(bf16x8, st[256 + (j * 4 + ks) * 64 + lane]));
-        });
+        const uint32_t addr = ring_lds + (uint32_t)slot * kSlotBytes + (uint32_t)lane * 16u;
+        if constexpr (s == 0) norm_mfma(acc, addr, bnorm);
+        bfr.template stage<s>(acc, addr);
         // refill the slot freed by stage g-1 with stage g + kAhead
         if (g + kAhead < nst) {
           int nslot = slot + kAhead;
@@ -382,11 +466,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       bool v2;
       candidates(I1, I2, a.K, c1, c2, v2);
       const bool last = l == a.L - 1;
-      float *dst = last ? a.res_final : a.r32;
+      const float *src = l == 0 ? a.src0 : a.rbuf[l & 1];
+      float *dst = last ? a.res_final : a.rbuf[(l + 1) & 1];
       const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
-      const int id = rescore_update<KS>(bfr, !last, l == 0 ? a.src0 : a.r32, dst,
-                                        live && dst != nullptr, rowc, a.dp, cb_l, c1, c2, v2, h);
+      const int id = rescore_update(src, dst, live && dst != nullptr, rowc, a.dp, cb_l, c1, c2,
+                                    v2, h);
       if (live && h == 0) a.ids[row * a.L + l] = id;
+      if (!last) {
+        // wait for this wave's stores of the new residual, then build the
+        // next level's fragments from it (lanes past row n-1 read row n-1;
+        // their results are discarded)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        build_bfrags<KS>(bfr, dst, rowc, a.dp, h);
+      }
     } else {
       if (live && h == 0)
         a.part[row * splits + sp] = make_float4(S1, __int_as_float(I1), S2, __int_as_float(I2));
@@ -416,11 +508,10 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   bool v2;
   candidates(I1, I2, a.K, c1, c2, v2);
   const bool last = level == a.L - 1;
-  float *dst = last ? a.res_final : a.r32;
+  const float *src = level == 0 ? a.src0 : a.rbuf[level & 1];
+  float *dst = last ? a.res_final : a.rbuf[(level + 1) & 1];
   const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
-  RowFrags<KS> unused;
-  const int id = rescore_update<KS>(unused, false, level == 0 ? a.src0 : a.r32, dst,
-                                    live && dst != nullptr, rowc, a.dp, cb_l, c1, c2, v2, h);
+  const int id = rescore_update(src, dst, live && dst != nullptr, rowc, a.dp, cb_l, c1, c2, v2, h);
   if (live && h == 0) a.ids[row * a.L + level] = id;
 }
 

@@ -8,7 +8,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/rvq.h"
+#include "rvq.h"
 #include "common.h"
 
 using namespace rvq;
@@ -89,15 +89,18 @@ PreparedLayout prepared_layout(int32_t L, int32_t K, int32_t d) {
 }
 
 struct EncodeLayout {
-  size_t r32_off, part_off, total;
+  size_t r0_off, r1_off, part_off, total;
 };
-// Workspace: the fp32 residual [n][d] and, for the split plan, one top-2
-// list per row and codeword tile [n][tiles] (the largest split count).
+// Workspace: two fp32 residual buffers [n][dp] (level l reads one and
+// writes the other) and, for the split plan, one top-2 list per row and
+// codeword tile [n][tiles] (the largest split count).
 EncodeLayout encode_layout(int64_t n, int32_t d, int32_t K) {
   EncodeLayout w;
   const size_t tiles = (size_t)(padded_k(K) / kTileCw);
-  w.r32_off = 0;
-  w.part_off = align256((size_t)n * row_stride(d) * sizeof(float));
+  const size_t rbytes = align256((size_t)n * row_stride(d) * sizeof(float));
+  w.r0_off = 0;
+  w.r1_off = rbytes;
+  w.part_off = 2 * rbytes;
   w.total = w.part_off + align256((size_t)n * tiles * sizeof(float4));
   if (w.total == 0) w.total = 256;
   return w;
@@ -211,7 +214,8 @@ rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int3
   a.L = L;
   a.K = K;
   a.cb = a.dp != d ? (const float *)((const char *)prepared + pl.cbpad_off) : codebooks;
-  a.r32 = (float *)(ws + wl.r32_off);
+  a.rbuf[0] = (float *)(ws + wl.r0_off);
+  a.rbuf[1] = (float *)(ws + wl.r1_off);
   a.residual_out = residual_out;
   a.ids = ids;
   a.part = (float4 *)(ws + wl.part_off);
