@@ -68,6 +68,42 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+# Encoder sources: HBM byte counts taken with rocprofv3 are valid only for
+# the kernel they were taken on.
+ENCODER_SOURCES = ["common.h", "encode_impl.h", "encode.hip", "encode_s1_2_4.hip",
+                   "encode_s8_12.hip", "encode_s16.hip", "encode_s18.hip", "encode_s20.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_kernel_native_batch_hbm_bytes.txt")
+
+
+def encoder_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ENCODER_SOURCES:
+        with open(os.path.join(ROOT, "residual_vector_quantization_rvq_amd", "csrc", name)) as f:
+            # code only: line comments and blank lines do not change a kernel
+            code = [ln.split("//", 1)[0].rstrip() for ln in f]
+        h.update(name.encode() + b"\0" + "\n".join(c for c in code if c).encode())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused encoder from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's counts), or
+    None when the summary is absent or was taken on other encoder sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("encoder_source_sha256") != encoder_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, target_s: float = 15.0) -> dict:
     """The fp64 oracle (encode + decode + counts + msr) on a seeded row sample."""
     import numpy as np
@@ -87,9 +123,13 @@ def cpu_baseline(w, target_s: float = 15.0) -> dict:
         oracle.msr(sub.x, ref["ids"], sub.codebooks, x_dtype=sub.x_dtype, threads=threads)
         return time.perf_counter() - t0
 
-    probe_rows = threads
-    t_probe = run(probe_rows)
-    rows = int(max(threads, min(4096, probe_rows * target_s / max(t_probe, 1e-3))))
+    # two probes separate the per-row cost from the fixed cost of a call
+    # (widening the codebooks to fp64), so the sample is sized to target_s
+    r1, r2 = threads, 4 * threads
+    t1, t2 = run(r1), run(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    fixed = max(t1 - r1 * per_row, 0.0)
+    rows = int(min(16384, max(r2, (target_s - fixed) / per_row)))
     rows = max(threads, rows // threads * threads)
     t = run(rows)
     return {"value": rows / t, "unit": "vectors/s", "cores": threads, "kind": "oracle",
@@ -104,6 +144,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain copy of this many MiB "
+                         "(the calibration dispatch for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the RVQ path runs on a single MI355X and has no "
@@ -196,7 +239,8 @@ def main() -> int:
         "roofline": {"bound": "mfma",
                      "kernel": "sweep_kernel" + ("<fused: all levels>" if launches.value == 1 else "<one level>"),
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if launches.value == 1 else None,
                      "launch_ms": round(dist_avg, 4),
                      "flops_per_launch": flops_per_launch},
         "mfma_pct": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
@@ -206,6 +250,12 @@ def main() -> int:
         "decode_ms": round(float(np.median(dec_ms)), 4),
         "level_stats_ms": round(float(np.median(st_ms)), 4),
     }
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize(dev)
+        del src, dst
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

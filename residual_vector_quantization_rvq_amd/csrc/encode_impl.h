@@ -17,8 +17,8 @@
 //    are read from memory once per level, never once per codeword tile.
 //  * The prepared codebook (common.h) is one contiguous stream of A-fragments
 //    per level.  All workgroups sweep it in the same order, so the 32 CUs of
-//    an XCD share every line in L2.  Each 16 KB stage is staged through a
-//    double-buffered LDS ring with register prefetch two stages ahead, and
+//    an XCD share every line in L2.  Each 16 KB stage goes through a 7-slot
+//    LDS ring filled by direct global->LDS loads six stages ahead, and
 //    every wave reads all A-fragments of a stage from LDS (no bank
 //    conflicts: lane L reads bytes 16L..16L+15 of a 1 KB fragment).
 //  * A per-tile norm k-step folds ||c||^2 into the accumulator, so the
