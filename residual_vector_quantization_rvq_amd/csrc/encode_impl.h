@@ -53,97 +53,126 @@ __device__ __forceinline__ float pack_key(float score, uint32_t tag) {
   return __uint_as_float((__float_as_uint(score) & ~31u) | tag);
 }
 
-// The row fragments do not fit in the 256 arch VGPRs next to everything
-// else, so the first kFragsInAgpr k-steps live in AGPRs (next to the 64
-// accumulator AGPRs) and feed the MFMA B operand from there; the compiler
-// only emits the VGPR form, so a stage's MFMAs are written out below.  A
-// fragment is one 128-bit value (8 bf16 packed in 4 words).
-constexpr int kFragsInAgpr = 48;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// One stage (4 k-steps x 4 sub-tiles) for this lane: A-fragments are read
-// from the ring slot at addr (slot base + 16*lane) with 8 LDS reads in
-// flight in two alternating sets, so the next k-step's reads overlap the
-// current k-step's 4 MFMAs; every read has completed when the block ends.
-#define RVQ_STAGE_ASM                                                                  \
-      "ds_read_b128 %[t0], %[addr] offset:4096\n\t" \
-      "ds_read_b128 %[t1], %[addr] offset:8192\n\t" \
-      "ds_read_b128 %[t2], %[addr] offset:12288\n\t" \
-      "ds_read_b128 %[t3], %[addr] offset:16384\n\t" \
-      "ds_read_b128 %[t4], %[addr] offset:5120\n\t" \
-      "ds_read_b128 %[t5], %[addr] offset:9216\n\t" \
-      "ds_read_b128 %[t6], %[addr] offset:13312\n\t" \
-      "ds_read_b128 %[t7], %[addr] offset:17408\n\t" \
-      "s_waitcnt lgkmcnt(4)\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c0], %[t0], %[b0], %[c0]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c1], %[t1], %[b0], %[c1]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c2], %[t2], %[b0], %[c2]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c3], %[t3], %[b0], %[c3]\n\t" \
-      "ds_read_b128 %[t0], %[addr] offset:6144\n\t" \
-      "ds_read_b128 %[t1], %[addr] offset:10240\n\t" \
-      "ds_read_b128 %[t2], %[addr] offset:14336\n\t" \
-      "ds_read_b128 %[t3], %[addr] offset:18432\n\t" \
-      "s_waitcnt lgkmcnt(4)\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c0], %[t4], %[b1], %[c0]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c1], %[t5], %[b1], %[c1]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c2], %[t6], %[b1], %[c2]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c3], %[t7], %[b1], %[c3]\n\t" \
-      "ds_read_b128 %[t4], %[addr] offset:7168\n\t" \
-      "ds_read_b128 %[t5], %[addr] offset:11264\n\t" \
-      "ds_read_b128 %[t6], %[addr] offset:15360\n\t" \
-      "ds_read_b128 %[t7], %[addr] offset:19456\n\t" \
-      "s_waitcnt lgkmcnt(4)\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c0], %[t0], %[b2], %[c0]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c1], %[t1], %[b2], %[c1]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c2], %[t2], %[b2], %[c2]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c3], %[t3], %[b2], %[c3]\n\t" \
-      "s_waitcnt lgkmcnt(0)\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c0], %[t4], %[b3], %[c0]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c1], %[t5], %[b3], %[c1]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c2], %[t6], %[b3], %[c2]\n\t" \
-      "v_mfma_f32_32x32x16_bf16 %[c3], %[t7], %[b3], %[c3]\n\t"
-
-#define RVQ_STAGE_OUTS(c)                                                               \
-  [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]),                \
-      [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]),         \
-      [t4] "=&v"(t[4]), [t5] "=&v"(t[5]), [t6] "=&v"(t[6]), [t7] "=&v"(t[7])
-
-template <bool B_IN_AGPR>
-__device__ __forceinline__ void stage_mfma(f32x16 (&c)[4], uint32_t addr, const u32x4 &b0,
-                                           const u32x4 &b1, const u32x4 &b2, const u32x4 &b3) {
-  u32x4 t[8];
-  if constexpr (B_IN_AGPR)
-    asm volatile(RVQ_STAGE_ASM
-                 : RVQ_STAGE_OUTS(c)
-                 : [addr] "v"(addr), [b0] "a"(b0), [b1] "a"(b1), [b2] "a"(b2), [b3] "a"(b3));
-  else
-    asm volatile(RVQ_STAGE_ASM
-                 : RVQ_STAGE_OUTS(c)
-                 : [addr] "v"(addr), [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3));
+// Codeword index of a key found in the 64-codeword block whose lane-half
+// base is b (kNoIndex when nothing was found).
+__device__ __forceinline__ int block_index(float key, int b) {
+  const uint32_t g = __float_as_uint(key) & 31u;
+  return b == kNoIndex ? kNoIndex : b + (int)((g >> 4) * 32 + ((g >> 2) & 3) * 8 + (g & 3));
 }
 
-// The norm k-step opening a tile: accumulators start from ||c||^2.
-__device__ __forceinline__ void norm_mfma(f32x16 (&c)[4], uint32_t addr, const u32x4 &bn) {
-  u32x4 t[4];
-  asm volatile("ds_read_b128 %[t0], %[addr] offset:0\n\t"
-               "ds_read_b128 %[t1], %[addr] offset:1024\n\t"
-               "ds_read_b128 %[t2], %[addr] offset:2048\n\t"
-               "ds_read_b128 %[t3], %[addr] offset:3072\n\t"
-               "s_waitcnt lgkmcnt(0)\n\t"
-               "v_mfma_f32_32x32x16_bf16 %[c0], %[t0], %[bn], 0\n\t"
-               "v_mfma_f32_32x32x16_bf16 %[c1], %[t1], %[bn], 0\n\t"
-               "v_mfma_f32_32x32x16_bf16 %[c2], %[t2], %[bn], 0\n\t"
-               "v_mfma_f32_32x32x16_bf16 %[c3], %[t3], %[bn], 0\n\t"
-               : [c0] "=&a"(c[0]), [c1] "=&a"(c[1]), [c2] "=&a"(c[2]), [c3] "=&a"(c[3]),
-                 [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3])
-               : [addr] "v"(addr), [bn] "v"(bn));
+// The row fragments do not fit in the 256 arch VGPRs next to everything
+// else, so the first kFragsInAgpr k-steps fill the 256 AGPRs and feed the
+// MFMA B operand from there (the compiler only emits the VGPR form, so a
+// stage's MFMAs are written out below); the accumulators stay in VGPRs,
+// where the epilogue reads them without copies.  A fragment is one 128-bit
+// value (8 bf16 packed in 4 words).
+constexpr int kFragsInAgpr = 64;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Stage blocks.  A slot holds a 4 KB norm area and one 16 KB stage; in the
+// stage, k-step ks of sub-tile j is the 1 KB A-fragment at byte
+// 4096 + (4*j + ks)*1024, and lane L reads its 16 bytes at slot base + 16*L.
+// A block runs one stage's MFMAs with LDS reads two k-steps ahead, and
+// before its last k-step it reads the first A-fragments of the next stage
+// (norm fragments when the next stage opens a tile) into p, so the next
+// block starts its MFMAs without waiting for LDS.  Every read has completed
+// when a block ends (no load is in flight across blocks).  The leading
+// wait covers any scalar load the compiler left in flight, so the counted
+// waits below see only this block's reads.
+#define RVQ_RD(t, base, off) "ds_read_b128 %[" #t "], %[" #base "] offset:" #off "\n\t"
+#define RVQ_MF(c, a, b) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n\t"
+#define RVQ_MF4(a0, a1, a2, a3, b) RVQ_MF(c0, a0, b) RVQ_MF(c1, a1, b) RVQ_MF(c2, a2, b) RVQ_MF(c3, a3, b)
+#define RVQ_RD4(t0, t1, t2, t3, o0, o1, o2, o3) \
+  RVQ_RD(t0, addr, o0) RVQ_RD(t1, addr, o1) RVQ_RD(t2, addr, o2) RVQ_RD(t3, addr, o3)
+// k-step ks of the four sub-tiles
+#define RVQ_K0(t0, t1, t2, t3) RVQ_RD4(t0, t1, t2, t3, 4096, 8192, 12288, 16384)
+#define RVQ_K1(t0, t1, t2, t3) RVQ_RD4(t0, t1, t2, t3, 5120, 9216, 13312, 17408)
+#define RVQ_K2(t0, t1, t2, t3) RVQ_RD4(t0, t1, t2, t3, 6144, 10240, 14336, 18432)
+#define RVQ_K3(t0, t1, t2, t3) RVQ_RD4(t0, t1, t2, t3, 7168, 11264, 15360, 19456)
+#define RVQ_NEXT_STAGE \
+  RVQ_RD(p0, naddr, 4096) RVQ_RD(p1, naddr, 8192) RVQ_RD(p2, naddr, 12288) RVQ_RD(p3, naddr, 16384)
+#define RVQ_NEXT_TILE \
+  RVQ_RD(p0, naddr, 0) RVQ_RD(p1, naddr, 1024) RVQ_RD(p2, naddr, 2048) RVQ_RD(p3, naddr, 3072)
+#define RVQ_WAIT(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
+
+// A stage inside a tile: p holds its k-step 0 on entry.
+#define RVQ_STAGE_BODY(NEXT)                                                               \
+  RVQ_WAIT(0) RVQ_K1(t0, t1, t2, t3) RVQ_MF4(p0, p1, p2, p3, b0) RVQ_K2(t4, t5, t6, t7) \
+      RVQ_WAIT(4) RVQ_MF4(t0, t1, t2, t3, b1) RVQ_K3(t0, t1, t2, t3) RVQ_WAIT(4)            \
+          RVQ_MF4(t4, t5, t6, t7, b2) NEXT RVQ_WAIT(4) RVQ_MF4(t0, t1, t2, t3, b3) RVQ_WAIT(0)
+
+// The stage opening a tile: p holds the norm k-step on entry, and the
+// accumulators start from ||c||^2 (B = ones at k = 0, 1).
+#define RVQ_STAGE0_BODY(NEXT)                                                              \
+  RVQ_WAIT(0) RVQ_K0(t0, t1, t2, t3)                                                     \
+  "v_mfma_f32_32x32x16_bf16 %[c0], %[p0], %[bn], 0\n\t"                                      \
+  "v_mfma_f32_32x32x16_bf16 %[c1], %[p1], %[bn], 0\n\t"                                      \
+  "v_mfma_f32_32x32x16_bf16 %[c2], %[p2], %[bn], 0\n\t"                                      \
+  "v_mfma_f32_32x32x16_bf16 %[c3], %[p3], %[bn], 0\n\t" RVQ_K1(t4, t5, t6, t7) RVQ_WAIT(4) \
+      RVQ_MF4(t0, t1, t2, t3, b0) RVQ_K2(t0, t1, t2, t3) RVQ_WAIT(4)                        \
+          RVQ_MF4(t4, t5, t6, t7, b1) RVQ_K3(t4, t5, t6, t7) RVQ_WAIT(4)                    \
+              RVQ_MF4(t0, t1, t2, t3, b2) NEXT RVQ_WAIT(4) RVQ_MF4(t4, t5, t6, t7, b3) RVQ_WAIT(0)
+
+#define RVQ_TEMPS                                                                          \
+  [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [t4] "=&v"(t[4]), \
+      [t5] "=&v"(t[5]), [t6] "=&v"(t[6]), [t7] "=&v"(t[7])
+#define RVQ_PREF [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3])
+
+// FIRST: the stage opens a tile.  NEXT_TILE: the next stage opens a tile.
+// B_IN_AGPR: the stage's row fragments live in AGPRs.
+template <bool FIRST, bool NEXT_TILE, bool B_IN_AGPR>
+__device__ __forceinline__ void stage_block(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
+                                            uint32_t naddr, const u32x4 &bn, const u32x4 &b0,
+                                            const u32x4 &b1, const u32x4 &b2, const u32x4 &b3) {
+  u32x4 t[8];
+#define RVQ_IN(cls) \
+  [addr] "v"(addr), [naddr] "v"(naddr), [b0] cls(b0), [b1] cls(b1), [b2] cls(b2), [b3] cls(b3)
+  if constexpr (FIRST) {
+#define RVQ_OUT0 \
+  [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]), RVQ_PREF, RVQ_TEMPS
+    if constexpr (NEXT_TILE) {
+      if constexpr (B_IN_AGPR)
+        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_TILE) : RVQ_OUT0 : RVQ_IN("a"), [bn] "v"(bn));
+      else
+        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_TILE) : RVQ_OUT0 : RVQ_IN("v"), [bn] "v"(bn));
+    } else {
+      if constexpr (B_IN_AGPR)
+        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_STAGE) : RVQ_OUT0 : RVQ_IN("a"), [bn] "v"(bn));
+      else
+        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_STAGE) : RVQ_OUT0 : RVQ_IN("v"), [bn] "v"(bn));
+    }
+#undef RVQ_OUT0
+  } else {
+#define RVQ_OUT \
+  [c0] "+v"(c[0]), [c1] "+v"(c[1]), [c2] "+v"(c[2]), [c3] "+v"(c[3]), RVQ_PREF, RVQ_TEMPS
+    if constexpr (NEXT_TILE) {
+      if constexpr (B_IN_AGPR)
+        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_TILE) : RVQ_OUT : RVQ_IN("a"));
+      else
+        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_TILE) : RVQ_OUT : RVQ_IN("v"));
+    } else {
+      if constexpr (B_IN_AGPR)
+        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_STAGE) : RVQ_OUT : RVQ_IN("a"));
+      else
+        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_STAGE) : RVQ_OUT : RVQ_IN("v"));
+    }
+#undef RVQ_OUT
+  }
+#undef RVQ_IN
+}
+
+// The norm fragments of the tile opening a level (slot base + 16*lane).
+__device__ __forceinline__ void read_tile_norms(u32x4 (&p)[4], uint32_t naddr) {
+  asm volatile(RVQ_WAIT(0) RVQ_NEXT_TILE RVQ_WAIT(0)
+               : [p0] "=&v"(p[0]), [p1] "=&v"(p[1]), [p2] "=&v"(p[2]), [p3] "=&v"(p[3])
+               : [naddr] "v"(naddr));
 }
 
 // Orders the epilogue's accumulator reads after the last MFMA's result
 // latency (the compiler does not see the MFMAs above).
 __device__ __forceinline__ void mfma_drain(f32x16 (&acc)[4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+               : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
 }
 
 // Row fragments split over AGPRs (k-steps < NA) and VGPRs (the rest); NA
@@ -172,13 +201,14 @@ struct RowFrags {
     if constexpr (k < NA) return fa[k];
     else return fv[k - NA];
   }
-  template <int s>
-  __device__ __forceinline__ void stage(f32x16 (&c)[4], uint32_t addr) const {
+  template <int s, int S>
+  __device__ __forceinline__ void stage(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
+                                        uint32_t naddr, const u32x4 &bn) const {
     static_assert(NA % 4 == 0, "a stage's k-steps must share a register file");
-    stage_mfma<(s * 4 < NA)>(c, addr, get<s * 4>(), get<s * 4 + 1>(), get<s * 4 + 2>(),
-                             get<s * 4 + 3>());
-  }
-};
+    stage_block<s == 0, s == S - 1, (s * 4 < NA)>(c, p, addr, naddr, bn, get<s * 4>(),
+                                                   get<s * 4 + 1>(), get<s * 4 + 2>(),
+                                                   get<s * 4 + 3>());
+  }};
 
 // Compile-time loop: f(integral_constant<int, i>) for i in [0, N).
 template <int I, int N, typename F>
@@ -287,6 +317,66 @@ __device__ __forceinline__ int rescore_update(const float *src, float *dst, bool
   return take2 ? c2 : c1;
 }
 
+// The same rescoring and update for the fused encoder, which also rebuilds
+// the row's B-fragments for the next level in the same pass: a lane's
+// update covers exactly the features its fragments hold (ks*16 + h*8 + e),
+// so the new residual never has to be read back.  Every k-step is unrolled
+// (fragments live in fixed registers); k-steps past the padded width dp are
+// zero and touch no memory.
+template <int KS>
+__device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const float *src,
+                                                    float *dst, bool store, int64_t row, int dp,
+                                                    const float *cb_l, int c1, int c2, bool v2,
+                                                    int h) {
+  float p1 = 0.f, p2 = 0.f;
+  static_for<0, KS>([&](auto K_) {
+    constexpr int ks = decltype(K_)::value;
+    const int i0 = ks * 16 + h * 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (ks * 16 < dp) {
+      float r[8], a[8], b[8];
+      read8(src, row, dp, i0, true, r);
+      read8(cb_l, c1, dp, i0, true, a);
+      read8(cb_l, c2, dp, i0, true, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = r[e] - a[e];
+        const float u = r[e] - b[e];
+        p1 = fmaf(t, t, p1);
+        p2 = fmaf(u, u, p2);
+        v[e] = t;
+      }
+      if (store) write8(dst, row, dp, i0, v);
+    }
+    bfr.template set<ks>(to_bf16x8(v));
+    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+  });
+  const float q1 = __shfl_xor(p1, 32, 64);
+  const float q2 = __shfl_xor(p2, 32, 64);
+  const float d1 = h ? q1 + p1 : p1 + q1;
+  const float d2 = h ? q2 + p2 : p2 + q2;
+  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
+  if (__ballot(take2)) {
+    if (take2) {
+      static_for<0, KS>([&](auto K_) {
+        constexpr int ks = decltype(K_)::value;
+        const int i0 = ks * 16 + h * 8;
+        if (ks * 16 < dp) {
+          float r[8], b[8], v[8];
+          read8(src, row, dp, i0, true, r);
+          read8(cb_l, c2, dp, i0, true, b);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = r[e] - b[e];
+          if (store) write8(dst, row, dp, i0, v);
+          bfr.template set<ks>(to_bf16x8(v));
+        }
+        if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+  }
+  return take2 ? c2 : c1;
+}
+
 // First two candidates of a row's top-2 list as valid codeword indices.
 __device__ __forceinline__ void candidates(int i1, int i2, int K, int &c1, int &c2, bool &v2) {
   c1 = (i1 >= 0 && i1 < K) ? i1 : 0;  // finite inputs always give a valid first candidate
@@ -313,11 +403,11 @@ __device__ __forceinline__ void dma16(const uint4 *src, uint32_t lds_addr) {
 // norm block when the stage starts a tile.
 __host__ __device__ constexpr int dma_count(int s) { return s == 0 ? 5 : 4; }
 
-// Loads issued after stage s's, for the stages s+1 .. s+kAhead-1.
+// Loads issued after stage s+1's, for the stages s+2 .. s+kAhead-1.
 template <int S>
-__host__ __device__ constexpr int dma_after(int s) {
+__host__ __device__ constexpr int dma_after_next(int s) {
   int c = 0;
-  for (int k = 1; k < kAhead; ++k) c += dma_count((s + k) % S);
+  for (int k = 2; k < kAhead; ++k) c += dma_count((s + k) % S);
   return c;
 }
 
@@ -388,33 +478,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   for (int l = l_begin; l < l_end; ++l) {
     ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l * T + t0) * tile_u4;
-    float S1 = __builtin_inff(), S2 = __builtin_inff();
-    int I1 = kNoIndex, I2 = kNoIndex;
+    // Running top-2 of this lane as (key, base of the key's 64-codeword
+    // block).  Blocks come in increasing codeword order and a key's tag is
+    // its position in the block, so keeping the earlier entry on equal keys
+    // is the (key, index) order.
+    float R1 = __builtin_inff(), R2 = __builtin_inff();
+    int B1 = kNoIndex, B2 = kNoIndex;
 
     int slot_t = 0;  // ring slot of the current tile's stage 0
+    u32x4 pre[4];    // first A-fragments of the next stage, read ahead
     for (int tt = 0; tt < ntiles; ++tt) {
       f32x16 acc[4];
       static_for<0, S>([&](auto S_) {
         constexpr int s = decltype(S_)::value;
         const int g = tt * S + s;
-        // this wave's loads of stage g are done once at most dma_after<S>(s)
-        // newer ones are outstanding; at the start of a level (update-phase
-        // accesses may be interleaved) and near the end wait for all
+        // Stage g+1 must be in LDS for every wave before this stage's block
+        // reads ahead into it: wait for this wave's loads of stage g+1 (at
+        // most dma_after_next<S>(s) newer loads outstanding), then the
+        // barrier, which also means every wave is done with stage g-1, whose
+        // slot the refill below overwrites.  At the start of a level
+        // (update-phase accesses may be interleaved) and near its end, wait
+        // for every load.
         if (g == 0 || g + kAhead - 1 >= nst) wait_vmcnt<0>();
-        else wait_vmcnt<dma_after<S>(s)>();
+        else wait_vmcnt<dma_after_next<S>(s)>();
         barrier_only();
         int slot = slot_t + s % kSlots;
         slot = slot >= kSlots ? slot - kSlots : slot;
+        const int nslot = slot + 1 == kSlots ? 0 : slot + 1;
         const uint32_t addr = ring_lds + (uint32_t)slot * kSlotBytes + (uint32_t)lane * 16u;
-        if constexpr (s == 0) norm_mfma(acc, addr, bnorm);
-        bfr.template stage<s>(acc, addr);
-        // refill the slot freed by stage g-1 with stage g + kAhead
+        const uint32_t naddr = ring_lds + (uint32_t)nslot * kSlotBytes + (uint32_t)lane * 16u;
+        if constexpr (s == 0) {
+          if (tt == 0) read_tile_norms(pre, addr);
+        }
+        // refill the slot of stage g-1 with stage g + kAhead
         if (g + kAhead < nst) {
-          int nslot = slot + kAhead;
-          nslot = nslot >= kSlots ? nslot - kSlots : nslot;
-          issue_stage(ls, tile_u4, tt + (s + kAhead) / S, (s + kAhead) % S, nslot, ring_lds,
+          int rslot = slot + kAhead;
+          rslot = rslot >= kSlots ? rslot - kSlots : rslot;
+          issue_stage(ls, tile_u4, tt + (s + kAhead) / S, (s + kAhead) % S, rslot, ring_lds,
                       wave, lane);
         }
+        // (the last stage of a level reads ahead into a slot it never uses)
+        bfr.template stage<s, S>(acc, pre, addr, naddr, bnorm);
       });
       slot_t += S % kSlots;
       slot_t = slot_t >= kSlots ? slot_t - kSlots : slot_t;
@@ -423,7 +527,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       // Epilogue: accumulator element i of sub-tile j is codeword
       // j*32 + (i/4)*8 + h*4 + i%4 of the tile for this lane's row.  Per
       // 64-codeword block p (sub-tiles 2p, 2p+1) the tag jj*16 + i is unique.
-      const int tbase = (t0 + tt) * kTileCw;
+      // Each key costs three VALU ops: pack, then the two-smallest update
+      // with med3 (med3(a, b, -inf) is min(a, b)).
+      const float ninf = -__builtin_inff();
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         float k1 = __builtin_inff(), k2 = __builtin_inff();
@@ -433,18 +539,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
           for (int i = 0; i < 16; ++i) {
             const float key = pack_key(acc[2 * p + jj][i], (uint32_t)(jj * 16 + i));
             k2 = __builtin_amdgcn_fmed3f(k1, k2, key);
-            k1 = fminf(k1, key);
+            k1 = __builtin_amdgcn_fmed3f(k1, key, ninf);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        const uint32_t g1 = __float_as_uint(k1) & 31u, g2 = __float_as_uint(k2) & 31u;
-        const int bb = tbase + p * 64 + h * 4;
-        const int j1 = bb + (int)((g1 >> 4) * 32 + ((g1 >> 2) & 3) * 8 + (g1 & 3));
-        const int j2 = bb + (int)((g2 >> 4) * 32 + ((g2 >> 2) & 3) * 8 + (g2 & 3));
-        merge_top2(S1, I1, S2, I2, k1, j1, k2, j2);
+        const int base = (t0 + tt) * kTileCw + p * 64 + h * 4;
+        const bool c = k1 < R1;
+        const float old = c ? R1 : R2;
+        const int oldb = c ? B1 : B2;
+        const float nw = c ? k2 : k1;
+        R1 = c ? k1 : R1;
+        B1 = c ? base : B1;
+        const bool d = nw < old;
+        R2 = d ? nw : old;
+        B2 = d ? base : oldb;
       }
     }
 
-    // Lanes L and L+32 hold the same row over disjoint codewords.
+    // Decode the tags, then merge with the other half of the row (lanes L
+    // and L+32 hold the same row over disjoint codewords).
+    float S1 = R1, S2 = R2;
+    int I1 = block_index(R1, B1), I2 = block_index(R2, B2);
     {
       const float t1 = __shfl_xor(S1, 32, 64), t2 = __shfl_xor(S2, 32, 64);
       const int j1 = __shfl_xor(I1, 32, 64), j2 = __shfl_xor(I2, 32, 64);
@@ -469,16 +584,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       const float *src = l == 0 ? a.src0 : a.rbuf[l & 1];
       float *dst = last ? a.res_final : a.rbuf[(l + 1) & 1];
       const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
-      const int id = rescore_update(src, dst, live && dst != nullptr, rowc, a.dp, cb_l, c1, c2,
-                                    v2, h);
+      // (lanes past row n-1 work on row n-1 and store nothing)
+      const int id = rescore_update_frags<KS>(bfr, src, dst, live && dst != nullptr, rowc, a.dp,
+                                              cb_l, c1, c2, v2, h);
       if (live && h == 0) a.ids[row * a.L + l] = id;
-      if (!last) {
-        // wait for this wave's stores of the new residual, then build the
-        // next level's fragments from it (lanes past row n-1 read row n-1;
-        // their results are discarded)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        build_bfrags<KS>(bfr, dst, rowc, a.dp, h);
-      }
     } else {
       if (live && h == 0)
         a.part[row * splits + sp] = make_float4(S1, __int_as_float(I1), S2, __int_as_float(I2));
