@@ -127,6 +127,7 @@ struct EncodeArgs {
   float4 *part;
   // set by launch_encode
   const float *src0;    // level-0 rows, fp32 stride dp (x itself or a staged copy)
+  const uint16_t *x16;  // fused mode with bf16 rows of stride dp: level 0 reads them directly
   float *res_final;     // where the last level writes its residual (or null)
 };
 hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a, hipEvent_t *events,
@@ -139,7 +140,6 @@ hipError_t launch_hist(const int32_t *ids, int64_t n, int L, int K, int64_t *his
                        uint32_t *partial, uint32_t *bad, hipStream_t s);
 size_t msr_partial_bytes(int64_t n, int L);
 hipError_t launch_msr(const void *x, bool x_bf16, const int32_t *ids, int64_t n, int d,
-                      const float *cb, int L, int K, double *msr, double *partial, uint32_t *bad,
-                      hipStream_t s);
+                      const float *cb, int L, int K, double *msr, double *partial, hipStream_t s);
 
 }  // namespace rvq

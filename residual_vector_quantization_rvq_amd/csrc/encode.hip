@@ -72,7 +72,12 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   if (a_in.n == 0) return hipSuccess;
   EncodeArgs a = a_in;
   const unsigned row_waves = (unsigned)ceil_div(a.n, 4);
-  if (a.x_bf16 || a.dp != a.d) {
+  a.x16 = nullptr;
+  if (p.fused && a.x_bf16 && a.dp == a.d) {
+    // level 0 of the fused encoder reads the bf16 rows directly
+    a.x16 = (const uint16_t *)a.x;
+    a.src0 = nullptr;
+  } else if (a.x_bf16 || a.dp != a.d) {
     stage_input_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(a.x, a.x_bf16, a.n, a.d, a.dp,
                                                            a.rbuf[0]);
     a.src0 = a.rbuf[0];

@@ -241,6 +241,20 @@ __device__ __forceinline__ void write8(float *base, int64_t row, int dp, int i0,
   *reinterpret_cast<float4 *>(base + row * dp + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// Eight bf16 features (16 bytes) widened exactly to fp32; q is returned too,
+// since it already is the B-fragment of these features.
+__device__ __forceinline__ uint4 read8_bf16(const uint16_t *base, int64_t row, int dp, int i0,
+                                            float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4 *>(base + row * dp + i0);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+  return q;
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 to_bf16x8(const float (&v)[8]) {
   u32x4 q;
@@ -262,6 +276,32 @@ __device__ __forceinline__ void build_bfrags(RowFrags<KS> &bfr, const float *src
     read8(src, row, dp, ks * 16 + h * 8, ks * 16 < dp, v);
     bfr.template set<ks>(to_bf16x8(v));
     // bound the loads the scheduler hoists ahead (register pressure)
+    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+__device__ __forceinline__ void read_src(const float *src, int64_t row, int dp, int i0,
+                                         float (&v)[8]) {
+  read8(src, row, dp, i0, true, v);
+}
+__device__ __forceinline__ void read_src(const uint16_t *src, int64_t row, int dp, int i0,
+                                         float (&v)[8]) {
+  read8_bf16(src, row, dp, i0, v);
+}
+
+// The same fragments straight from bf16 rows (stride dp): the stored bits
+// are the fragment.
+template <int KS>
+__device__ __forceinline__ void build_bfrags_bf16(RowFrags<KS> &bfr, const uint16_t *src,
+                                                  int64_t row, int dp, int h) {
+  static_for<0, KS>([&](auto K_) {
+    constexpr int ks = decltype(K_)::value;
+    u32x4 f = {0u, 0u, 0u, 0u};
+    if (ks * 16 < dp) {
+      const uint4 q = *reinterpret_cast<const uint4 *>(src + row * dp + ks * 16 + h * 8);
+      f = u32x4{q.x, q.y, q.z, q.w};
+    }
+    bfr.template set<ks>(f);
     if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
   });
 }
@@ -323,8 +363,8 @@ __device__ __forceinline__ int rescore_update(const float *src, float *dst, bool
 // so the new residual never has to be read back.  Every k-step is unrolled
 // (fragments live in fixed registers); k-steps past the padded width dp are
 // zero and touch no memory.
-template <int KS>
-__device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const float *src,
+template <int KS, typename SrcT>
+__device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const SrcT *src,
                                                     float *dst, bool store, int64_t row, int dp,
                                                     const float *cb_l, int c1, int c2, bool v2,
                                                     int h) {
@@ -335,7 +375,7 @@ __device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const flo
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (ks * 16 < dp) {
       float r[8], a[8], b[8];
-      read8(src, row, dp, i0, true, r);
+      read_src(src, row, dp, i0, r);
       read8(cb_l, c1, dp, i0, true, a);
       read8(cb_l, c2, dp, i0, true, b);
 #pragma unroll
@@ -363,7 +403,7 @@ __device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const flo
         const int i0 = ks * 16 + h * 8;
         if (ks * 16 < dp) {
           float r[8], b[8], v[8];
-          read8(src, row, dp, i0, true, r);
+          read_src(src, row, dp, i0, r);
           read8(cb_l, c2, dp, i0, true, b);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = r[e] - b[e];
@@ -464,7 +504,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const uint32_t ring_lds = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4 *)ring);
 
   RowFrags<KS> bfr;
-  build_bfrags<KS>(bfr, l_begin == 0 ? a.src0 : a.rbuf[l_begin & 1], rowc, a.dp, h);
+  if (l_begin == 0 && a.x16)
+    build_bfrags_bf16<KS>(bfr, a.x16, rowc, a.dp, h);
+  else
+    build_bfrags<KS>(bfr, l_begin == 0 ? a.src0 : a.rbuf[l_begin & 1], rowc, a.dp, h);
   // B-fragment of the norm k-step: ones at k = 0, 1 (lanes of half 0)
   u32x4 bnorm = {0u, 0u, 0u, 0u};
   if (h == 0) bnorm[0] = 0x3F803F80u;  // two bf16 ones
@@ -581,12 +624,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       bool v2;
       candidates(I1, I2, a.K, c1, c2, v2);
       const bool last = l == a.L - 1;
-      const float *src = l == 0 ? a.src0 : a.rbuf[l & 1];
       float *dst = last ? a.res_final : a.rbuf[(l + 1) & 1];
       const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
       // (lanes past row n-1 work on row n-1 and store nothing)
-      const int id = rescore_update_frags<KS>(bfr, src, dst, live && dst != nullptr, rowc, a.dp,
-                                              cb_l, c1, c2, v2, h);
+      const bool store = live && dst != nullptr;
+      int id;
+      if (l == 0 && a.x16)
+        id = rescore_update_frags<KS>(bfr, a.x16, dst, store, rowc, a.dp, cb_l, c1, c2, v2, h);
+      else
+        id = rescore_update_frags<KS>(bfr, l == 0 ? a.src0 : a.rbuf[l & 1], dst, store, rowc,
+                                      a.dp, cb_l, c1, c2, v2, h);
       if (live && h == 0) a.ids[row * a.L + l] = id;
     } else {
       if (live && h == 0)

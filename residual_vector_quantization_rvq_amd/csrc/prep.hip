@@ -1,4 +1,4 @@
-// prep.hip -- codebook preparation.
+// prep.hip -- codebook preparation (one pass over the fp32 codebooks).
 //
 // The tokenizer is fixed ("LongCat-2.5 Native Multimodality for Agentic
 // Tasks", "Visual Primitive Modeling", paragraph "Offline Visual
@@ -9,68 +9,64 @@
 
 namespace rvq {
 
-// norms[l][k] = ||c_{l,k}||^2 in fp32: lane-strided partial sums, then a
-// fixed butterfly.  One wave per (level, padded codeword); padding gets
-// kPadNorm.
-__global__ __launch_bounds__(256) void norms_kernel(const float *__restrict__ cb, int L, int K,
-                                                    int d, int Kp, float *__restrict__ norms) {
-  const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= (int64_t)L * Kp) return;
-  const int l = (int)(w / Kp);
-  const int k = (int)(w % Kp);
-  if (k >= K) {
-    if (lane == 0) norms[w] = kPadNorm;
-    return;
-  }
-  const float *src = cb + ((int64_t)l * K + k) * d;
-  float acc = 0.f;
-  for (int i = lane; i < d; i += 64) acc = fmaf(src[i], src[i], acc);
-  acc = wave_sum_f32(acc);
-  if (lane == 0) norms[w] = acc;
-}
-
-// One thread per 16-byte chunk of the stream.  Writes are contiguous; each
-// group of 256 threads reads 32 codewords x 64 features.
-__global__ __launch_bounds__(256) void stream_kernel(const float *__restrict__ cb,
-                                                     const float *__restrict__ norms, int L, int K,
-                                                     int d, int Kp, int S,
-                                                     uint4 *__restrict__ stream) {
-  const int64_t chunk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// One workgroup per (level, 128-codeword tile), one pass over the tile's
+// codewords.  Wave j takes sub-tile j (32 codewords); lane L takes codeword
+// j*32 + L%32 and half h = L/32 of every k-step, i.e. exactly the 16-byte
+// chunks it writes into the stream (features s*64 + ks*16 + h*8 .. +7 of
+// stage s, k-step ks), so each wave writes 1 KB contiguous per k-step.  The
+// lane sums the squares of its features in increasing order (fmaf), and
+// ||c||^2 = (half 0) + (half 1).  Padded codewords (index >= K) are zero
+// with norm kPadNorm.
+__global__ __launch_bounds__(256) void prepare_tile_kernel(const float *__restrict__ cb, int L,
+                                                           int K, int d, int Kp, int S,
+                                                           float *__restrict__ norms,
+                                                           uint4 *__restrict__ stream) {
   const int T = Kp / kTileCw;
-  const int64_t per_tile = 256 + (int64_t)S * 1024;
-  if (chunk >= (int64_t)L * T * per_tile) return;
-  const int64_t lt = chunk / per_tile;
-  const int c = (int)(chunk % per_tile);
-  const int l = (int)(lt / T);
-  const int t = (int)(lt % T);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  if (c < 256) {
-    const int j = c >> 6, lane = c & 63;
-    if (lane < 32) {
-      const int k = t * kTileCw + j * 32 + lane;
-      const float nv = norms[(int64_t)l * Kp + k];
-      const uint16_t hi = f32_to_bf16_bits(nv);
-      const uint16_t lo = k < K ? f32_to_bf16_bits(nv - bf16_bits_to_f32(hi)) : (uint16_t)0;
-      w[0] = (uint32_t)hi | ((uint32_t)lo << 16);
-    }
-  } else {
-    const int c2 = c - 256;
-    const int s = c2 >> 10, rem = c2 & 1023;
-    const int j = rem >> 8, ks = (rem >> 6) & 3, lane = rem & 63;
-    const int k = t * kTileCw + j * 32 + (lane & 31);
-    const int d0 = s * kStageCols + ks * 16 + (lane >> 5) * 8;
-    if (k < K) {
-      const float *src = cb + ((int64_t)l * K + k) * d;
+  const int l = blockIdx.x / T, t = blockIdx.x % T;
+  const int lane = threadIdx.x & 63;
+  const int j = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int k = t * kTileCw + j * 32 + (lane & 31);
+  const bool real = k < K;
+  const float *src = cb + ((int64_t)l * K + (real ? k : 0)) * d;
+  const bool vec = (d & 3) == 0;
+  uint4 *tile = stream + ((int64_t)l * T + t) * (tile_bytes(S) / 16);
+  float acc = 0.f;
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d0 = s * kStageCols + ks * 16 + h * 8;
+      float v[8];
+      if (real && vec && d0 + 8 <= d) {
+        const float4 a = *reinterpret_cast<const float4 *>(src + d0);
+        const float4 b = *reinterpret_cast<const float4 *>(src + d0 + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (real && d0 + e < d) ? src[d0 + e] : 0.f;
+      }
+      uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float a = d0 + e < d ? -2.0f * src[d0 + e] : 0.f;
-        const float b = d0 + e + 1 < d ? -2.0f * src[d0 + e + 1] : 0.f;
-        w[e >> 1] = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+        acc = fmaf(v[e], v[e], acc);
+        acc = fmaf(v[e + 1], v[e + 1], acc);
+        w[e >> 1] = (uint32_t)f32_to_bf16_bits(-2.0f * v[e]) |
+                    ((uint32_t)f32_to_bf16_bits(-2.0f * v[e + 1]) << 16);
       }
+      tile[256 + s * 1024 + (j * 4 + ks) * 64 + lane] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
-  stream[chunk] = make_uint4(w[0], w[1], w[2], w[3]);
+  const float other = __shfl_xor(acc, 32, 64);
+  const float nv = real ? (h ? other + acc : acc + other) : kPadNorm;
+  uint32_t w0 = 0u;
+  if (h == 0) {
+    const uint16_t hi = f32_to_bf16_bits(nv);
+    const uint16_t lo = real ? f32_to_bf16_bits(nv - bf16_bits_to_f32(hi)) : (uint16_t)0;
+    w0 = (uint32_t)hi | ((uint32_t)lo << 16);
+    norms[(int64_t)l * Kp + k] = nv;
+  }
+  tile[j * 64 + lane] = make_uint4(w0, 0u, 0u, 0u);
 }
 
 // fp32 codebook copy with row stride dp and zero padding.
@@ -92,11 +88,9 @@ hipError_t launch_prepare(const float *cb, int L, int K, int d, float *norms, ui
                                                                                       dp, cbpad);
   }
   const int Kp = (int)padded_k(K), S = (int)(padded_d(d) / kStageCols);
-  const int64_t waves = (int64_t)L * Kp;
-  norms_kernel<<<dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, s>>>(cb, L, K, d, Kp, norms);
-  const int64_t chunks = stream_bytes(L, K, d) / 16;
-  stream_kernel<<<dim3((unsigned)ceil_div(chunks, 256)), dim3(256), 0, s>>>(
-      cb, norms, L, K, d, Kp, S, reinterpret_cast<uint4 *>(stream));
+  const int64_t tiles = (int64_t)L * (Kp / kTileCw);
+  prepare_tile_kernel<<<dim3((unsigned)tiles), dim3(256), 0, s>>>(
+      cb, L, K, d, Kp, S, norms, reinterpret_cast<uint4 *>(stream));
   return hipGetLastError();
 }
 

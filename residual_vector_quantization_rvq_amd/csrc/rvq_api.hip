@@ -298,8 +298,7 @@ rvq_status rvq_level_stats(const int32_t *ids, int64_t n, int32_t L, int32_t K, 
   double *mpart = (double *)(ws + align256(hist_partial_bytes(n, L, K)));
   HIP_TRY(launch_hist(ids, n, L, K, hist, hpart, bad_ids, stream), "histogram launch");
   if (with_msr)
-    HIP_TRY(launch_msr(x, x_dtype == RVQ_BF16, ids, n, d, codebooks, L, K, msr, mpart, bad_ids,
-                       stream),
+    HIP_TRY(launch_msr(x, x_dtype == RVQ_BF16, ids, n, d, codebooks, L, K, msr, mpart, stream),
             "msr launch");
   return RVQ_OK;
 }

@@ -117,47 +117,98 @@ hipError_t launch_hist(const int32_t *ids, int64_t n, int L, int K, int64_t *his
   return hipGetLastError();
 }
 
-// One wave per row, 4 rows per workgroup.  Each lane walks its columns,
-// subtracting the row's codewords level by level in fp32 and accumulating
-// the squared residual of every level in fp64; the wave then sums lanes in
-// a fixed butterfly, and the workgroup sums its 4 rows in wave order.
-constexpr int kMsrLevelChunk = 16;
+// Each workgroup takes kMsrRowsPerBlock consecutive rows; wave w takes rows
+// w, w+4, ... of them.  A lane owns float4 column groups of its row (scalar
+// columns when d is not a multiple of 4), subtracts the row's codewords
+// level by level in fp32, with the gathers of up to kMsrLevelChunk levels
+// in flight, and accumulates each level's squared residual in fp64 over its
+// rows in order.  The wave then sums lanes in a fixed butterfly and the
+// workgroup sums its waves in order, so every sum's order depends only on n.
+// An out-of-range ID adds nothing (the histogram pass counts it).
+// Levels past kMsrLevelChunk are done in further passes that recompute the
+// residual prefix.
+constexpr int kMsrRowsPerBlock = 32;
+constexpr int kMsrLevelChunk = 8;
 
+__device__ __forceinline__ float4 load_x4(const void *x, bool x_bf16, int64_t row, int d4, int i4) {
+  if (x_bf16) {
+    const uint2 b = reinterpret_cast<const uint2 *>(x)[row * d4 + i4];
+    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                       __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
+  }
+  return reinterpret_cast<const float4 *>(x)[row * d4 + i4];
+}
+
+__device__ __forceinline__ double sq4(double acc, float4 r) {
+  acc = fma((double)r.x, (double)r.x, acc);
+  acc = fma((double)r.y, (double)r.y, acc);
+  acc = fma((double)r.z, (double)r.z, acc);
+  return fma((double)r.w, (double)r.w, acc);
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void msr_rows_kernel(const void *__restrict__ x, int x_bf16,
                                                        const int32_t *__restrict__ ids, int64_t n,
                                                        int d, const float *__restrict__ cb, int L,
                                                        int K, double *__restrict__ partial,
-                                                       uint32_t *__restrict__ bad) {
-  __shared__ double rowsum[4][64];
+                                                       int64_t nblocks) {
+  __shared__ double wsum[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  const bool live = row < n;
-  const int32_t *rid = ids + (live ? row : 0) * L;
-  if (live && bad) {
-    const int my_id = lane < L ? rid[lane] : 0;
-    const unsigned long long m = __ballot(my_id < 0 || my_id >= K);
-    if (lane == 0 && m) atomicAdd(bad, (uint32_t)__popcll(m));
-  }
+  const int64_t r0 = (int64_t)blockIdx.x * kMsrRowsPerBlock;
+  const int d4 = d >> 2;
+  const float4 *cb4 = reinterpret_cast<const float4 *>(cb);
   for (int lc = 0; lc < L; lc += kMsrLevelChunk) {
     double sq[kMsrLevelChunk];
 #pragma unroll
     for (int u = 0; u < kMsrLevelChunk; ++u) sq[u] = 0.0;
-    if (live) {
-      for (int i = lane; i < d; i += 64) {
-        float r = x_bf16 ? bf16_bits_to_f32(((const uint16_t *)x)[row * d + i])
-                         : ((const float *)x)[row * d + i];
-        for (int l = 0; l < lc; ++l) {
-          const int id = rid[l];
-          if (id >= 0 && id < K) r -= cb[((int64_t)l * K + id) * d + i];
-        }
+    for (int j = wave; j < kMsrRowsPerBlock; j += 4) {
+      const int64_t row = r0 + j;  // wave-uniform
+      if (row >= n) break;
+      const int32_t *rid = ids + row * L;
+      if constexpr (VEC) {
+        for (int i4 = lane; i4 < d4; i4 += 64) {
+          float4 r = load_x4(x, x_bf16, row, d4, i4);
+          for (int l = 0; l < lc; ++l) {
+            const int id = rid[l];
+            if (id >= 0 && id < K) {
+              const float4 c = cb4[((int64_t)l * K + id) * d4 + i4];
+              r.x -= c.x; r.y -= c.y; r.z -= c.z; r.w -= c.w;
+            }
+          }
+          float4 v[kMsrLevelChunk];
+          bool ok[kMsrLevelChunk];
 #pragma unroll
-        for (int u = 0; u < kMsrLevelChunk; ++u) {
-          const int l = lc + u;
-          if (l < L) {
+          for (int u = 0; u < kMsrLevelChunk; ++u) {
+            const int l = lc + u;
+            const int id = l < L ? rid[l] : -1;  // uniform load
+            ok[u] = id >= 0 && id < K;
+            v[u] = ok[u] ? cb4[((int64_t)l * K + id) * d4 + i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+          for (int u = 0; u < kMsrLevelChunk; ++u) {
+            if (lc + u < L) {
+              r.x -= v[u].x; r.y -= v[u].y; r.z -= v[u].z; r.w -= v[u].w;
+              sq[u] = sq4(sq[u], r);
+            }
+          }
+        }
+      } else {
+        for (int i = lane; i < d; i += 64) {
+          float r = x_bf16 ? bf16_bits_to_f32(((const uint16_t *)x)[row * d + i])
+                           : ((const float *)x)[row * d + i];
+          for (int l = 0; l < lc; ++l) {
             const int id = rid[l];
             if (id >= 0 && id < K) r -= cb[((int64_t)l * K + id) * d + i];
-            sq[u] += (double)r * (double)r;
+          }
+#pragma unroll
+          for (int u = 0; u < kMsrLevelChunk; ++u) {
+            const int l = lc + u;
+            if (l < L) {
+              const int id = rid[l];
+              if (id >= 0 && id < K) r -= cb[((int64_t)l * K + id) * d + i];
+              sq[u] = fma((double)r, (double)r, sq[u]);
+            }
           }
         }
       }
@@ -165,53 +216,59 @@ __global__ __launch_bounds__(256) void msr_rows_kernel(const void *__restrict__ 
 #pragma unroll
     for (int u = 0; u < kMsrLevelChunk; ++u) {
       const double t = wave_sum_f64(sq[u]);
-      if (lane == 0 && lc + u < L) rowsum[wave][lc + u] = t;
+      if (lane == 0 && lc + u < L) wsum[wave][lc + u] = t;
     }
   }
   __syncthreads();
   if (threadIdx.x < L) {
     const int l = threadIdx.x;
-    double s = rowsum[0][l];
-    s += rowsum[1][l];
-    s += rowsum[2][l];
-    s += rowsum[3][l];
-    partial[(int64_t)blockIdx.x * L + l] = s;
+    double s = wsum[0][l];
+    s += wsum[1][l];
+    s += wsum[2][l];
+    s += wsum[3][l];
+    partial[(int64_t)l * nblocks + blockIdx.x] = s;
   }
 }
 
-// msr[l] = (sum of the workgroup partials) / n; thread t sums partials
-// t, t+256, ... in order, then a fixed tree over the 256 threads.
+// msr[l] = (sum of the workgroup partials) / n, partials stored level-major;
+// workgroup l: thread t sums partials t, t+256, ... in order, then a fixed
+// tree over the 256 threads.
 __global__ __launch_bounds__(256) void msr_final_kernel(const double *__restrict__ partial,
-                                                        int64_t nblocks, int L, int64_t n,
+                                                        int64_t nblocks, int64_t n,
                                                         double *__restrict__ msr) {
   __shared__ double sh[256];
-  for (int l = 0; l < L; ++l) {
-    double s = 0.0;
-    for (int64_t b = threadIdx.x; b < nblocks; b += 256) s += partial[b * L + l];
-    sh[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-      if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) msr[l] = n > 0 ? sh[0] / (double)n : 0.0;
+  const int l = blockIdx.x;
+  double s = 0.0;
+  for (int64_t b = threadIdx.x; b < nblocks; b += 256) s += partial[(int64_t)l * nblocks + b];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
     __syncthreads();
   }
+  if (threadIdx.x == 0) msr[l] = n > 0 ? sh[0] / (double)n : 0.0;
 }
 
 size_t msr_partial_bytes(int64_t n, int L) {
-  const int64_t blocks = n > 0 ? ceil_div(n, 4) : 1;
+  const int64_t blocks = n > 0 ? ceil_div(n, kMsrRowsPerBlock) : 1;
   return (size_t)blocks * (size_t)L * sizeof(double);
 }
 
 hipError_t launch_msr(const void *x, bool x_bf16, const int32_t *ids, int64_t n, int d,
-                      const float *cb, int L, int K, double *msr, double *partial, uint32_t *bad,
-                      hipStream_t s) {
-  const int64_t blocks = n > 0 ? ceil_div(n, 4) : 0;
-  if (blocks > 0)
-    msr_rows_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(x, x_bf16 ? 1 : 0, ids, n, d, cb,
-                                                                 L, K, partial, bad);
-  msr_final_kernel<<<dim3(1), dim3(256), 0, s>>>(partial, blocks, L, n, msr);
+                      const float *cb, int L, int K, double *msr, double *partial, hipStream_t s) {
+  const int64_t blocks = n > 0 ? ceil_div(n, kMsrRowsPerBlock) : 0;
+  // float4 columns need d % 4 == 0 and 16-byte (fp32) / 8-byte (bf16) row starts,
+  // which the aligned base pointers then give for every row
+  const bool vec = (d & 3) == 0;
+  if (blocks > 0) {
+    if (vec)
+      msr_rows_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+          x, x_bf16 ? 1 : 0, ids, n, d, cb, L, K, partial, blocks);
+    else
+      msr_rows_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+          x, x_bf16 ? 1 : 0, ids, n, d, cb, L, K, partial, blocks);
+  }
+  msr_final_kernel<<<dim3((unsigned)L), dim3(256), 0, s>>>(partial, blocks, n, msr);
   return hipGetLastError();
 }
 

@@ -236,6 +236,26 @@ def test_invalid_ids_are_counted_and_skipped(rvq, dev):
     np.testing.assert_array_equal(hist.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("d,x_dtype", [(36, "f32"), (37, "f32"), (40, "bf16")])
+def test_invalid_ids_with_msr_are_counted_once(rvq, dev, d, x_dtype):
+    # d = 36 and 40 take the float4 path, d = 37 the scalar one; an invalid ID
+    # adds nothing to the residual, which is the same as a zero codeword
+    w = workloads.random_problem(44, 70, d, 3, 50, x_dtype=x_dtype)
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids_h = np.random.default_rng(6).integers(0, w.K, size=(70, 3)).astype(np.int32)
+    ids_h[4, 0] = -7
+    ids_h[33, 2] = w.K
+    ids_h[69, 1] = w.K + 100
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    hist, msr = rvq.rvq_level_stats(torch.from_numpy(ids_h).to(dev), w.K, x, cb, bad_ids=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 3
+    ok = (ids_h >= 0) & (ids_h < w.K)
+    ext = np.concatenate([w.codebooks, np.zeros((3, 1, d), dtype=np.float32)], axis=1)
+    parity.check_msr(msr.cpu().numpy(), w.x, x_dtype, np.where(ok, ids_h, w.K).astype(np.int32), ext)
+
+
 def test_prefix_decode_levels(rvq, dev):
     w = workloads.random_problem(43, 90, 72, 5, 64)
     ids_h = np.random.default_rng(6).integers(0, w.K, size=(90, 5)).astype(np.int32)
