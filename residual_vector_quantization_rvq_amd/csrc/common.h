@@ -85,12 +85,23 @@ constexpr float kPadNorm = 3.0e38f;
 // Stage counts (features / 64) with an instantiated encoder; a width is
 // padded with zeros up to the next one (zero features change no distance).
 #define RVQ_FOR_EACH_STAGE_COUNT(X) X(1) X(2) X(4) X(8) X(12) X(16) X(18) X(20)
+constexpr int kStageCounts[] = {1, 2, 4, 8, 12, 16, 18, 20};
 __host__ __device__ inline int stages_for(int64_t d) {
   const int s = (int)ceil_div(d, kStageCols);
-  const int counts[] = {1, 2, 4, 8, 12, 16, 18, 20};
-  for (int c : counts)
+  for (int c : kStageCounts)
     if (c >= s) return c;
   return 0;
+}
+// The instantiated stage count below S (0 for the smallest): a row encoded
+// with S stages is wider than 64 * prev_stage_count(S) features, so its first
+// 4 * prev_stage_count(S) k-steps of 16 features are all inside the row.
+__host__ __device__ constexpr int prev_stage_count(int S) {
+  int p = 0;
+  for (int c : kStageCounts) {
+    if (c >= S) return p;
+    p = c;
+  }
+  return p;
 }
 __host__ __device__ inline int64_t padded_k(int64_t K) { return round_up(K, kTileCw); }
 __host__ __device__ inline int64_t padded_d(int64_t d) { return (int64_t)stages_for(d) * kStageCols; }

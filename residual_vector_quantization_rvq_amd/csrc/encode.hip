@@ -73,7 +73,7 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   EncodeArgs a = a_in;
   const unsigned row_waves = (unsigned)ceil_div(a.n, 4);
   a.x16 = nullptr;
-  if (p.fused && a.x_bf16 && a.dp == a.d) {
+  if (p.fused && a.x_bf16 && a.dp == a.d && (a.L > 1 || a.residual_out)) {
     // level 0 of the fused encoder reads the bf16 rows directly
     a.x16 = (const uint16_t *)a.x;
     a.src0 = nullptr;

@@ -266,17 +266,37 @@ __device__ __forceinline__ u32x4 to_bf16x8(const float (&v)[8]) {
   return q;
 }
 
+// Re-defines values through an empty asm: code that computes addresses from
+// them cannot move above this point, which bounds how far the compiler
+// hoists loads (and so the registers they hold).
+template <typename T>
+__device__ __forceinline__ void opaque1(T &v) {
+  asm volatile("" : "+v"(v) : : "memory");
+}
+template <typename... T>
+__device__ __forceinline__ void opaque(T &...v) {
+  (opaque1(v), ...);
+}
+
 // B-fragments of one row half: lane half h holds features ks*16 + h*8 + e.
+// Loads are issued eight k-steps at a time before any fragment is pinned,
+// so the waits for them overlap.
 template <int KS>
 __device__ __forceinline__ void build_bfrags(RowFrags<KS> &bfr, const float *src, int64_t row,
                                              int dp, int h) {
-  static_for<0, KS>([&](auto K_) {
-    constexpr int ks = decltype(K_)::value;
-    float v[8];
-    read8(src, row, dp, ks * 16 + h * 8, ks * 16 < dp, v);
-    bfr.template set<ks>(to_bf16x8(v));
-    // bound the loads the scheduler hoists ahead (register pressure)
-    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+  static_for<0, (KS + 7) / 8>([&](auto G_) {
+    constexpr int g = decltype(G_)::value;
+    constexpr int n = KS - g * 8 < 8 ? KS - g * 8 : 8;
+    float v[8][8];
+    static_for<0, n>([&](auto U_) {
+      constexpr int ks = g * 8 + decltype(U_)::value;
+      read8(src, row, dp, ks * 16 + h * 8, ks * 16 < dp, v[decltype(U_)::value]);
+    });
+    static_for<0, n>([&](auto U_) {
+      constexpr int ks = g * 8 + decltype(U_)::value;
+      bfr.template set<ks>(to_bf16x8(v[decltype(U_)::value]));
+    });
+    opaque(row);
   });
 }
 
@@ -294,15 +314,21 @@ __device__ __forceinline__ void read_src(const uint16_t *src, int64_t row, int d
 template <int KS>
 __device__ __forceinline__ void build_bfrags_bf16(RowFrags<KS> &bfr, const uint16_t *src,
                                                   int64_t row, int dp, int h) {
-  static_for<0, KS>([&](auto K_) {
-    constexpr int ks = decltype(K_)::value;
-    u32x4 f = {0u, 0u, 0u, 0u};
-    if (ks * 16 < dp) {
-      const uint4 q = *reinterpret_cast<const uint4 *>(src + row * dp + ks * 16 + h * 8);
-      f = u32x4{q.x, q.y, q.z, q.w};
-    }
-    bfr.template set<ks>(f);
-    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+  static_for<0, (KS + 7) / 8>([&](auto G_) {
+    constexpr int g = decltype(G_)::value;
+    constexpr int n = KS - g * 8 < 8 ? KS - g * 8 : 8;
+    u32x4 f[8];
+    static_for<0, n>([&](auto U_) {
+      constexpr int ks = g * 8 + decltype(U_)::value;
+      const bool active = ks * 16 < dp;
+      const uint4 q = *reinterpret_cast<const uint4 *>(src + row * dp + (active ? ks * 16 + h * 8 : 0));
+      f[decltype(U_)::value] = active ? u32x4{q.x, q.y, q.z, q.w} : u32x4{0u, 0u, 0u, 0u};
+    });
+    static_for<0, n>([&](auto U_) {
+      constexpr int ks = g * 8 + decltype(U_)::value;
+      bfr.template set<ks>(f[decltype(U_)::value]);
+    });
+    opaque(row);
   });
 }
 
@@ -357,19 +383,94 @@ __device__ __forceinline__ int rescore_update(const float *src, float *dst, bool
   return take2 ? c2 : c1;
 }
 
+// ---- group loads for the fused update ----
+// A group is four k-steps of one lane: 32 bytes (8 fp32) per k-step at a
+// 64-byte stride, or 16 bytes (8 bf16) at a 32-byte stride.  All loads of a
+// group are issued in one block and waited for at its end, so a group costs
+// one memory latency however the compiler would have scheduled them.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define RVQ_GL(o, p, off) "global_load_dwordx4 %[" #o "], %[" #p "], off offset:" #off "\n\t"
+#define RVQ_GL8(o, p)                                                                         \
+  RVQ_GL(o##0, p, 0) RVQ_GL(o##1, p, 16) RVQ_GL(o##2, p, 64) RVQ_GL(o##3, p, 80)              \
+      RVQ_GL(o##4, p, 128) RVQ_GL(o##5, p, 144) RVQ_GL(o##6, p, 192) RVQ_GL(o##7, p, 208)
+#define RVQ_GL4H(o, p) RVQ_GL(o##0, p, 0) RVQ_GL(o##1, p, 32) RVQ_GL(o##2, p, 64) RVQ_GL(o##3, p, 96)
+#define RVQ_OUT8(o, v)                                                                        \
+  [o##0] "=&v"(v[0]), [o##1] "=&v"(v[1]), [o##2] "=&v"(v[2]), [o##3] "=&v"(v[3]),             \
+      [o##4] "=&v"(v[4]), [o##5] "=&v"(v[5]), [o##6] "=&v"(v[6]), [o##7] "=&v"(v[7])
+#define RVQ_OUT4(o, v) [o##0] "=&v"(v[0]), [o##1] "=&v"(v[1]), [o##2] "=&v"(v[2]), [o##3] "=&v"(v[3])
+
+// r (row features), a and b (two codewords) of one group.
+__device__ __forceinline__ void group_load3(const float *pr, const float *pa, const float *pb,
+                                            f32x4 (&r)[8], f32x4 (&a)[8], f32x4 (&b)[8]) {
+  asm volatile(RVQ_GL8(r, pr) RVQ_GL8(a, pa) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
+               : RVQ_OUT8(r, r), RVQ_OUT8(a, a), RVQ_OUT8(b, b)
+               : [pr] "v"(pr), [pa] "v"(pa), [pb] "v"(pb)
+               : "memory");
+}
+__device__ __forceinline__ void group_load3(const uint16_t *pr, const float *pa, const float *pb,
+                                            f32x4 (&r)[8], f32x4 (&a)[8], f32x4 (&b)[8]) {
+  u32x4 q[4];
+  asm volatile(RVQ_GL4H(q, pr) RVQ_GL8(a, pa) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
+               : RVQ_OUT4(q, q), RVQ_OUT8(a, a), RVQ_OUT8(b, b)
+               : [pr] "v"(pr), [pa] "v"(pa), [pb] "v"(pb)
+               : "memory");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[2 * j] = f32x4{__uint_as_float(q[j][0] << 16), __uint_as_float(q[j][0] & 0xffff0000u),
+                     __uint_as_float(q[j][1] << 16), __uint_as_float(q[j][1] & 0xffff0000u)};
+    r[2 * j + 1] = f32x4{__uint_as_float(q[j][2] << 16), __uint_as_float(q[j][2] & 0xffff0000u),
+                         __uint_as_float(q[j][3] << 16), __uint_as_float(q[j][3] & 0xffff0000u)};
+  }
+}
+__device__ __forceinline__ void group_load2(const float *pr, const float *pb, f32x4 (&r)[8],
+                                            f32x4 (&b)[8]) {
+  asm volatile(RVQ_GL8(r, pr) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
+               : RVQ_OUT8(r, r), RVQ_OUT8(b, b)
+               : [pr] "v"(pr), [pb] "v"(pb)
+               : "memory");
+}
+__device__ __forceinline__ void group_load2(const uint16_t *pr, const float *pb, f32x4 (&r)[8],
+                                            f32x4 (&b)[8]) {
+  u32x4 q[4];
+  asm volatile(RVQ_GL4H(q, pr) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
+               : RVQ_OUT4(q, q), RVQ_OUT8(b, b)
+               : [pr] "v"(pr), [pb] "v"(pb)
+               : "memory");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[2 * j] = f32x4{__uint_as_float(q[j][0] << 16), __uint_as_float(q[j][0] & 0xffff0000u),
+                     __uint_as_float(q[j][1] << 16), __uint_as_float(q[j][1] & 0xffff0000u)};
+    r[2 * j + 1] = f32x4{__uint_as_float(q[j][2] << 16), __uint_as_float(q[j][2] & 0xffff0000u),
+                         __uint_as_float(q[j][3] << 16), __uint_as_float(q[j][3] & 0xffff0000u)};
+  }
+}
+
+__device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // The same rescoring and update for the fused encoder, which also rebuilds
 // the row's B-fragments for the next level in the same pass: a lane's
 // update covers exactly the features its fragments hold (ks*16 + h*8 + e),
-// so the new residual never has to be read back.  Every k-step is unrolled
-// (fragments live in fixed registers); k-steps past the padded width dp are
-// zero and touch no memory.
-template <int KS, typename SrcT>
+// so the new residual never has to be read back.  Work goes in groups of
+// four k-steps (fragments live in fixed registers, so every group is
+// unrolled); a group wholly inside the row uses one block of loads, and
+// only a group that crosses the row's end (padded widths) goes k-step by
+// k-step (k-steps past dp are zero and touch no memory).  With STORE the new
+// residual goes to dst for every lane: lanes past row n-1 work on row n-1
+// and store exactly what its own lane stores, so no lane-dependent branch
+// splits the loads.
+template <int KS, bool STORE, typename SrcT>
 __device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const SrcT *src,
-                                                    float *dst, bool store, int64_t row, int dp,
+                                                    float *dst, int64_t row, int dp,
                                                     const float *cb_l, int c1, int c2, bool v2,
                                                     int h) {
+  static_assert(KS % 4 == 0, "k-steps come in stages of four");
   float p1 = 0.f, p2 = 0.f;
-  static_for<0, KS>([&](auto K_) {
+  const int64_t lane_off = row * dp + h * 8;
+  const int64_t off1 = (int64_t)c1 * dp + h * 8, off2 = (int64_t)c2 * dp + h * 8;
+  auto kstep = [&](auto K_) {  // one k-step, for groups crossing the row's end
     constexpr int ks = decltype(K_)::value;
     const int i0 = ks * 16 + h * 8;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -386,33 +487,75 @@ __device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const Src
         p2 = fmaf(u, u, p2);
         v[e] = t;
       }
-      if (store) write8(dst, row, dp, i0, v);
+      if constexpr (STORE) write8(dst, row, dp, i0, v);
     }
     bfr.template set<ks>(to_bf16x8(v));
-    if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+  };
+  static_for<0, KS / 4>([&](auto G_) {
+    constexpr int g = decltype(G_)::value;
+    if (g * 64 + 64 <= dp) {
+      f32x4 r[8], a[8], b[8];
+      group_load3(src + lane_off + g * 64, cb_l + off1 + g * 64, cb_l + off2 + g * 64, r, a, b);
+      static_for<0, 4>([&](auto J_) {
+        constexpr int j = decltype(J_)::value;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float re = r[2 * j + e / 4][e % 4];
+          const float t = re - a[2 * j + e / 4][e % 4];
+          const float u = re - b[2 * j + e / 4][e % 4];
+          p1 = fmaf(t, t, p1);
+          p2 = fmaf(u, u, p2);
+          v[e] = t;
+        }
+        if constexpr (STORE) store8(dst + lane_off + g * 64 + j * 16, v);
+        bfr.template set<g * 4 + j>(to_bf16x8(v));
+      });
+    } else {
+      static_for<g * 4, g * 4 + 4>(kstep);
+    }
   });
   const float q1 = __shfl_xor(p1, 32, 64);
   const float q2 = __shfl_xor(p2, 32, 64);
   const float d1 = h ? q1 + p1 : p1 + q1;
   const float d2 = h ? q2 + p2 : p2 + q2;
   const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
+  // Rows where the second candidate won are redone.  Every lane of the wave
+  // takes part (no divergent branch, so fragments are rewritten in place):
+  // a lane whose first candidate won recomputes exactly r - c1 again.
   if (__ballot(take2)) {
-    if (take2) {
-      static_for<0, KS>([&](auto K_) {
-        constexpr int ks = decltype(K_)::value;
-        const int i0 = ks * 16 + h * 8;
-        if (ks * 16 < dp) {
-          float r[8], b[8], v[8];
-          read_src(src, row, dp, i0, r);
-          read8(cb_l, c2, dp, i0, true, b);
+    const int cs = take2 ? c2 : c1;
+    const int64_t offs = (int64_t)cs * dp + h * 8;
+    auto redo_kstep = [&](auto K_) {
+      constexpr int ks = decltype(K_)::value;
+      const int i0 = ks * 16 + h * 8;
+      if (ks * 16 < dp) {
+        float r[8], b[8], v[8];
+        read_src(src, row, dp, i0, r);
+        read8(cb_l, cs, dp, i0, true, b);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = r[e] - b[e];
-          if (store) write8(dst, row, dp, i0, v);
-          bfr.template set<ks>(to_bf16x8(v));
-        }
-        if constexpr (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-      });
-    }
+        for (int e = 0; e < 8; ++e) v[e] = r[e] - b[e];
+        if constexpr (STORE) write8(dst, row, dp, i0, v);
+        bfr.template set<ks>(to_bf16x8(v));
+      }
+    };
+    static_for<0, KS / 4>([&](auto G_) {
+      constexpr int g = decltype(G_)::value;
+      if (g * 64 + 64 <= dp) {
+        f32x4 r[8], b[8];
+        group_load2(src + lane_off + g * 64, cb_l + offs + g * 64, r, b);
+        static_for<0, 4>([&](auto J_) {
+          constexpr int j = decltype(J_)::value;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = r[2 * j + e / 4][e % 4] - b[2 * j + e / 4][e % 4];
+          if constexpr (STORE) store8(dst + lane_off + g * 64 + j * 16, v);
+          bfr.template set<g * 4 + j>(to_bf16x8(v));
+        });
+      } else {
+        static_for<g * 4, g * 4 + 4>(redo_kstep);
+      }
+    });
   }
   return take2 ? c2 : c1;
 }
@@ -530,7 +673,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
     int slot_t = 0;  // ring slot of the current tile's stage 0
     u32x4 pre[4];    // first A-fragments of the next stage, read ahead
-    for (int tt = 0; tt < ntiles; ++tt) {
+    // One tile: FIRST / LAST say whether it is the level's first / last tile
+    // (0 no, 1 yes, 2 only known at run time), so the middle tiles carry no
+    // run-time tests of the level's boundaries.
+    auto tile = [&](int tt, auto FIRST_, auto LAST_) {
+      constexpr int FIRST = decltype(FIRST_)::value, LAST = decltype(LAST_)::value;
       f32x16 acc[4];
       static_for<0, S>([&](auto S_) {
         constexpr int s = decltype(S_)::value;
@@ -542,21 +689,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // slot the refill below overwrites.  At the start of a level
         // (update-phase accesses may be interleaved) and near its end, wait
         // for every load.
-        if (g == 0 || g + kAhead - 1 >= nst) wait_vmcnt<0>();
-        else wait_vmcnt<dma_after_next<S>(s)>();
+        if constexpr (FIRST == 2 || LAST == 2) {
+          if (g == 0 || g + kAhead - 1 >= nst) wait_vmcnt<0>();
+          else wait_vmcnt<dma_after_next<S>(s)>();
+        } else if constexpr ((FIRST == 1 && s == 0) || (LAST == 1 && s + kAhead - 1 >= S)) {
+          wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<dma_after_next<S>(s)>();
+        }
         barrier_only();
         int slot = slot_t + s % kSlots;
         slot = slot >= kSlots ? slot - kSlots : slot;
         const int nslot = slot + 1 == kSlots ? 0 : slot + 1;
         const uint32_t addr = ring_lds + (uint32_t)slot * kSlotBytes + (uint32_t)lane * 16u;
         const uint32_t naddr = ring_lds + (uint32_t)nslot * kSlotBytes + (uint32_t)lane * 16u;
-        if constexpr (s == 0) {
+        if constexpr (s == 0 && FIRST == 1) read_tile_norms(pre, addr);
+        if constexpr (s == 0 && FIRST == 2) {
           if (tt == 0) read_tile_norms(pre, addr);
         }
         // refill the slot of stage g-1 with stage g + kAhead
-        if (g + kAhead < nst) {
-          int rslot = slot + kAhead;
-          rslot = rslot >= kSlots ? rslot - kSlots : rslot;
+        int rslot = slot + kAhead;
+        rslot = rslot >= kSlots ? rslot - kSlots : rslot;
+        if constexpr (LAST == 2) {
+          if (g + kAhead < nst)
+            issue_stage(ls, tile_u4, tt + (s + kAhead) / S, (s + kAhead) % S, rslot, ring_lds,
+                        wave, lane);
+        } else if constexpr (LAST == 0 || s + kAhead < S) {
           issue_stage(ls, tile_u4, tt + (s + kAhead) / S, (s + kAhead) % S, rslot, ring_lds,
                       wave, lane);
         }
@@ -566,7 +724,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       slot_t += S % kSlots;
       slot_t = slot_t >= kSlots ? slot_t - kSlots : slot_t;
       mfma_drain(acc);
-
       // Epilogue: accumulator element i of sub-tile j is codeword
       // j*32 + (i/4)*8 + h*4 + i%4 of the tile for this lane's row.  Per
       // 64-codeword block p (sub-tiles 2p, 2p+1) the tag jj*16 + i is unique.
@@ -597,6 +754,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         R2 = d ? nw : old;
         B2 = d ? base : oldb;
       }
+    };
+    using TNo = std::integral_constant<int, 0>;
+    using TYes = std::integral_constant<int, 1>;
+    using TRun = std::integral_constant<int, 2>;
+    if constexpr (S >= kAhead) {
+      // with at least kAhead stages per tile only the first and the last
+      // tile of a level see its boundaries
+      if (ntiles == 1) {
+        tile(0, TYes{}, TYes{});
+      } else {
+        tile(0, TYes{}, TNo{});
+        for (int tt = 1; tt + 1 < ntiles; ++tt) tile(tt, TNo{}, TNo{});
+        tile(ntiles - 1, TNo{}, TYes{});
+      }
+    } else {
+      for (int tt = 0; tt < ntiles; ++tt) tile(tt, TRun{}, TRun{});
     }
 
     // Decode the tags, then merge with the other half of the row (lanes L
@@ -626,14 +799,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       const bool last = l == a.L - 1;
       float *dst = last ? a.res_final : a.rbuf[(l + 1) & 1];
       const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
-      // (lanes past row n-1 work on row n-1 and store nothing)
-      const bool store = live && dst != nullptr;
+      // (a.x16 is set only when level 0 stores a residual)
       int id;
       if (l == 0 && a.x16)
-        id = rescore_update_frags<KS>(bfr, a.x16, dst, store, rowc, a.dp, cb_l, c1, c2, v2, h);
+        id = rescore_update_frags<KS, true>(bfr, a.x16, dst, rowc, a.dp, cb_l, c1, c2, v2, h);
+      else if (dst)
+        id = rescore_update_frags<KS, true>(bfr, l == 0 ? a.src0 : a.rbuf[l & 1], dst, rowc,
+                                            a.dp, cb_l, c1, c2, v2, h);
       else
-        id = rescore_update_frags<KS>(bfr, l == 0 ? a.src0 : a.rbuf[l & 1], dst, store, rowc,
-                                      a.dp, cb_l, c1, c2, v2, h);
+        id = rescore_update_frags<KS, false>(bfr, l == 0 ? a.src0 : a.rbuf[l & 1], dst, rowc,
+                                             a.dp, cb_l, c1, c2, v2, h);
       if (live && h == 0) a.ids[row * a.L + l] = id;
     } else {
       if (live && h == 0)
