@@ -95,23 +95,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   RVQ_RD(p0, naddr, 0) RVQ_RD(p1, naddr, 1024) RVQ_RD(p2, naddr, 2048) RVQ_RD(p3, naddr, 3072)
 #define RVQ_WAIT(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
 
+// Refill loads placed inside a block, one after each k-step's MFMAs, so they
+// issue while the matrix core is busy: this wave's four 1 KB blocks of the
+// stage being refilled (global source gsrc, LDS destination lds).  Lane i's
+// 16 bytes land at M0 + offset + 16*i: the instruction offset moves the
+// global and the LDS address alike, so M0 is set once.
+#define RVQ_D0 "s_mov_b32 m0, %[lds]\n\tglobal_load_lds_dwordx4 %[gsrc], off\n\t"
+#define RVQ_D1 "global_load_lds_dwordx4 %[gsrc], off offset:1024\n\t"
+#define RVQ_D2 "global_load_lds_dwordx4 %[gsrc], off offset:2048\n\t"
+#define RVQ_D3 "global_load_lds_dwordx4 %[gsrc], off offset:3072\n\t"
+
 // A stage inside a tile: p holds its k-step 0 on entry.
-#define RVQ_STAGE_BODY(NEXT)                                                               \
-  RVQ_WAIT(0) RVQ_K1(t0, t1, t2, t3) RVQ_MF4(p0, p1, p2, p3, b0) RVQ_K2(t4, t5, t6, t7) \
-      RVQ_WAIT(4) RVQ_MF4(t0, t1, t2, t3, b1) RVQ_K3(t0, t1, t2, t3) RVQ_WAIT(4)            \
-          RVQ_MF4(t4, t5, t6, t7, b2) NEXT RVQ_WAIT(4) RVQ_MF4(t0, t1, t2, t3, b3) RVQ_WAIT(0)
+#define RVQ_STAGE_BODY(NEXT, D0, D1, D2, D3)                                                \
+  RVQ_WAIT(0) RVQ_K1(t0, t1, t2, t3) RVQ_MF4(p0, p1, p2, p3, b0) D0 RVQ_K2(t4, t5, t6, t7) \
+      RVQ_WAIT(4) RVQ_MF4(t0, t1, t2, t3, b1) D1 RVQ_K3(t0, t1, t2, t3) RVQ_WAIT(4)         \
+          RVQ_MF4(t4, t5, t6, t7, b2) D2 NEXT RVQ_WAIT(4) RVQ_MF4(t0, t1, t2, t3, b3) D3    \
+              RVQ_WAIT(0)
 
 // The stage opening a tile: p holds the norm k-step on entry, and the
 // accumulators start from ||c||^2 (B = ones at k = 0, 1).
-#define RVQ_STAGE0_BODY(NEXT)                                                              \
+#define RVQ_STAGE0_BODY(NEXT, D0, D1, D2, D3)                                               \
   RVQ_WAIT(0) RVQ_K0(t0, t1, t2, t3)                                                     \
   "v_mfma_f32_32x32x16_bf16 %[c0], %[p0], %[bn], 0\n\t"                                      \
   "v_mfma_f32_32x32x16_bf16 %[c1], %[p1], %[bn], 0\n\t"                                      \
   "v_mfma_f32_32x32x16_bf16 %[c2], %[p2], %[bn], 0\n\t"                                      \
   "v_mfma_f32_32x32x16_bf16 %[c3], %[p3], %[bn], 0\n\t" RVQ_K1(t4, t5, t6, t7) RVQ_WAIT(4) \
-      RVQ_MF4(t0, t1, t2, t3, b0) RVQ_K2(t0, t1, t2, t3) RVQ_WAIT(4)                        \
-          RVQ_MF4(t4, t5, t6, t7, b1) RVQ_K3(t4, t5, t6, t7) RVQ_WAIT(4)                    \
-              RVQ_MF4(t0, t1, t2, t3, b2) NEXT RVQ_WAIT(4) RVQ_MF4(t4, t5, t6, t7, b3) RVQ_WAIT(0)
+      RVQ_MF4(t0, t1, t2, t3, b0) D0 RVQ_K2(t0, t1, t2, t3) RVQ_WAIT(4)                     \
+          RVQ_MF4(t4, t5, t6, t7, b1) D1 RVQ_K3(t4, t5, t6, t7) RVQ_WAIT(4)                 \
+              RVQ_MF4(t0, t1, t2, t3, b2) D2 NEXT RVQ_WAIT(4) RVQ_MF4(t4, t5, t6, t7, b3) D3 \
+                  RVQ_WAIT(0)
 
 #define RVQ_TEMPS                                                                          \
   [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [t4] "=&v"(t[4]), \
@@ -119,46 +131,58 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define RVQ_PREF [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3])
 
 // FIRST: the stage opens a tile.  NEXT_TILE: the next stage opens a tile.
-// B_IN_AGPR: the stage's row fragments live in AGPRs.
-template <bool FIRST, bool NEXT_TILE, bool B_IN_AGPR>
+// B_IN_AGPR: the stage's row fragments live in AGPRs.  DMA: the block also
+// issues this wave's refill loads (gsrc, lds).
+template <bool FIRST, bool NEXT_TILE, bool B_IN_AGPR, bool DMA>
 __device__ __forceinline__ void stage_block(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
                                             uint32_t naddr, const u32x4 &bn, const u32x4 &b0,
-                                            const u32x4 &b1, const u32x4 &b2, const u32x4 &b3) {
+                                            const u32x4 &b1, const u32x4 &b2, const u32x4 &b3,
+                                            const uint4 *gsrc, uint32_t lds) {
   u32x4 t[8];
-#define RVQ_IN(cls) \
-  [addr] "v"(addr), [naddr] "v"(naddr), [b0] cls(b0), [b1] cls(b1), [b2] cls(b2), [b3] cls(b3)
-  if constexpr (FIRST) {
-#define RVQ_OUT0 \
-  [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]), RVQ_PREF, RVQ_TEMPS
-    if constexpr (NEXT_TILE) {
-      if constexpr (B_IN_AGPR)
-        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_TILE) : RVQ_OUT0 : RVQ_IN("a"), [bn] "v"(bn));
-      else
-        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_TILE) : RVQ_OUT0 : RVQ_IN("v"), [bn] "v"(bn));
-    } else {
-      if constexpr (B_IN_AGPR)
-        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_STAGE) : RVQ_OUT0 : RVQ_IN("a"), [bn] "v"(bn));
-      else
-        asm volatile(RVQ_STAGE0_BODY(RVQ_NEXT_STAGE) : RVQ_OUT0 : RVQ_IN("v"), [bn] "v"(bn));
-    }
-#undef RVQ_OUT0
-  } else {
-#define RVQ_OUT \
-  [c0] "+v"(c[0]), [c1] "+v"(c[1]), [c2] "+v"(c[2]), [c3] "+v"(c[3]), RVQ_PREF, RVQ_TEMPS
-    if constexpr (NEXT_TILE) {
-      if constexpr (B_IN_AGPR)
-        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_TILE) : RVQ_OUT : RVQ_IN("a"));
-      else
-        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_TILE) : RVQ_OUT : RVQ_IN("v"));
-    } else {
-      if constexpr (B_IN_AGPR)
-        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_STAGE) : RVQ_OUT : RVQ_IN("a"));
-      else
-        asm volatile(RVQ_STAGE_BODY(RVQ_NEXT_STAGE) : RVQ_OUT : RVQ_IN("v"));
-    }
-#undef RVQ_OUT
+  uint32_t m0_out;
+#define RVQ_IN(cls)                                                                        \
+  [addr] "v"(addr), [naddr] "v"(naddr), [b0] cls(b0), [b1] cls(b1), [b2] cls(b2), [b3] cls(b3), \
+      [gsrc] "v"(gsrc), [lds] "s"(lds)
+#define RVQ_OUTSEL_0 \
+  [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]), RVQ_PREF, RVQ_TEMPS, [m0o] "=&{m0}"(m0_out)
+#define RVQ_OUTSEL_1 \
+  [c0] "+v"(c[0]), [c1] "+v"(c[1]), [c2] "+v"(c[2]), [c3] "+v"(c[3]), RVQ_PREF, RVQ_TEMPS, [m0o] "=&{m0}"(m0_out)
+#define RVQ_EMIT(BODY, OSEL, CLS, ...)                                                     \
+  asm volatile(BODY : RVQ_OUTSEL_##OSEL : RVQ_IN(CLS) __VA_ARGS__ : "memory")
+#define RVQ_NEXT_SEL(B0DY, NX) \
+  B0DY(NX, RVQ_D0, RVQ_D1, RVQ_D2, RVQ_D3)
+#define RVQ_NEXT_NODMA(B0DY, NX) B0DY(NX, "", "", "", "")
+#define RVQ_CASES(B0DY, OSEL, ...)                                                          \
+  if constexpr (NEXT_TILE) {                                                                \
+    if constexpr (DMA) {                                                                    \
+      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_TILE), OSEL, "a", __VA_ARGS__); \
+      else RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_TILE), OSEL, "v", __VA_ARGS__);              \
+    } else {                                                                                \
+      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_TILE), OSEL, "a", __VA_ARGS__); \
+      else RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_TILE), OSEL, "v", __VA_ARGS__);            \
+    }                                                                                       \
+  } else {                                                                                  \
+    if constexpr (DMA) {                                                                    \
+      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_STAGE), OSEL, "a", __VA_ARGS__); \
+      else RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_STAGE), OSEL, "v", __VA_ARGS__);             \
+    } else {                                                                                \
+      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_STAGE), OSEL, "a", __VA_ARGS__); \
+      else RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_STAGE), OSEL, "v", __VA_ARGS__);           \
+    }                                                                                       \
   }
+  if constexpr (FIRST) {
+    RVQ_CASES(RVQ_STAGE0_BODY, 0, , [bn] "v"(bn))
+  } else {
+    RVQ_CASES(RVQ_STAGE_BODY, 1, )
+  }
+#undef RVQ_CASES
+#undef RVQ_NEXT_NODMA
+#undef RVQ_NEXT_SEL
+#undef RVQ_EMIT
+#undef RVQ_OUTSEL_1
+#undef RVQ_OUTSEL_0
 #undef RVQ_IN
+  (void)m0_out;
 }
 
 // The norm fragments of the tile opening a level (slot base + 16*lane).
@@ -201,13 +225,14 @@ struct RowFrags {
     if constexpr (k < NA) return fa[k];
     else return fv[k - NA];
   }
-  template <int s, int S>
+  template <int s, int S, bool DMA>
   __device__ __forceinline__ void stage(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
-                                        uint32_t naddr, const u32x4 &bn) const {
+                                        uint32_t naddr, const u32x4 &bn, const uint4 *gsrc,
+                                        uint32_t lds) const {
     static_assert(NA % 4 == 0, "a stage's k-steps must share a register file");
-    stage_block<s == 0, s == S - 1, (s * 4 < NA)>(c, p, addr, naddr, bn, get<s * 4>(),
-                                                   get<s * 4 + 1>(), get<s * 4 + 2>(),
-                                                   get<s * 4 + 3>());
+    stage_block<s == 0, s == S - 1, (s * 4 < NA), DMA>(c, p, addr, naddr, bn, get<s * 4>(),
+                                                        get<s * 4 + 1>(), get<s * 4 + 2>(),
+                                                        get<s * 4 + 3>(), gsrc, lds);
   }};
 
 // Compile-time loop: f(integral_constant<int, i>) for i in [0, N).
@@ -645,6 +670,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int l_end = FUSED ? a.L : level + 1;
   const int64_t tile_u4 = tile_bytes(S) / 16;
   const uint32_t ring_lds = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4 *)ring);
+  const uint32_t lane_lds = ring_lds + (uint32_t)lane * 16u;
 
   RowFrags<KS> bfr;
   if (l_begin == 0 && a.x16)
@@ -671,14 +697,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     float R1 = __builtin_inff(), R2 = __builtin_inff();
     int B1 = kNoIndex, B2 = kNoIndex;
 
-    int slot_t = 0;  // ring slot of the current tile's stage 0
-    u32x4 pre[4];    // first A-fragments of the next stage, read ahead
+    // byte offsets in the ring of the slots of stages g-1, g and g+1 (the
+    // refill of stage g + kAhead goes to the slot of stage g-1)
+    uint32_t prv = (kSlots - 1) * kSlotBytes, cur = 0, nxt = kSlotBytes;
+    u32x4 pre[4];  // first A-fragments of the next stage, read ahead
+    // this wave's lanes in the stream: stage blocks and norm blocks
+    const uint4 *lsrc = ls + wave * 256 + lane;
+    const uint4 *nsrc = ls + wave * 64 + lane;
     // One tile: FIRST / LAST say whether it is the level's first / last tile
     // (0 no, 1 yes, 2 only known at run time), so the middle tiles carry no
     // run-time tests of the level's boundaries.
     auto tile = [&](int tt, auto FIRST_, auto LAST_) {
       constexpr int FIRST = decltype(FIRST_)::value, LAST = decltype(LAST_)::value;
       f32x16 acc[4];
+      const uint4 *tsrc = lsrc + (int64_t)tt * tile_u4;
       static_for<0, S>([&](auto S_) {
         constexpr int s = decltype(S_)::value;
         const int g = tt * S + s;
@@ -686,9 +718,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // reads ahead into it: wait for this wave's loads of stage g+1 (at
         // most dma_after_next<S>(s) newer loads outstanding), then the
         // barrier, which also means every wave is done with stage g-1, whose
-        // slot the refill below overwrites.  At the start of a level
-        // (update-phase accesses may be interleaved) and near its end, wait
-        // for every load.
+        // slot the refill overwrites.  At the start of a level (update-phase
+        // accesses may be interleaved) and near its end, wait for every load.
         if constexpr (FIRST == 2 || LAST == 2) {
           if (g == 0 || g + kAhead - 1 >= nst) wait_vmcnt<0>();
           else wait_vmcnt<dma_after_next<S>(s)>();
@@ -698,31 +729,36 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
           wait_vmcnt<dma_after_next<S>(s)>();
         }
         barrier_only();
-        int slot = slot_t + s % kSlots;
-        slot = slot >= kSlots ? slot - kSlots : slot;
-        const int nslot = slot + 1 == kSlots ? 0 : slot + 1;
-        const uint32_t addr = ring_lds + (uint32_t)slot * kSlotBytes + (uint32_t)lane * 16u;
-        const uint32_t naddr = ring_lds + (uint32_t)nslot * kSlotBytes + (uint32_t)lane * 16u;
+        const uint32_t addr = lane_lds + cur;
+        const uint32_t naddr = lane_lds + nxt;
         if constexpr (s == 0 && FIRST == 1) read_tile_norms(pre, addr);
         if constexpr (s == 0 && FIRST == 2) {
           if (tt == 0) read_tile_norms(pre, addr);
         }
-        // refill the slot of stage g-1 with stage g + kAhead
-        int rslot = slot + kAhead;
-        rslot = rslot >= kSlots ? rslot - kSlots : rslot;
-        if constexpr (LAST == 2) {
-          if (g + kAhead < nst)
-            issue_stage(ls, tile_u4, tt + (s + kAhead) / S, (s + kAhead) % S, rslot, ring_lds,
-                        wave, lane);
-        } else if constexpr (LAST == 0 || s + kAhead < S) {
-          issue_stage(ls, tile_u4, tt + (s + kAhead) / S, (s + kAhead) % S, rslot, ring_lds,
-                      wave, lane);
-        }
+        // refill: stage g + kAhead is stage sr of tile tt + dt; the block
+        // issues its four stage loads, and its norm block goes first when it
+        // opens a tile
+        constexpr int sr = (s + kAhead) % S, dt = (s + kAhead) / S;
+        const uint4 *gsrc = tsrc + (dt * tile_u4 + 256 + sr * 1024);
+        const uint32_t lds = ring_lds + prv + kNormBytes + (uint32_t)wave * 4096u;
+        auto with_refill = [&]() {
+          if constexpr (sr == 0)
+            dma16(nsrc + (int64_t)(tt + dt) * tile_u4, ring_lds + prv + (uint32_t)wave * kBlockBytes);
+          bfr.template stage<s, S, true>(acc, pre, addr, naddr, bnorm, gsrc, lds);
+        };
         // (the last stage of a level reads ahead into a slot it never uses)
-        bfr.template stage<s, S>(acc, pre, addr, naddr, bnorm);
+        if constexpr (LAST == 2) {
+          if (g + kAhead < nst) with_refill();
+          else bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsrc, lds);
+        } else if constexpr (LAST == 0 || s + kAhead < S) {
+          with_refill();
+        } else {
+          bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsrc, lds);
+        }
+        prv = cur;
+        cur = nxt;
+        nxt = nxt == (kSlots - 1) * kSlotBytes ? 0u : nxt + kSlotBytes;
       });
-      slot_t += S % kSlots;
-      slot_t = slot_t >= kSlots ? slot_t - kSlots : slot_t;
       mfma_drain(acc);
       // Epilogue: accumulator element i of sub-tile j is codeword
       // j*32 + (i/4)*8 + h*4 + i%4 of the tile for this lane's row.  Per
