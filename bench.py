@@ -137,6 +137,77 @@ def cpu_baseline(w, target_s: float = 15.0) -> dict:
                       f"(D={w.D}, K={w.K}, L={w.L}); fp64 encode+decode+counts+msr, {t:.1f} s"}
 
 
+def _time_ms(torch, fn, reps: int) -> float:
+    """Median over reps of fn() timed with events on the current stream."""
+    import numpy as np
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return float(np.median(times))
+
+
+def secondary(torch, rvq, workloads, dev) -> dict:
+    """The other configured workloads, each against its own roofline (not
+    part of the step above): the single 32x32 image (1024 rows, K=4096, the
+    small-batch encoder mode), and the decode-heavy workload (4,194,304 x 8
+    IDs decoded to bf16; counts over them; mean squared residual of a
+    65,536-row fp32 subset encoded at L=8)."""
+    import numpy as np
+    out = {}
+    w = workloads.single_image()
+    x = torch.from_numpy(w.x).to(dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prep = rvq.rvq_prepare_codebooks(cb)
+    wsp = torch.empty(rvq.rvq_encode_workspace_size(w.N, w.D, w.L, w.K), dtype=torch.uint8,
+                      device=dev)
+    ids = rvq.rvq_encode(x, cb, prep, workspace=wsp)
+    torch.cuda.synchronize(dev)
+    ms = _time_ms(torch, lambda: rvq.rvq_encode(x, cb, prep, workspace=wsp, ids_out=ids), 20)
+    fl = 2.0 * w.N * w.K * w.D * w.L
+    out["single_image_encode"] = {
+        "N": w.N, "D": w.D, "K": w.K, "L": w.L, "ms": round(ms, 4),
+        "vectors_per_s": round(w.N / (ms * 1e-3), 1),
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+        "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del x, cb, prep, ids, wsp
+    w = workloads.decode_heavy()
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids = torch.from_numpy(w.ids).to(dev)
+    n, L = w.ids.shape
+    dec = torch.empty((n, w.D), dtype=torch.bfloat16, device=dev)
+    rvq.rvq_decode(ids, cb, torch.bfloat16, out=dec)
+    torch.cuda.synchronize(dev)
+    ms = _time_ms(torch, lambda: rvq.rvq_decode(ids, cb, torch.bfloat16, out=dec), 5)
+    gathered = n * (4 * L + 4 * L * w.D + 2 * w.D)       # IDs + every gathered row + output
+    floor = n * (4 * L + 2 * w.D) + cb.numel() * 4       # IDs + output + codebooks once
+    out["decode_heavy_decode"] = {
+        "N": n, "L": L, "D": w.D, "out": "bf16", "ms": round(ms, 3),
+        "gather_counted_GBps": round(gathered / (ms * 1e-3) / 1e9, 1),
+        "gather_counted_frac_8TBps": round(gathered / (ms * 1e-3) / 8e12, 4),
+        "compulsory_GBps": round(floor / (ms * 1e-3) / 1e9, 1),
+        "compulsory_frac_8TBps": round(floor / (ms * 1e-3) / 8e12, 4)}
+    del dec
+    ws = torch.empty(rvq.rvq_level_stats_workspace_size(n, L, w.K, w.D, False), dtype=torch.uint8,
+                     device=dev)
+    ms = _time_ms(torch, lambda: rvq.rvq_level_stats(ids, w.K, workspace=ws), 5)
+    out["decode_heavy_counts"] = {"N": n, "L": L, "K": w.K, "ms": round(ms, 4),
+                                  "GBps": round(n * L * 4 / (ms * 1e-3) / 1e9, 1)}
+    xs = torch.from_numpy(w.x).to(dev)
+    sids = rvq.rvq_encode(xs, cb)
+    ws2 = torch.empty(rvq.rvq_level_stats_workspace_size(w.N, L, w.K, w.D, True), dtype=torch.uint8,
+                      device=dev)
+    ms = _time_ms(torch, lambda: rvq.rvq_level_stats(sids, w.K, xs, cb, workspace=ws2), 10)
+    gathered = w.N * (4 * w.D + 4 * L + 4 * L * w.D)
+    out["decode_heavy_msr"] = {"N": w.N, "L": L, "D": w.D, "ms": round(ms, 4),
+                               "gather_counted_GBps": round(gathered / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +215,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the single-image encode and decode-heavy measurements")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain copy of this many MiB "
                          "(the calibration dispatch for HBM byte counters)")
@@ -250,6 +323,10 @@ def main() -> int:
         "decode_ms": round(float(np.median(dec_ms)), 4),
         "level_stats_ms": round(float(np.median(st_ms)), 4),
     }
+    if not args.no_secondary:
+        del x, cb, prepared, ws, ws2, ids, out
+        torch.cuda.empty_cache()
+        rec["secondary"] = secondary(torch, rvq, workloads, dev)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

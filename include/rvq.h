@@ -166,9 +166,11 @@ rvq_status rvq_decode(const int32_t *ids, int64_t n, const float *codebooks,
  *   hist[l][k] = number of rows whose level-l ID is k (exact integer count;
  *                out-of-range IDs are not counted and go to *bad_ids).
  *   msr[l]     = mean over rows of ||x_row - sum_{j <= l} codebooks[j][ids[row][j]]||^2,
- *                the mean squared residual left after levels 0..l.  Per-row
- *                residuals are fp32, squared norms and the mean are fp64,
- *                reduced in a fixed order (bitwise reproducible).
+ *                the mean squared residual left after levels 0..l (an
+ *                out-of-range ID subtracts nothing).  Per-row residuals are
+ *                fp32, squared norms and the mean are fp64, reduced in an
+ *                order that depends only on n (bitwise reproducible).
+ * Each out-of-range ID is counted once in *bad_ids per call.
  * ---------------------------------------------------------------------- */
 
 /* Workspace bytes needed by rvq_level_stats (with_msr != 0 when msr is requested). */
