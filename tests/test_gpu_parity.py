@@ -306,3 +306,40 @@ def test_batch_invariance_across_encoder_modes(rvq, dev):
     parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
     parity.check_residual(res[torch.from_numpy(sel).to(dev)].cpu().numpy(), sub.x, "bf16",
                           ids_h[sel], w.codebooks)
+
+
+# Shapes for the all-levels-in-one-launch encoder (n >= 19,712 rows fills the
+# 256 compute units): a padded width whose last k-steps lie past the row and
+# K not a multiple of the 128-codeword tile; a single codeword tile (the
+# level's first tile is also its last); one level of bf16 rows.
+FUSED = [
+    (46, 20000, 700, 3, 1000, "f32"),
+    (47, 20100, 512, 2, 100, "bf16"),
+    (48, 19800, 1152, 1, 300, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: f"s{c[0]}_n{c[1]}_d{c[2]}_L{c[3]}_K{c[4]}_{c[5]}")
+def test_fused_mode_shapes(rvq, dev, case):
+    seed, n, d, L, K, dt = case
+    w = workloads.random_problem(seed, n, d, L, K, x_dtype=dt)
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prep = rvq.rvq_prepare_codebooks(cb)
+    ids, res = rvq.rvq_encode(x, cb, prep, residual=True)
+    ids_only = rvq.rvq_encode(x, cb, prep)
+    # a slice in the small-batch plan gives the same bits
+    a, b = n - 150, n
+    sub_ids, sub_res = rvq.rvq_encode(x[a:b].contiguous(), cb, prep, residual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_only, ids)
+    assert torch.equal(sub_ids, ids[a:b])
+    assert torch.equal(sub_res.view(torch.int32), res[a:b].view(torch.int32))
+    sel = np.unique(np.concatenate([np.arange(0, n, 97), np.arange(n - 40, n)]))
+    sub = w.rows(sel)
+    ids_h = ids.cpu().numpy()
+    ref = oracle.encode(sub.x, sub.codebooks, x_dtype=dt)
+    print(f"[fused {w.name}]", parity.check_strict_prefix(ids_h[sel], ref))
+    parity.check_teacher_forced(sub.x, dt, ids_h[sel], w.codebooks)
+    parity.check_residual(res[torch.from_numpy(sel).to(dev)].cpu().numpy(), sub.x, dt,
+                          ids_h[sel], w.codebooks)
