@@ -97,13 +97,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Refill loads placed inside a block, one after each k-step's MFMAs, so they
 // issue while the matrix core is busy: this wave's four 1 KB blocks of the
-// stage being refilled (global source gsrc, LDS destination lds).  Lane i's
-// 16 bytes land at M0 + offset + 16*i: the instruction offset moves the
-// global and the LDS address alike, so M0 is set once.
-#define RVQ_D0 "s_mov_b32 m0, %[lds]\n\tglobal_load_lds_dwordx4 %[gsrc], off\n\t"
-#define RVQ_D1 "global_load_lds_dwordx4 %[gsrc], off offset:1024\n\t"
-#define RVQ_D2 "global_load_lds_dwordx4 %[gsrc], off offset:2048\n\t"
-#define RVQ_D3 "global_load_lds_dwordx4 %[gsrc], off offset:3072\n\t"
+// stage being refilled (uniform global base gsb in SGPRs plus the lane's
+// 32-bit offset voff; LDS destination lds).  Lane i's 16 bytes land at
+// M0 + offset + 16*i: the instruction offset moves the global and the LDS
+// address alike, so M0 is set once.  The scalar-base form keeps the
+// per-lane address at 32 bits, which costs the issuing wave measurably
+// fewer cycles than a 64-bit per-lane address.
+#define RVQ_D0 "s_mov_b32 m0, %[lds]\n\tglobal_load_lds_dwordx4 %[voff], %[gsb]\n\t"
+#define RVQ_D1 "global_load_lds_dwordx4 %[voff], %[gsb] offset:1024\n\t"
+#define RVQ_D2 "global_load_lds_dwordx4 %[voff], %[gsb] offset:2048\n\t"
+#define RVQ_D3 "global_load_lds_dwordx4 %[voff], %[gsb] offset:3072\n\t"
 
 // A stage inside a tile: p holds its k-step 0 on entry.
 #define RVQ_STAGE_BODY(NEXT, D0, D1, D2, D3)                                                \
@@ -132,17 +135,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // FIRST: the stage opens a tile.  NEXT_TILE: the next stage opens a tile.
 // B_IN_AGPR: the stage's row fragments live in AGPRs.  DMA: the block also
-// issues this wave's refill loads (gsrc, lds).
+// issues this wave's refill loads (gsb + voff, lds).
 template <bool FIRST, bool NEXT_TILE, bool B_IN_AGPR, bool DMA>
 __device__ __forceinline__ void stage_block(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
                                             uint32_t naddr, const u32x4 &bn, const u32x4 &b0,
                                             const u32x4 &b1, const u32x4 &b2, const u32x4 &b3,
-                                            const uint4 *gsrc, uint32_t lds) {
+                                            const uint4 *gsb, uint32_t voff, uint32_t lds) {
   u32x4 t[8];
   uint32_t m0_out;
 #define RVQ_IN(cls)                                                                        \
   [addr] "v"(addr), [naddr] "v"(naddr), [b0] cls(b0), [b1] cls(b1), [b2] cls(b2), [b3] cls(b3), \
-      [gsrc] "v"(gsrc), [lds] "s"(lds)
+      [gsb] "s"(gsb), [voff] "v"(voff), [lds] "s"(lds)
 #define RVQ_OUTSEL_0 \
   [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]), RVQ_PREF, RVQ_TEMPS, [m0o] "=&{m0}"(m0_out)
 #define RVQ_OUTSEL_1 \
@@ -227,12 +230,12 @@ struct RowFrags {
   }
   template <int s, int S, bool DMA>
   __device__ __forceinline__ void stage(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
-                                        uint32_t naddr, const u32x4 &bn, const uint4 *gsrc,
-                                        uint32_t lds) const {
+                                        uint32_t naddr, const u32x4 &bn, const uint4 *gsb,
+                                        uint32_t voff, uint32_t lds) const {
     static_assert(NA % 4 == 0, "a stage's k-steps must share a register file");
     stage_block<s == 0, s == S - 1, (s * 4 < NA), DMA>(c, p, addr, naddr, bn, get<s * 4>(),
                                                         get<s * 4 + 1>(), get<s * 4 + 2>(),
-                                                        get<s * 4 + 3>(), gsrc, lds);
+                                                        get<s * 4 + 3>(), gsb, voff, lds);
   }};
 
 // Compile-time loop: f(integral_constant<int, i>) for i in [0, N).
@@ -603,8 +606,21 @@ constexpr int kSlots = 7;                  // stages resident in LDS
 constexpr int kAhead = kSlots - 1;         // stages loaded ahead of the one in use
 constexpr int kSlotBytes = kNormBytes + kStageBytes;
 
-__device__ __forceinline__ void dma16(const uint4 *src, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr) : "memory");
+// One 1 KB block: lane i's 16 bytes from base + voff (base uniform, in
+// SGPRs) land at lds_addr + 16*i.
+__device__ __forceinline__ void dma16(const uint4 *base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+
+// This wave's four 1 KB blocks of a stage (gsb + voff, landing at lds), as
+// one statement; the instruction offset moves both addresses.
+__device__ __forceinline__ void dma_stage(const uint4 *gsb, uint32_t voff, uint32_t lds) {
+  uint32_t m0_out;
+  asm volatile(RVQ_D0 RVQ_D1 RVQ_D2 RVQ_D3
+               : [m0o] "=&{m0}"(m0_out)
+               : [gsb] "s"(gsb), [voff] "v"(voff), [lds] "s"(lds)
+               : "memory");
+  (void)m0_out;
 }
 
 // Load instructions one wave issues for a stage: 4 x 1 KB blocks, plus its
@@ -631,12 +647,13 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 __device__ __forceinline__ void issue_stage(const uint4 *ls, int64_t tile_u4, int tt, int s,
                                             int slot, uint32_t ring_lds, int wave, int lane) {
   const uint4 *tp = ls + (int64_t)tt * tile_u4;
-  const uint4 *sp = tp + 256 + (int64_t)s * 1024 + wave * 256 + lane;
+  const uint4 *sp = tp + 256 + (int64_t)s * 1024;
   const uint32_t base = ring_lds + (uint32_t)slot * kSlotBytes;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    dma16(sp + q * 64, base + kNormBytes + (uint32_t)(wave * 4 + q) * kBlockBytes);
-  if (s == 0) dma16(tp + wave * 64 + lane, base + (uint32_t)wave * kBlockBytes);
+    dma16(sp, (uint32_t)(wave * 256 + q * 64 + lane) * 16u,
+          base + kNormBytes + (uint32_t)(wave * 4 + q) * kBlockBytes);
+  if (s == 0) dma16(tp, (uint32_t)(wave * 64 + lane) * 16u, base + (uint32_t)wave * kBlockBytes);
 }
 
 }  // namespace
@@ -701,16 +718,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // refill of stage g + kAhead goes to the slot of stage g-1)
     uint32_t prv = (kSlots - 1) * kSlotBytes, cur = 0, nxt = kSlotBytes;
     u32x4 pre[4];  // first A-fragments of the next stage, read ahead
-    // this wave's lanes in the stream: stage blocks and norm blocks
-    const uint4 *lsrc = ls + wave * 256 + lane;
-    const uint4 *nsrc = ls + wave * 64 + lane;
+    // byte offsets of this wave's lanes in a stage and in a norm block
+    const uint32_t soff = (uint32_t)(wave * 256 + lane) * 16u;
+    const uint32_t noff = (uint32_t)(wave * 64 + lane) * 16u;
     // One tile: FIRST / LAST say whether it is the level's first / last tile
     // (0 no, 1 yes, 2 only known at run time), so the middle tiles carry no
     // run-time tests of the level's boundaries.
     auto tile = [&](int tt, auto FIRST_, auto LAST_) {
       constexpr int FIRST = decltype(FIRST_)::value, LAST = decltype(LAST_)::value;
       f32x16 acc[4];
-      const uint4 *tsrc = lsrc + (int64_t)tt * tile_u4;
+      const uint4 *tsb = ls + (int64_t)tt * tile_u4;  // the tile in the stream
       static_for<0, S>([&](auto S_) {
         constexpr int s = decltype(S_)::value;
         const int g = tt * S + s;
@@ -739,21 +756,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // issues its four stage loads, and its norm block goes first when it
         // opens a tile
         constexpr int sr = (s + kAhead) % S, dt = (s + kAhead) / S;
-        const uint4 *gsrc = tsrc + (dt * tile_u4 + 256 + sr * 1024);
-        const uint32_t lds = ring_lds + prv + kNormBytes + (uint32_t)wave * 4096u;
+        const uint4 *gsb = tsb + (dt * tile_u4 + 256 + sr * 1024);
+        // (uniform: read from lane 0 so that it is kept in an SGPR for M0)
+        const uint32_t lds =
+            __builtin_amdgcn_readfirstlane(ring_lds + prv + kNormBytes + (uint32_t)wave * 4096u);
         auto with_refill = [&]() {
           if constexpr (sr == 0)
-            dma16(nsrc + (int64_t)(tt + dt) * tile_u4, ring_lds + prv + (uint32_t)wave * kBlockBytes);
-          bfr.template stage<s, S, true>(acc, pre, addr, naddr, bnorm, gsrc, lds);
+            dma16(tsb + dt * tile_u4, noff, ring_lds + prv + (uint32_t)wave * kBlockBytes);
+          bfr.template stage<s, S, true>(acc, pre, addr, naddr, bnorm, gsb, soff, lds);
         };
         // (the last stage of a level reads ahead into a slot it never uses)
         if constexpr (LAST == 2) {
-          if (g + kAhead < nst) with_refill();
-          else bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsrc, lds);
+          // Whether this stage refills is known only at run time.  The block
+          // itself must be one asm statement on both paths: two variants
+          // would let the compiler give their accumulators different
+          // registers and copy them at the join, reading MFMA results whose
+          // latency it cannot see.  So the refill loads go first, on their
+          // own, and the block is always the one without loads.
+          if (g + kAhead < nst) {
+            if constexpr (sr == 0)
+              dma16(tsb + dt * tile_u4, noff, ring_lds + prv + (uint32_t)wave * kBlockBytes);
+            dma_stage(gsb, soff, lds);
+          }
+          bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsb, soff, lds);
         } else if constexpr (LAST == 0 || s + kAhead < S) {
           with_refill();
         } else {
-          bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsrc, lds);
+          bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsb, soff, lds);
         }
         prv = cur;
         cur = nxt;
@@ -858,7 +887,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // same rescoring and update as the fused kernel.
 template <int S>
 __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int level, int splits) {
-  constexpr int KS = 4 * S;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
