@@ -20,6 +20,27 @@ __global__ __launch_bounds__(256) void stage_input_kernel(const void *__restrict
   }
 }
 
+// residual_out [n][d] from the fused encoder's fragment-major residual: one
+// workgroup per block of 32 rows; the 16-byte run of lane L in k-step ks,
+// half q holds row 32*blk + L%32, features ks*16 + (L/32)*8 + q*4 .. +3.
+__global__ __launch_bounds__(256) void unfragment_kernel(const float *__restrict__ fm, int64_t n,
+                                                         int d, int dp, float *__restrict__ out) {
+  const int64_t blk = blockIdx.x;
+  const int runs = (dp >> 4) * 2 * 64;  // 16-byte runs in a block
+  const float *src = fm + blk * 32 * dp;
+  for (int i = threadIdx.x; i < runs; i += 256) {
+    const int lane = i & 63, q = (i >> 6) & 1, ks = i >> 7;
+    const int64_t row = blk * 32 + (lane & 31);
+    if (row >= n) continue;
+    const float4 v = *reinterpret_cast<const float4 *>(src + (int64_t)i * 4);
+    const int f0 = ks * 16 + (lane >> 5) * 8 + q * 4;
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (f0 + k < d) out[row * d + f0 + k] = e[k];
+  }
+}
+
 // residual_out [n][d] from the padded fp32 residual [n][dp].
 __global__ __launch_bounds__(256) void unpad_kernel(const float *__restrict__ src, int64_t n,
                                                     int d, int dp, float *__restrict__ out) {
@@ -73,7 +94,7 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   EncodeArgs a = a_in;
   const unsigned row_waves = (unsigned)ceil_div(a.n, 4);
   a.x16 = nullptr;
-  if (p.fused && a.x_bf16 && a.dp == a.d && (a.L > 1 || a.residual_out)) {
+  if (p.fused && a.x_bf16 && a.dp == a.d) {
     // level 0 of the fused encoder reads the bf16 rows directly
     a.x16 = (const uint16_t *)a.x;
     a.src0 = nullptr;
@@ -84,17 +105,23 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   } else {
     a.src0 = (const float *)a.x;
   }
-  // the last level reads rbuf[(L-1) & 1] and writes the final residual to
-  // the caller's buffer, or (padded width) to the other buffer first
-  const bool unpad = a.residual_out && a.dp != a.d;
-  float *padded_final = a.rbuf[a.L & 1];
-  a.res_final = unpad ? padded_final : a.residual_out;
+  // The last level reads rbuf[(L-1) & 1] and writes the final residual to
+  // rbuf[L & 1]: fragment-major in fused mode (converted afterwards), rows of
+  // stride dp in split mode (written straight to the caller's buffer when
+  // d == dp).
+  float *final_buf = a.rbuf[a.L & 1];
+  const bool convert = a.residual_out && (p.fused || a.dp != a.d);
+  a.res_final = convert ? final_buf : a.residual_out;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_stages(p, a, events, s);
-  if (e != hipSuccess || !unpad) return e;
-  unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(padded_final, a.n, a.d, a.dp,
-                                                     a.residual_out);
+  if (e != hipSuccess || !convert) return e;
+  if (p.fused)
+    unfragment_kernel<<<dim3((unsigned)ceil_div(a.n, 32)), dim3(256), 0, s>>>(final_buf, a.n, a.d,
+                                                                          a.dp, a.residual_out);
+  else
+    unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(final_buf, a.n, a.d, a.dp,
+                                                       a.residual_out);
   return hipGetLastError();
 }
 

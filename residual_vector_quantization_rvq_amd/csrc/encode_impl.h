@@ -68,6 +68,7 @@ __device__ __forceinline__ int block_index(float key, int b) {
 // value (8 bf16 packed in 4 words).
 constexpr int kFragsInAgpr = 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Stage blocks.  A slot holds a 4 KB norm area and one 16 KB stage; in the
 // stage, k-step ks of sub-tile j is the 1 KB A-fragment at byte
@@ -411,183 +412,6 @@ __device__ __forceinline__ int rescore_update(const float *src, float *dst, bool
   return take2 ? c2 : c1;
 }
 
-// ---- group loads for the fused update ----
-// A group is four k-steps of one lane: 32 bytes (8 fp32) per k-step at a
-// 64-byte stride, or 16 bytes (8 bf16) at a 32-byte stride.  All loads of a
-// group are issued in one block and waited for at its end, so a group costs
-// one memory latency however the compiler would have scheduled them.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-#define RVQ_GL(o, p, off) "global_load_dwordx4 %[" #o "], %[" #p "], off offset:" #off "\n\t"
-#define RVQ_GL8(o, p)                                                                         \
-  RVQ_GL(o##0, p, 0) RVQ_GL(o##1, p, 16) RVQ_GL(o##2, p, 64) RVQ_GL(o##3, p, 80)              \
-      RVQ_GL(o##4, p, 128) RVQ_GL(o##5, p, 144) RVQ_GL(o##6, p, 192) RVQ_GL(o##7, p, 208)
-#define RVQ_GL4H(o, p) RVQ_GL(o##0, p, 0) RVQ_GL(o##1, p, 32) RVQ_GL(o##2, p, 64) RVQ_GL(o##3, p, 96)
-#define RVQ_OUT8(o, v)                                                                        \
-  [o##0] "=&v"(v[0]), [o##1] "=&v"(v[1]), [o##2] "=&v"(v[2]), [o##3] "=&v"(v[3]),             \
-      [o##4] "=&v"(v[4]), [o##5] "=&v"(v[5]), [o##6] "=&v"(v[6]), [o##7] "=&v"(v[7])
-#define RVQ_OUT4(o, v) [o##0] "=&v"(v[0]), [o##1] "=&v"(v[1]), [o##2] "=&v"(v[2]), [o##3] "=&v"(v[3])
-
-// r (row features), a and b (two codewords) of one group.
-__device__ __forceinline__ void group_load3(const float *pr, const float *pa, const float *pb,
-                                            f32x4 (&r)[8], f32x4 (&a)[8], f32x4 (&b)[8]) {
-  asm volatile(RVQ_GL8(r, pr) RVQ_GL8(a, pa) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
-               : RVQ_OUT8(r, r), RVQ_OUT8(a, a), RVQ_OUT8(b, b)
-               : [pr] "v"(pr), [pa] "v"(pa), [pb] "v"(pb)
-               : "memory");
-}
-__device__ __forceinline__ void group_load3(const uint16_t *pr, const float *pa, const float *pb,
-                                            f32x4 (&r)[8], f32x4 (&a)[8], f32x4 (&b)[8]) {
-  u32x4 q[4];
-  asm volatile(RVQ_GL4H(q, pr) RVQ_GL8(a, pa) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
-               : RVQ_OUT4(q, q), RVQ_OUT8(a, a), RVQ_OUT8(b, b)
-               : [pr] "v"(pr), [pa] "v"(pa), [pb] "v"(pb)
-               : "memory");
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[2 * j] = f32x4{__uint_as_float(q[j][0] << 16), __uint_as_float(q[j][0] & 0xffff0000u),
-                     __uint_as_float(q[j][1] << 16), __uint_as_float(q[j][1] & 0xffff0000u)};
-    r[2 * j + 1] = f32x4{__uint_as_float(q[j][2] << 16), __uint_as_float(q[j][2] & 0xffff0000u),
-                         __uint_as_float(q[j][3] << 16), __uint_as_float(q[j][3] & 0xffff0000u)};
-  }
-}
-__device__ __forceinline__ void group_load2(const float *pr, const float *pb, f32x4 (&r)[8],
-                                            f32x4 (&b)[8]) {
-  asm volatile(RVQ_GL8(r, pr) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
-               : RVQ_OUT8(r, r), RVQ_OUT8(b, b)
-               : [pr] "v"(pr), [pb] "v"(pb)
-               : "memory");
-}
-__device__ __forceinline__ void group_load2(const uint16_t *pr, const float *pb, f32x4 (&r)[8],
-                                            f32x4 (&b)[8]) {
-  u32x4 q[4];
-  asm volatile(RVQ_GL4H(q, pr) RVQ_GL8(b, pb) "s_waitcnt vmcnt(0)"
-               : RVQ_OUT4(q, q), RVQ_OUT8(b, b)
-               : [pr] "v"(pr), [pb] "v"(pb)
-               : "memory");
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[2 * j] = f32x4{__uint_as_float(q[j][0] << 16), __uint_as_float(q[j][0] & 0xffff0000u),
-                     __uint_as_float(q[j][1] << 16), __uint_as_float(q[j][1] & 0xffff0000u)};
-    r[2 * j + 1] = f32x4{__uint_as_float(q[j][2] << 16), __uint_as_float(q[j][2] & 0xffff0000u),
-                         __uint_as_float(q[j][3] << 16), __uint_as_float(q[j][3] & 0xffff0000u)};
-  }
-}
-
-__device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
-  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-
-// The same rescoring and update for the fused encoder, which also rebuilds
-// the row's B-fragments for the next level in the same pass: a lane's
-// update covers exactly the features its fragments hold (ks*16 + h*8 + e),
-// so the new residual never has to be read back.  Work goes in groups of
-// four k-steps (fragments live in fixed registers, so every group is
-// unrolled); a group wholly inside the row uses one block of loads, and
-// only a group that crosses the row's end (padded widths) goes k-step by
-// k-step (k-steps past dp are zero and touch no memory).  With STORE the new
-// residual goes to dst for every lane: lanes past row n-1 work on row n-1
-// and store exactly what its own lane stores, so no lane-dependent branch
-// splits the loads.
-template <int KS, bool STORE, typename SrcT>
-__device__ __forceinline__ int rescore_update_frags(RowFrags<KS> &bfr, const SrcT *src,
-                                                    float *dst, int64_t row, int dp,
-                                                    const float *cb_l, int c1, int c2, bool v2,
-                                                    int h) {
-  static_assert(KS % 4 == 0, "k-steps come in stages of four");
-  float p1 = 0.f, p2 = 0.f;
-  const int64_t lane_off = row * dp + h * 8;
-  const int64_t off1 = (int64_t)c1 * dp + h * 8, off2 = (int64_t)c2 * dp + h * 8;
-  auto kstep = [&](auto K_) {  // one k-step, for groups crossing the row's end
-    constexpr int ks = decltype(K_)::value;
-    const int i0 = ks * 16 + h * 8;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (ks * 16 < dp) {
-      float r[8], a[8], b[8];
-      read_src(src, row, dp, i0, r);
-      read8(cb_l, c1, dp, i0, true, a);
-      read8(cb_l, c2, dp, i0, true, b);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = r[e] - a[e];
-        const float u = r[e] - b[e];
-        p1 = fmaf(t, t, p1);
-        p2 = fmaf(u, u, p2);
-        v[e] = t;
-      }
-      if constexpr (STORE) write8(dst, row, dp, i0, v);
-    }
-    bfr.template set<ks>(to_bf16x8(v));
-  };
-  static_for<0, KS / 4>([&](auto G_) {
-    constexpr int g = decltype(G_)::value;
-    if (g * 64 + 64 <= dp) {
-      f32x4 r[8], a[8], b[8];
-      group_load3(src + lane_off + g * 64, cb_l + off1 + g * 64, cb_l + off2 + g * 64, r, a, b);
-      static_for<0, 4>([&](auto J_) {
-        constexpr int j = decltype(J_)::value;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float re = r[2 * j + e / 4][e % 4];
-          const float t = re - a[2 * j + e / 4][e % 4];
-          const float u = re - b[2 * j + e / 4][e % 4];
-          p1 = fmaf(t, t, p1);
-          p2 = fmaf(u, u, p2);
-          v[e] = t;
-        }
-        if constexpr (STORE) store8(dst + lane_off + g * 64 + j * 16, v);
-        bfr.template set<g * 4 + j>(to_bf16x8(v));
-      });
-    } else {
-      static_for<g * 4, g * 4 + 4>(kstep);
-    }
-  });
-  const float q1 = __shfl_xor(p1, 32, 64);
-  const float q2 = __shfl_xor(p2, 32, 64);
-  const float d1 = h ? q1 + p1 : p1 + q1;
-  const float d2 = h ? q2 + p2 : p2 + q2;
-  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
-  // Rows where the second candidate won are redone.  Every lane of the wave
-  // takes part (no divergent branch, so fragments are rewritten in place):
-  // a lane whose first candidate won recomputes exactly r - c1 again.
-  if (__ballot(take2)) {
-    const int cs = take2 ? c2 : c1;
-    const int64_t offs = (int64_t)cs * dp + h * 8;
-    auto redo_kstep = [&](auto K_) {
-      constexpr int ks = decltype(K_)::value;
-      const int i0 = ks * 16 + h * 8;
-      if (ks * 16 < dp) {
-        float r[8], b[8], v[8];
-        read_src(src, row, dp, i0, r);
-        read8(cb_l, cs, dp, i0, true, b);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = r[e] - b[e];
-        if constexpr (STORE) write8(dst, row, dp, i0, v);
-        bfr.template set<ks>(to_bf16x8(v));
-      }
-    };
-    static_for<0, KS / 4>([&](auto G_) {
-      constexpr int g = decltype(G_)::value;
-      if (g * 64 + 64 <= dp) {
-        f32x4 r[8], b[8];
-        group_load2(src + lane_off + g * 64, cb_l + offs + g * 64, r, b);
-        static_for<0, 4>([&](auto J_) {
-          constexpr int j = decltype(J_)::value;
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = r[2 * j + e / 4][e % 4] - b[2 * j + e / 4][e % 4];
-          if constexpr (STORE) store8(dst + lane_off + g * 64 + j * 16, v);
-          bfr.template set<g * 4 + j>(to_bf16x8(v));
-        });
-      } else {
-        static_for<g * 4, g * 4 + 4>(redo_kstep);
-      }
-    });
-  }
-  return take2 ? c2 : c1;
-}
-
 // First two candidates of a row's top-2 list as valid codeword indices.
 __device__ __forceinline__ void candidates(int i1, int i2, int K, int &c1, int &c2, bool &v2) {
   c1 = (i1 >= 0 && i1 < K) ? i1 : 0;  // finite inputs always give a valid first candidate
@@ -654,6 +478,340 @@ __device__ __forceinline__ void issue_stage(const uint4 *ls, int64_t tile_u4, in
     dma16(sp, (uint32_t)(wave * 256 + q * 64 + lane) * 16u,
           base + kNormBytes + (uint32_t)(wave * 4 + q) * kBlockBytes);
   if (s == 0) dma16(tp, (uint32_t)(wave * 64 + lane) * 16u, base + (uint32_t)wave * kBlockBytes);
+}
+
+// ---- fused update through LDS ----
+// After a level's sweep each lane-row needs three rows: its residual and its
+// two candidate codewords.  Loaded straight into fragment layout, every load
+// instruction touches 32 rows at 32 bytes each, which the memory pipeline
+// serves slowly per cache line.  Instead each row is copied global->LDS in a
+// coalesced pattern (8 lanes per 128-byte row piece, 8 rows per instruction;
+// the residual, kept in fragment-major order between levels, as 1 KB runs)
+// and read back in fragment layout with ds_read_b128.  Work goes in half
+// groups of two k-steps, double-buffered in this wave's own 4 KB stage areas
+// of ring slots 0..5: the ring is idle between a level's sweep and the next
+// level's first loads, which the wave issues only after its update, and no
+// other wave touches these areas in the meantime.
+//
+// Fragment-major residual (the fused encoder's internal buffers): for each
+// block of 32 rows and each k-step ks < dp/16, two 1 KB runs (q = 0, 1);
+// lane L's 16 bytes hold row 32*blk + L%32, features ks*16 + (L/32)*8 +
+// q*4 .. +3.  One block is 32*dp floats; buffers cover n rounded up to 128.
+
+enum class RSrc { kFragMajor, kRowF32, kRowBF16 };
+
+// LDS byte offset, within a 4 KB area, of 16-byte chunk m (0..7) of row rho
+// (0..31) of a 128-byte fp32 row piece: 8 rows per 1 KB, chunks swizzled so
+// that any 16 consecutive lanes reading one chunk index of 16 rows (and any
+// 8 consecutive lanes) hit distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t swz_f32(int rho, int m) {
+  const int f = (rho & 7) ^ ((rho >> 3) & 1);
+  return (uint32_t)((rho >> 3) * 1024 + (rho & 7) * 128 + ((m ^ f) << 4));
+}
+// The same for a 64-byte bf16 row piece (4 chunks): 16 rows per 1 KB.
+__device__ __forceinline__ uint32_t swz_bf16(int rho, int m) {
+  const int f = ((rho >> 1) ^ (rho >> 3)) & 3;
+  return (uint32_t)((rho >> 4) * 1024 + (rho & 15) * 64 + ((m ^ f) << 4));
+}
+
+// This wave's 4 KB area in ring slot k (0..5).
+__device__ __forceinline__ uint32_t upd_area(uint32_t ring_lds, int wave, int k) {
+  return ring_lds + (uint32_t)k * kSlotBytes + kNormBytes + (uint32_t)wave * 4096u;
+}
+
+#define RVQ_DL(o, b) "global_load_lds_dwordx4 %[" #o "], %[" #b "]\n\t"
+#define RVQ_M0(a, off) "s_add_u32 m0, %[" #a "], " #off "\n\t"
+
+// Four 1 KB copies into the area at lds: lane offsets o0..o3 from base b
+// (one instruction each, the i-th landing at lds + 1 KB * i).
+__device__ __forceinline__ void dma_rows4(const void *b, uint32_t lds, uint32_t o0, uint32_t o1,
+                                          uint32_t o2, uint32_t o3) {
+  uint32_t m0_out;
+  asm volatile("s_mov_b32 m0, %[a]\n\t" RVQ_DL(o0, b) RVQ_M0(a, 0x400) RVQ_DL(o1, b)
+                   RVQ_M0(a, 0x800) RVQ_DL(o2, b) RVQ_M0(a, 0xc00) RVQ_DL(o3, b)
+               : [m0o] "=&{m0}"(m0_out)
+               : [a] "s"(lds), [b] "s"(b), [o0] "v"(o0), [o1] "v"(o1), [o2] "v"(o2), [o3] "v"(o3)
+               : "memory", "scc");
+  (void)m0_out;
+}
+// Two 1 KB copies (lanes offsets o0, o1).
+__device__ __forceinline__ void dma_rows2(const void *b, uint32_t lds, uint32_t o0, uint32_t o1) {
+  uint32_t m0_out;
+  asm volatile("s_mov_b32 m0, %[a]\n\t" RVQ_DL(o0, b) RVQ_M0(a, 0x400) RVQ_DL(o1, b)
+               : [m0o] "=&{m0}"(m0_out)
+               : [a] "s"(lds), [b] "s"(b), [o0] "v"(o0), [o1] "v"(o1)
+               : "memory", "scc");
+  (void)m0_out;
+}
+#undef RVQ_M0
+#undef RVQ_DL
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_upd() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Lane offsets of this wave's row copies for one level.  Copy instruction i
+// (0..3) of an fp32 row piece serves rows 8i .. 8i+7: lane l fetches chunk
+// m = (l%8) ^ f(row) of row 8i + l/8.  crow(i) gives that row's index into
+// the source (a codeword or an input row), stride the row stride in bytes.
+struct RowCopy {
+  uint32_t off[4];  // byte offset of the lane's chunk from the copy base, per instruction
+  uint32_t hi;      // 64 when the lane's chunk lies in the second k-step (for odd tails,
+                    // which fetch the chunk 64 bytes lower instead and never read it)
+};
+
+__device__ __forceinline__ RowCopy row_copy_f32(int lane, int64_t stride_bytes,
+                                                const int (&rows)[4]) {
+  RowCopy c;
+  const int p = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rho = 8 * i + (lane >> 3);
+    const int f = (rho & 7) ^ ((rho >> 3) & 1);
+    const int m = p ^ f;
+    c.off[i] = (uint32_t)((int64_t)rows[i] * stride_bytes + m * 16);
+  }
+  // f(8i + l/8) = (l/8) ^ (i & 1) changes only bit 0 of m across i, so
+  // whether m >= 4 is the same for every instruction
+  c.hi = ((p ^ (lane >> 3)) >= 4) ? 64u : 0u;
+  return c;
+}
+
+// Row indices (relative to the copy base) that copy instruction i of an fp32
+// piece serves, from per-lane values held by lanes 0..31 (one per row).
+__device__ __forceinline__ void rows_f32(int v, int (&rows)[4], int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rows[i] = __shfl(v, 8 * i + (lane >> 3), 64);
+}
+
+// Exact fp32 rescoring of the two candidates and residual update for the
+// fused encoder, through LDS.  Lanes L and L+32 hold one row (h = 0, 1) and
+// each takes features ks*16 + h*8 + e in order ks, e, accumulating (r - c)^2
+// with fmaf; the row's distance is (half 0) + (half 1).  r - c1 is written as
+// it goes (fragment-major, when STORE) and becomes the next level's
+// B-fragments; rows where c2 wins are redone with every lane taking part.
+// Returns the chosen index.  rsrc: the level's residual (fragment-major
+// buffer, or for level 0 the fp32 / bf16 input rows of stride dp, based at
+// row wbase of this wave, rrow = this lane's row relative to wbase).
+template <int KS, RSrc SRC, bool STORE>
+__device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc, int rrow,
+                                             float *dst_blk, int dp, const float *cb_l, int c1,
+                                             int c2, bool v2, int lane_in, uint32_t ring_lds,
+                                             int wave) {
+  // Everything below derives from this opaque copy of the lane index, so the
+  // compiler cannot hoist lane-dependent addresses out of the level loop and
+  // keep them live through the sweep.
+  int lane = lane_in;
+  opaque1(lane);
+  const int h = lane >> 5;
+  const int rho = lane & 31;
+  const int nks = dp >> 4;                // k-steps inside the row
+  const int nhg = (nks + 1) >> 1;         // half groups
+  const bool odd = nks & 1;               // the last half group has one k-step
+  constexpr int kStores = STORE ? 4 : 0;  // stores a full half group issues
+
+  // residual copies (the same in the first pass and the redo)
+  RowCopy rc{};
+  uint32_t rc2[2] = {0u, 0u}, rhi2[2] = {0u, 0u};
+  if constexpr (SRC == RSrc::kRowF32) {
+    int rows[4];
+    rows_f32(rrow, rows, lane);
+    rc = row_copy_f32(lane, (int64_t)dp * 4, rows);
+  } else if constexpr (SRC == RSrc::kRowBF16) {
+    // copy instruction i (0, 1) serves rows 16i .. 16i+15: lane l fetches
+    // chunk (l%4) ^ f(row) of row 16i + l/4
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + (lane >> 2);
+      const int rr = __shfl(rrow, r, 64);
+      const int f = ((r >> 1) ^ (r >> 3)) & 3;
+      const int m = (lane & 3) ^ f;
+      rc2[i] = (uint32_t)((int64_t)rr * dp * 2 + m * 16);
+      rhi2[i] = m >= 2 ? 32u : 0u;  // chunk in the second k-step (odd tails)
+    }
+  }
+  const uint32_t fm_off = (uint32_t)lane * 16u;
+
+  // Issues the copies of half group hg into buffer b: the residual, then
+  // codewords ca (and cb when TWO).
+  // Issues the copies of the next half group (hg, in increasing order within
+  // a pass) into buffer b: the residual, then codewords ca (and cb when
+  // TWO).  The source bases advance by one half group per call through an
+  // opaque scalar, so the compiler cannot precompute (and hold) all of them.
+  const char *rnext = static_cast<const char *>(rsrc);
+  const char *cnext = reinterpret_cast<const char *>(cb_l);
+  auto restart = [&]() {
+    rnext = static_cast<const char *>(rsrc);
+    cnext = reinterpret_cast<const char *>(cb_l);
+  };
+  auto issue = [&](int hg, int b, const RowCopy &ca, const RowCopy &cbw, auto TWO_) {
+    constexpr bool TWO = decltype(TWO_)::value;
+    const bool part = odd && hg == nhg - 1;
+    const uint32_t ar = upd_area(ring_lds, wave, 3 * b);
+    if constexpr (SRC == RSrc::kFragMajor) {
+      if (part) dma_rows2(rnext, ar, fm_off, fm_off + 1024u);
+      else dma_rows4(rnext, ar, fm_off, fm_off + 1024u, fm_off + 2048u, fm_off + 3072u);
+      rnext += 4096;  // two k-steps of 2 KB
+    } else if constexpr (SRC == RSrc::kRowF32) {
+      const uint32_t d = part ? rc.hi : 0u;
+      dma_rows4(rnext, ar, rc.off[0] - d, rc.off[1] - d, rc.off[2] - d, rc.off[3] - d);
+      rnext += 128;  // 32 fp32 features
+    } else {
+      dma_rows2(rnext, ar, rc2[0] - (part ? rhi2[0] : 0u), rc2[1] - (part ? rhi2[1] : 0u));
+      rnext += 64;  // 32 bf16 features
+    }
+    {
+      const uint32_t d = part ? ca.hi : 0u;
+      dma_rows4(cnext, upd_area(ring_lds, wave, 3 * b + 1), ca.off[0] - d, ca.off[1] - d,
+                ca.off[2] - d, ca.off[3] - d);
+    }
+    if constexpr (TWO) {
+      const uint32_t d = part ? cbw.hi : 0u;
+      dma_rows4(cnext, upd_area(ring_lds, wave, 3 * b + 2), cbw.off[0] - d, cbw.off[1] - d,
+                cbw.off[2] - d, cbw.off[3] - d);
+    }
+    cnext += 128;
+    asm volatile("" : "+s"(rnext), "+s"(cnext));
+  };
+
+  // Eight residual features of k-step j (0, 1) of the half group in buffer b.
+  auto lds16 = [](uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) f32x4 *>((size_t)addr);
+  };
+  auto read_r = [&](int b, int j, float (&r)[8]) {
+    const uint32_t ar = upd_area(ring_lds, wave, 3 * b);
+    if constexpr (SRC == RSrc::kRowBF16) {
+      const f32x4 q = lds16(ar + swz_bf16(rho, 2 * j + h));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = __float_as_uint(q[e]);
+        r[2 * e] = __uint_as_float(w << 16);
+        r[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t a = SRC == RSrc::kFragMajor
+                               ? ar + (uint32_t)(2 * j + q) * 1024u + fm_off
+                               : ar + swz_f32(rho, 4 * j + 2 * h + q);
+        const f32x4 v = lds16(a);
+        r[4 * q] = v[0]; r[4 * q + 1] = v[1]; r[4 * q + 2] = v[2]; r[4 * q + 3] = v[3];
+      }
+    }
+  };
+  auto read_c = [&](uint32_t area, int j, float (&c)[8]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const f32x4 v = lds16(area + swz_f32(rho, 4 * j + 2 * h + q));
+      c[4 * q] = v[0]; c[4 * q + 1] = v[1]; c[4 * q + 2] = v[2]; c[4 * q + 3] = v[3];
+    }
+  };
+  // r - c of k-step ks into the fragment-major buffer: a uniform base per
+  // k-step plus the lane's 32-bit offset (scalar-base stores, so no 64-bit
+  // address per k-step is held in VGPRs).
+  // (st_off is re-made opaque at the start of each pass, so the redo does not
+  // share address values with the first pass and keep them alive between.)
+  uint32_t st_off = fm_off;
+  auto store = [&](int ks, const float (&v)[8]) {
+    char *sb = reinterpret_cast<char *>(dst_blk) + (int64_t)ks * 2048;
+    *reinterpret_cast<f32x4 *>(sb + st_off) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(sb + 1024 + st_off) = f32x4{v[4], v[5], v[6], v[7]};
+  };
+
+  // Half groups whose k-steps all lie inside every row this stage count
+  // serves need no run-time test; k-steps past the row are never touched
+  // (their fragments were built as zeros and stay zero).
+  constexpr int kSure = 4 * prev_stage_count(KS / 4);  // k-steps inside every row
+  auto sure = [](int hg) { return 2 * hg + 1 < kSure; };
+
+  // First pass: both distances, r - c1 stored and made the next fragments.
+  int rows[4];
+  rows_f32(c1, rows, lane);
+  const RowCopy k1 = row_copy_f32(lane, (int64_t)dp * 4, rows);
+  rows_f32(c2, rows, lane);
+  const RowCopy k2 = row_copy_f32(lane, (int64_t)dp * 4, rows);
+  float p1 = 0.f, p2 = 0.f;
+  opaque1(st_off);
+  auto first = [&](auto HG_) {
+    constexpr int hg = decltype(HG_)::value;
+    constexpr int b = hg & 1;
+    // this half group's copies have landed (only the previous half group's
+    // stores may be newer)
+    if constexpr (hg == 0) wait_vmcnt_upd<0>();
+    else wait_vmcnt_upd<kStores>();
+    if (sure(hg + 1) || hg + 1 < nhg) issue(hg + 1, b ^ 1, k1, k2, std::true_type{});
+    static_for<0, 2>([&](auto J_) {
+      constexpr int j = decltype(J_)::value;
+      constexpr int ks = 2 * hg + j;
+      if (ks < kSure || ks < nks) {
+        float r[8], a[8], c[8], v[8];
+        read_r(b, j, r);
+        read_c(upd_area(ring_lds, wave, 3 * b + 1), j, a);
+        read_c(upd_area(ring_lds, wave, 3 * b + 2), j, c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = r[e] - a[e];
+          const float u = r[e] - c[e];
+          p1 = fmaf(t, t, p1);
+          p2 = fmaf(u, u, p2);
+          v[e] = t;
+        }
+        if constexpr (STORE) store(ks, v);
+        bfr.template set<ks>(to_bf16x8(v));
+        // the distance sums are finished here, in order, so the compiler
+        // cannot defer them and keep every difference alive
+        opaque(p1, p2);
+      }
+    });
+  };
+  issue(0, 0, k1, k2, std::true_type{});
+  static_for<0, KS / 2>([&](auto G_) {
+    constexpr int hg = decltype(G_)::value;
+    if (sure(hg) || hg < nhg) first(G_);
+  });
+  const float q1 = __shfl_xor(p1, 32, 64);
+  const float q2 = __shfl_xor(p2, 32, 64);
+  const float d1 = h ? q1 + p1 : p1 + q1;
+  const float d2 = h ? q2 + p2 : p2 + q2;
+  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
+  // Rows where the second candidate won are redone.  Every lane of the wave
+  // takes part (no divergent branch, so fragments are rewritten in place):
+  // a lane whose first candidate won recomputes exactly r - c1 again.
+  if (__ballot(take2)) {
+    const int cs = take2 ? c2 : c1;
+    rows_f32(cs, rows, lane);
+    const RowCopy kc = row_copy_f32(lane, (int64_t)dp * 4, rows);
+    auto redo = [&](auto HG_) {
+      constexpr int hg = decltype(HG_)::value;
+      constexpr int b = hg & 1;
+      if constexpr (hg == 0) wait_vmcnt_upd<0>();
+      else wait_vmcnt_upd<kStores>();
+      if (sure(hg + 1) || hg + 1 < nhg) issue(hg + 1, b ^ 1, kc, kc, std::false_type{});
+      static_for<0, 2>([&](auto J_) {
+        constexpr int j = decltype(J_)::value;
+        constexpr int ks = 2 * hg + j;
+        if (ks < kSure || ks < nks) {
+          float r[8], c[8], v[8];
+          read_r(b, j, r);
+          read_c(upd_area(ring_lds, wave, 3 * b + 1), j, c);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = r[e] - c[e];
+          if constexpr (STORE) store(ks, v);
+          bfr.template set<ks>(to_bf16x8(v));
+        }
+      });
+    };
+    restart();
+    st_off = fm_off;
+    opaque1(st_off);
+    issue(0, 0, kc, kc, std::false_type{});
+    static_for<0, KS / 2>([&](auto G_) {
+      constexpr int hg = decltype(G_)::value;
+      if (sure(hg) || hg < nhg) redo(G_);
+    });
+  }
+  return take2 ? c2 : c1;
 }
 
 }  // namespace
@@ -847,34 +1005,49 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       merge_top2(S1, I1, S2, I2, t1, j1, t2, j2);
     }
 
-    if (FUSED && l + 1 < l_end) {
-      // every wave is done with the ring; start streaming the next level
-      // while this level's rescoring and update run
-      barrier_only();
-      const uint4 *ln = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)(l + 1) * T + t0) * tile_u4;
-      static_for<0, kAhead>([&](auto K_) {
-        constexpr int k = decltype(K_)::value;
-        if (k < nst) issue_stage(ln, tile_u4, k / S, k % S, k, ring_lds, wave, lane);
-      });
-    }
     if (FUSED) {
+      // every wave is done with the ring: the update may use this wave's
+      // areas of it
+      barrier_only();
       int c1, c2;
       bool v2;
       candidates(I1, I2, a.K, c1, c2, v2);
-      const bool last = l == a.L - 1;
-      float *dst = last ? a.res_final : a.rbuf[(l + 1) & 1];
+      const bool store = l + 1 < a.L || a.res_final != nullptr;
+      // this wave's block of 32 rows in the fragment-major buffers
+      const int64_t blk_off = ((int64_t)rb * 4 + wave) * 32 * a.dp;
+      float *dst = a.rbuf[(l + 1) & 1] + blk_off;
       const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
-      // (a.x16 is set only when level 0 stores a residual)
       int id;
-      if (l == 0 && a.x16)
-        id = rescore_update_frags<KS, true>(bfr, a.x16, dst, rowc, a.dp, cb_l, c1, c2, v2, h);
-      else if (dst)
-        id = rescore_update_frags<KS, true>(bfr, l == 0 ? a.src0 : a.rbuf[l & 1], dst, rowc,
-                                            a.dp, cb_l, c1, c2, v2, h);
-      else
-        id = rescore_update_frags<KS, false>(bfr, l == 0 ? a.src0 : a.rbuf[l & 1], dst, rowc,
-                                             a.dp, cb_l, c1, c2, v2, h);
+      if (l == 0) {
+        // input rows, based at this wave's first row (clamped into the batch)
+        const int64_t w0 = (int64_t)rb * kRowsPerWG + wave * 32;
+        const int64_t wbase = w0 < a.n ? w0 : a.n - 1;
+        const int rrow = (int)(rowc - wbase);
+        if (a.x16)
+          id = update_staged<KS, RSrc::kRowBF16, true>(bfr, a.x16 + wbase * a.dp, rrow, dst, a.dp,
+                                                       cb_l, c1, c2, v2, lane, ring_lds, wave);
+        else
+          id = update_staged<KS, RSrc::kRowF32, true>(bfr, a.src0 + wbase * a.dp, rrow, dst, a.dp,
+                                                      cb_l, c1, c2, v2, lane, ring_lds, wave);
+      } else if (store) {
+        id = update_staged<KS, RSrc::kFragMajor, true>(bfr, a.rbuf[l & 1] + blk_off, 0, dst, a.dp,
+                                                       cb_l, c1, c2, v2, lane, ring_lds, wave);
+      } else {
+        id = update_staged<KS, RSrc::kFragMajor, false>(bfr, a.rbuf[l & 1] + blk_off, 0, dst,
+                                                         a.dp, cb_l, c1, c2, v2, lane, ring_lds,
+                                                         wave);
+      }
       if (live && h == 0) a.ids[row * a.L + l] = id;
+      if (l + 1 < l_end) {
+        // the next level's first stages, into this wave's areas of the ring
+        // (its own update is done with them; other waves touch only theirs)
+        const uint4 *ln =
+            reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)(l + 1) * T + t0) * tile_u4;
+        static_for<0, kAhead>([&](auto K_) {
+          constexpr int k = decltype(K_)::value;
+          if (k < nst) issue_stage(ln, tile_u4, k / S, k % S, k, ring_lds, wave, lane);
+        });
+      }
     } else {
       if (live && h == 0)
         a.part[row * splits + sp] = make_float4(S1, __int_as_float(I1), S2, __int_as_float(I2));

@@ -97,7 +97,10 @@ struct EncodeLayout {
 EncodeLayout encode_layout(int64_t n, int32_t d, int32_t K) {
   EncodeLayout w;
   const size_t tiles = (size_t)(padded_k(K) / kTileCw);
-  const size_t rbytes = align256((size_t)n * row_stride(d) * sizeof(float));
+  // rows rounded up to whole workgroups: the fused encoder keeps residuals
+  // in fragment-major blocks of 32 rows, one set of 4 per workgroup
+  const size_t rbytes =
+      align256((size_t)round_up(n, kRowsPerWG) * row_stride(d) * sizeof(float));
   w.r0_off = 0;
   w.r1_off = rbytes;
   w.part_off = 2 * rbytes;
@@ -114,7 +117,7 @@ int num_cus() {
   return cus > 0 ? cus : 256;
 }
 
-rvq_status check_encode_width(int32_t d);
+rvq_status check_encode_width(int32_t d, int32_t K);
 
 }  // namespace
 
@@ -134,17 +137,21 @@ const char *rvq_status_string(rvq_status s) {
 const char *rvq_last_error(void) { return g_err; }
 
 namespace {
-rvq_status check_encode_width(int32_t d) {
+rvq_status check_encode_width(int32_t d, int32_t K) {
   if (stages_for(d) == 0)
     return fail(RVQ_ERR_UNSUPPORTED, "encode supports d <= %d (got %d)", kMaxStages * kStageCols,
                 d);
+  // the fused update addresses a level's codewords with 32-bit lane offsets
+  if ((int64_t)K * row_stride(d) * (int64_t)sizeof(float) > (int64_t)UINT32_MAX)
+    return fail(RVQ_ERR_UNSUPPORTED, "encode supports K * d below 2^30 per level (got K=%d, d=%d)",
+                K, d);
   return RVQ_OK;
 }
 }  // namespace
 
 rvq_status rvq_prepared_size(int32_t L, int32_t K, int32_t d, size_t *bytes) {
   RVQ_TRY(check_shape(0, d, L, K));
-  RVQ_TRY(check_encode_width(d));
+  RVQ_TRY(check_encode_width(d, K));
   if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
   *bytes = prepared_layout(L, K, d).total;
   return RVQ_OK;
@@ -153,7 +160,7 @@ rvq_status rvq_prepared_size(int32_t L, int32_t K, int32_t d, size_t *bytes) {
 rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, int32_t d,
                                  void *prepared, size_t prepared_bytes, hipStream_t stream) {
   RVQ_TRY(check_shape(0, d, L, K));
-  RVQ_TRY(check_encode_width(d));
+  RVQ_TRY(check_encode_width(d, K));
   RVQ_TRY(need(codebooks, "codebooks", 16));
   RVQ_TRY(need(prepared, "prepared", 256));
   const PreparedLayout pl = prepared_layout(L, K, d);
@@ -171,7 +178,7 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
 
 rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K, size_t *bytes) {
   RVQ_TRY(check_shape(n, d, L, K));
-  RVQ_TRY(check_encode_width(d));
+  RVQ_TRY(check_encode_width(d, K));
   if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
   *bytes = encode_layout(n, d, K).total;
   return RVQ_OK;
@@ -183,7 +190,7 @@ rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int3
                                size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
                                int32_t *launches) {
   RVQ_TRY(check_shape(n, d, L, K));
-  RVQ_TRY(check_encode_width(d));
+  RVQ_TRY(check_encode_width(d, K));
   if (x_dtype != RVQ_F32 && x_dtype != RVQ_BF16)
     return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown x_dtype %d", (int)x_dtype);
   RVQ_TRY(need(codebooks, "codebooks", 16));

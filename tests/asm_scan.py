@@ -14,16 +14,18 @@ from __future__ import annotations
 
 import re
 
-_VREG = re.compile(r"[va]\[(\d+):(\d+)\]$")
-_VONE = re.compile(r"[va](\d+)$")
+_VREG = re.compile(r"([va])\[(\d+):(\d+)\]$")
+_VONE = re.compile(r"([va])(\d+)$")
 
 
-def _regs(tok: str) -> set[int]:
+def _regs(tok: str) -> set[tuple[str, int]]:
+    """Vector registers named by an operand, as (file, index): v and a
+    (arch VGPRs and AGPRs) are separate files."""
     m = _VREG.match(tok)
     if m:
-        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
     m = _VONE.match(tok)
-    return {int(m.group(1))} if m else set()
+    return {(m.group(1), int(m.group(2)))} if m else set()
 
 
 def kernel_bodies(asm: str, prefix: str) -> dict[str, list[str]]:

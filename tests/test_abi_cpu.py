@@ -54,13 +54,21 @@ def test_prepared_size_layout(rvq):
 
 
 def test_encode_workspace_size(rvq):
-    # two fp32 residuals [n][d rounded up to 16] and one top-2 list per row and
-    # 128-codeword tile
+    # two fp32 residuals [n rounded up to 128][d rounded up to 16] and one
+    # top-2 list per row and 128-codeword tile
     al = lambda v: (v + 255) // 256 * 256
     n, d, L, K = 1000, 64, 4, 256
-    assert rvq.rvq_encode_workspace_size(n, d, L, K) == 2 * al(n * 64 * 4) + al(n * 2 * 16)
-    assert rvq.rvq_encode_workspace_size(10, 70, 2, 300) == 2 * al(10 * 80 * 4) + al(10 * 3 * 16)
+    assert rvq.rvq_encode_workspace_size(n, d, L, K) == 2 * al(1024 * 64 * 4) + al(n * 2 * 16)
+    assert rvq.rvq_encode_workspace_size(10, 70, 2, 300) == 2 * al(128 * 80 * 4) + al(10 * 3 * 16)
     assert rvq.rvq_encode_workspace_size(0, d, L, K) == 256
+
+
+def test_encode_codebook_level_limit(rvq):
+    # one level of codewords (K x d rounded up to 16, fp32) must stay below 4 GiB
+    assert rvq.rvq_encode_workspace_size(1, 1280, 1, 800_000) > 0
+    with pytest.raises(rvq.RVQError) as e:
+        rvq.rvq_encode_workspace_size(1, 1280, 1, 1 << 20)
+    assert e.value.status == 2
 
 
 @pytest.mark.parametrize("n,d,L,K,err", [
