@@ -119,7 +119,11 @@ rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K,
  * residual_out : device, [n][d] fp32 output x - sum_l codebooks[l][ids[l]],
  *                or NULL when not wanted.  16-byte aligned.
  * d            : 1..1280 (RVQ_ERR_UNSUPPORTED above: a row's features stay
- *                resident in registers during the sweep).
+ *                resident in registers during the sweep).  One level of
+ *                codewords, K x (d rounded up to 16) fp32, must be below
+ *                4 GiB (RVQ_ERR_UNSUPPORTED otherwise; the same check applies
+ *                to rvq_prepared_size, rvq_prepare_codebooks and
+ *                rvq_encode_workspace_size).
  * workspace    : device, >= rvq_encode_workspace_size bytes, 256-byte
  *                aligned; contents on entry are ignored.
  */
