@@ -73,8 +73,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Stage blocks.  A slot holds a 4 KB norm area and one 16 KB stage; in the
 // stage, k-step ks of sub-tile j is the 1 KB A-fragment at byte
 // 4096 + (4*j + ks)*1024, and lane L reads its 16 bytes at slot base + 16*L.
-// A block runs one stage's MFMAs with each LDS read four MFMAs (one k-step)
-// ahead of its use, and during its last k-step it reads the first
+// A block runs one stage's MFMAs with each LDS read five MFMAs ahead of its
+// use, and during its last k-steps it reads the first
 // A-fragments of the next stage (norm fragments when the next stage opens a
 // tile) into p, so the next block starts its MFMAs without waiting for LDS.  Every read has completed
 // when a block ends (no load is in flight across blocks).  The leading
@@ -93,12 +93,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define RVQ_NEXT_TILE_2 RVQ_RD(p2, naddr, 2048)
 #define RVQ_NEXT_TILE_3 RVQ_RD(p3, naddr, 3072)
 #define RVQ_WAIT(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
-// One MFMA, then the read of the fragment four MFMAs ahead, once the
-// fragment it uses has arrived (at most four newer reads in flight).
-#define RVQ_STEP(rd, c, a, b) rd RVQ_WAIT(4) RVQ_MF(c, a, b)
 
-// Refill loads placed inside a block, one after each k-step's MFMAs, so they
-// issue while the matrix core is busy: this wave's four 1 KB blocks of the
+
+// Refill loads placed inside a block, one after the first MFMA of each
+// k-step, so they issue while the matrix core is busy: this wave's four 1 KB blocks of the
 // stage being refilled (uniform global base gsb in SGPRs plus the lane's
 // 32-bit offset voff; LDS destination lds).  Lane i's 16 bytes land at
 // M0 + offset + 16*i: the instruction offset moves the global and the LDS
@@ -111,39 +109,39 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define RVQ_D3 "global_load_lds_dwordx4 %[voff], %[gsb] offset:3072\n\t"
 
 // A stage inside a tile: p holds its k-step 0 on entry.  Reads are spread
-// one per MFMA, each four MFMAs ahead of its use: evenly spaced requests
-// keep the LDS queue short (a probe of this block measured 657 instead of
-// 682 cycles for the same reads issued in bursts of four).
-#define RVQ_STAGE_BODY(NX, D0, D1, D2, D3)                                                  \
-  RVQ_WAIT(0) RVQ_RD(t0, addr, 5120) RVQ_MF(c0, p0, b0) RVQ_RD(t1, addr, 9216)              \
-  RVQ_MF(c1, p1, b0) RVQ_RD(t2, addr, 13312) RVQ_MF(c2, p2, b0) RVQ_RD(t3, addr, 17408)     \
-  RVQ_MF(c3, p3, b0) D0                                                                     \
-  RVQ_STEP(RVQ_RD(t4, addr, 6144), c0, t0, b1) RVQ_STEP(RVQ_RD(t5, addr, 10240), c1, t1, b1) \
-  RVQ_STEP(RVQ_RD(t6, addr, 14336), c2, t2, b1) RVQ_STEP(RVQ_RD(t7, addr, 18432), c3, t3, b1) \
-  D1                                                                                        \
-  RVQ_STEP(RVQ_RD(t0, addr, 7168), c0, t4, b2) RVQ_STEP(RVQ_RD(t1, addr, 11264), c1, t5, b2) \
-  RVQ_STEP(RVQ_RD(t2, addr, 15360), c2, t6, b2) RVQ_STEP(RVQ_RD(t3, addr, 19456), c3, t7, b2) \
-  D2                                                                                        \
-  RVQ_STEP(NX##_0, c0, t0, b3) RVQ_STEP(NX##_1, c1, t1, b3) RVQ_STEP(NX##_2, c2, t2, b3)    \
-  RVQ_STEP(NX##_3, c3, t3, b3) D3 RVQ_WAIT(0)
+// one per MFMA, each five MFMAs ahead of its use, and a refill load follows
+// the first MFMA of each k-step: evenly spaced requests keep the LDS queue
+// short.  (Probes of this block measured 682 cycles with reads in bursts of
+// four one k-step ahead, 657 spread four ahead, 635 as here.)
+#define RVQ_STAGE_BODY(NX, D0, D1, D2, D3)                                               \
+  RVQ_WAIT(0) RVQ_RD(t0, addr, 5120) RVQ_RD(t1, addr, 9216) RVQ_MF(c0, p0, b0) D0        \
+  RVQ_RD(t2, addr, 13312) RVQ_MF(c1, p1, b0) RVQ_RD(t3, addr, 17408) RVQ_MF(c2, p2, b0)  \
+  RVQ_RD(t4, addr, 6144) RVQ_MF(c3, p3, b0) RVQ_RD(t5, addr, 10240) RVQ_WAIT(5)          \
+  RVQ_MF(c0, t0, b1) D1 RVQ_RD(t6, addr, 14336) RVQ_WAIT(5) RVQ_MF(c1, t1, b1)           \
+  RVQ_RD(t7, addr, 18432) RVQ_WAIT(5) RVQ_MF(c2, t2, b1) RVQ_RD(t0, addr, 7168)          \
+  RVQ_WAIT(5) RVQ_MF(c3, t3, b1) RVQ_RD(t1, addr, 11264) RVQ_WAIT(5) RVQ_MF(c0, t4, b2)  \
+  D2 RVQ_RD(t2, addr, 15360) RVQ_WAIT(5) RVQ_MF(c1, t5, b2) RVQ_RD(t3, addr, 19456)      \
+  RVQ_WAIT(5) RVQ_MF(c2, t6, b2) NX##_0 RVQ_WAIT(5) RVQ_MF(c3, t7, b2) NX##_1            \
+  RVQ_WAIT(5) RVQ_MF(c0, t0, b3) D3 NX##_2 RVQ_WAIT(5) RVQ_MF(c1, t1, b3) NX##_3         \
+  RVQ_WAIT(5) RVQ_MF(c2, t2, b3) RVQ_WAIT(4) RVQ_MF(c3, t3, b3) RVQ_WAIT(0)             
 
 // The stage opening a tile: p holds the norm k-step on entry, and the
 // accumulators start from ||c||^2 (B = ones at k = 0, 1).
 #define RVQ_MFN(c, a) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #a "], %[bn], 0\n\t"
-#define RVQ_STAGE0_BODY(NX, D0, D1, D2, D3)                                                 \
-  RVQ_WAIT(0) RVQ_RD(t0, addr, 4096) RVQ_MFN(c0, p0) RVQ_RD(t1, addr, 8192) RVQ_MFN(c1, p1) \
-  RVQ_RD(t2, addr, 12288) RVQ_MFN(c2, p2) RVQ_RD(t3, addr, 16384) RVQ_MFN(c3, p3)           \
-  RVQ_STEP(RVQ_RD(t4, addr, 5120), c0, t0, b0) RVQ_STEP(RVQ_RD(t5, addr, 9216), c1, t1, b0) \
-  RVQ_STEP(RVQ_RD(t6, addr, 13312), c2, t2, b0) RVQ_STEP(RVQ_RD(t7, addr, 17408), c3, t3, b0) \
-  D0                                                                                        \
-  RVQ_STEP(RVQ_RD(t0, addr, 6144), c0, t4, b1) RVQ_STEP(RVQ_RD(t1, addr, 10240), c1, t5, b1) \
-  RVQ_STEP(RVQ_RD(t2, addr, 14336), c2, t6, b1) RVQ_STEP(RVQ_RD(t3, addr, 18432), c3, t7, b1) \
-  D1                                                                                        \
-  RVQ_STEP(RVQ_RD(t4, addr, 7168), c0, t0, b2) RVQ_STEP(RVQ_RD(t5, addr, 11264), c1, t1, b2) \
-  RVQ_STEP(RVQ_RD(t6, addr, 15360), c2, t2, b2) RVQ_STEP(RVQ_RD(t7, addr, 19456), c3, t3, b2) \
-  D2                                                                                        \
-  RVQ_STEP(NX##_0, c0, t4, b3) RVQ_STEP(NX##_1, c1, t5, b3) RVQ_STEP(NX##_2, c2, t6, b3)    \
-  RVQ_STEP(NX##_3, c3, t7, b3) D3 RVQ_WAIT(0)
+#define RVQ_STAGE0_BODY(NX, D0, D1, D2, D3)                                              \
+  RVQ_WAIT(0) RVQ_RD(t0, addr, 4096) RVQ_RD(t1, addr, 8192) RVQ_MFN(c0, p0)              \
+  RVQ_RD(t2, addr, 12288) RVQ_MFN(c1, p1) RVQ_RD(t3, addr, 16384) RVQ_MFN(c2, p2)        \
+  RVQ_RD(t4, addr, 5120) RVQ_MFN(c3, p3) RVQ_RD(t5, addr, 9216) RVQ_WAIT(5)              \
+  RVQ_MF(c0, t0, b0) D0 RVQ_RD(t6, addr, 13312) RVQ_WAIT(5) RVQ_MF(c1, t1, b0)           \
+  RVQ_RD(t7, addr, 17408) RVQ_WAIT(5) RVQ_MF(c2, t2, b0) RVQ_RD(t0, addr, 6144)          \
+  RVQ_WAIT(5) RVQ_MF(c3, t3, b0) RVQ_RD(t1, addr, 10240) RVQ_WAIT(5) RVQ_MF(c0, t4, b1)  \
+  D1 RVQ_RD(t2, addr, 14336) RVQ_WAIT(5) RVQ_MF(c1, t5, b1) RVQ_RD(t3, addr, 18432)      \
+  RVQ_WAIT(5) RVQ_MF(c2, t6, b1) RVQ_RD(t4, addr, 7168) RVQ_WAIT(5) RVQ_MF(c3, t7, b1)   \
+  RVQ_RD(t5, addr, 11264) RVQ_WAIT(5) RVQ_MF(c0, t0, b2) D2 RVQ_RD(t6, addr, 15360)      \
+  RVQ_WAIT(5) RVQ_MF(c1, t1, b2) RVQ_RD(t7, addr, 19456) RVQ_WAIT(5) RVQ_MF(c2, t2, b2)  \
+  NX##_0 RVQ_WAIT(5) RVQ_MF(c3, t3, b2) NX##_1 RVQ_WAIT(5) RVQ_MF(c0, t4, b3) D3 NX##_2  \
+  RVQ_WAIT(5) RVQ_MF(c1, t5, b3) NX##_3 RVQ_WAIT(5) RVQ_MF(c2, t6, b3) RVQ_WAIT(4)       \
+  RVQ_MF(c3, t7, b3) RVQ_WAIT(0)
 
 #define RVQ_TEMPS                                                                          \
   [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [t4] "=&v"(t[4]), \
