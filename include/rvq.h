@@ -197,6 +197,26 @@ rvq_status rvq_level_stats(const int32_t *ids, int64_t n, int32_t L, int32_t K, 
                            double *msr, uint32_t *bad_ids,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Decode and level statistics of the same IDs in one pass.
+ *
+ * Produces exactly (bit for bit) what rvq_decode with levels == L followed by
+ * rvq_level_stats with msr would: out[row] = sum of the row's codewords in
+ * level order (fp32, out-of-range IDs skipped, stored as out_dtype), hist and
+ * msr as defined above.  The msr pass already gathers every level's codeword
+ * of every row, so the decode costs only its output writes.  Each
+ * out-of-range ID is counted once in *bad_ids.
+ *
+ * Arguments are those of rvq_decode and rvq_level_stats; x, msr and out are
+ * required (n > 0), and the workspace is sized by
+ * rvq_level_stats_workspace_size(n, L, K, d, 1).
+ * ---------------------------------------------------------------------- */
+rvq_status rvq_decode_level_stats(const int32_t *ids, int64_t n, const float *codebooks,
+                                  int32_t L, int32_t K, int32_t d, void *out, rvq_dtype out_dtype,
+                                  int64_t *hist, const void *x, rvq_dtype x_dtype, double *msr,
+                                  uint32_t *bad_ids, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

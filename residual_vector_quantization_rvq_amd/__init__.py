@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "RVQError", "library_path", "exported_symbols", "RVQ_F32", "RVQ_BF16",
     "rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size", "rvq_encode",
-    "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_status_string",
+    "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_decode_level_stats",
+    "rvq_status_string",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,8 +69,11 @@ _lib.rvq_decode.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _i32, _p, ctypes.c_i
 _lib.rvq_level_stats_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _psz]
 _lib.rvq_level_stats.argtypes = [_p, _i64, _i32, _i32, _p, _p, ctypes.c_int, _i32, _p, _p, _p,
                                  _p, _sz, _p]
+_lib.rvq_decode_level_stats.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _p, ctypes.c_int, _p, _p,
+                                        ctypes.c_int, _p, _p, _p, _sz, _p]
 for _f in ("rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size",
-           "rvq_encode", "rvq_encode_profiled", "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats"):
+           "rvq_encode", "rvq_encode_profiled", "rvq_decode", "rvq_level_stats_workspace_size",
+           "rvq_level_stats", "rvq_decode_level_stats"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -222,3 +226,36 @@ def rvq_level_stats(ids: torch.Tensor, K: int, x: Optional[torch.Tensor] = None,
                                 _ptr(msr), _ptr(bad_ids), _ptr(workspace), workspace.numel(),
                                 _stream(dev)))
     return hist, msr
+
+
+def rvq_decode_level_stats(ids: torch.Tensor, x: torch.Tensor, codebooks: torch.Tensor,
+                           out_dtype: torch.dtype = torch.float32,
+                           bad_ids: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None
+                           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Full decode [n, d], usage counts [L, K] int64 and mean squared residual
+    [L] fp64 of the same IDs in one gather pass (the same bits as rvq_decode
+    followed by rvq_level_stats)."""
+    _need_cuda("ids", ids)
+    _need_cuda("x", x)
+    _need_cuda("codebooks", codebooks)
+    L, K, d = codebooks.shape
+    n = ids.shape[0]
+    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[1] != L:
+        raise ValueError("ids must be int32 [n, L]")
+    if x.dim() != 2 or x.shape[0] != n or x.shape[1] != d:
+        raise ValueError("x must be [n, d] with the codebooks' d")
+    dev = ids.device
+    if out is None:
+        out = torch.empty((n, d), dtype=out_dtype, device=dev)
+    hist = torch.empty((L, K), dtype=torch.int64, device=dev)
+    msr = torch.empty((L,), dtype=torch.float64, device=dev)
+    wbytes = rvq_level_stats_workspace_size(n, L, K, d, True)
+    if workspace is None or workspace.numel() < wbytes:
+        workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    _check(_lib.rvq_decode_level_stats(_ptr(ids), n, _ptr(codebooks), L, K, d, _ptr(out),
+                                       _dtype_code(out.dtype), _ptr(hist), _ptr(x),
+                                       _dtype_code(x.dtype), _ptr(msr), _ptr(bad_ids),
+                                       _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, hist, msr

@@ -150,7 +150,10 @@ size_t hist_partial_bytes(int64_t n, int L, int K);
 hipError_t launch_hist(const int32_t *ids, int64_t n, int L, int K, int64_t *hist,
                        uint32_t *partial, uint32_t *bad, hipStream_t s);
 size_t msr_partial_bytes(int64_t n, int L);
+// out_kind 0: statistics only; 1 / 2: also write the full decode of the
+// rows to out as fp32 / bf16.
 hipError_t launch_msr(const void *x, bool x_bf16, const int32_t *ids, int64_t n, int d,
-                      const float *cb, int L, int K, double *msr, double *partial, hipStream_t s);
+                      const float *cb, int L, int K, double *msr, double *partial, void *out,
+                      int out_kind, hipStream_t s);
 
 }  // namespace rvq

@@ -305,8 +305,48 @@ rvq_status rvq_level_stats(const int32_t *ids, int64_t n, int32_t L, int32_t K, 
   double *mpart = (double *)(ws + align256(hist_partial_bytes(n, L, K)));
   HIP_TRY(launch_hist(ids, n, L, K, hist, hpart, bad_ids, stream), "histogram launch");
   if (with_msr)
-    HIP_TRY(launch_msr(x, x_dtype == RVQ_BF16, ids, n, d, codebooks, L, K, msr, mpart, stream),
+    HIP_TRY(launch_msr(x, x_dtype == RVQ_BF16, ids, n, d, codebooks, L, K, msr, mpart, nullptr,
+                       0, stream),
             "msr launch");
+  return RVQ_OK;
+}
+
+rvq_status rvq_decode_level_stats(const int32_t *ids, int64_t n, const float *codebooks,
+                                  int32_t L, int32_t K, int32_t d, void *out, rvq_dtype out_dtype,
+                                  int64_t *hist, const void *x, rvq_dtype x_dtype, double *msr,
+                                  uint32_t *bad_ids, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  RVQ_TRY(check_shape(n, d, L, K));
+  if (L > kMaxLevelsGather)
+    return fail(RVQ_ERR_UNSUPPORTED, "level statistics support L <= %d (got %d)",
+                kMaxLevelsGather, L);
+  if (out_dtype != RVQ_F32 && out_dtype != RVQ_BF16)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", (int)out_dtype);
+  if (x_dtype != RVQ_F32 && x_dtype != RVQ_BF16)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown x_dtype %d", (int)x_dtype);
+  RVQ_TRY(need(codebooks, "codebooks", 16));
+  RVQ_TRY(need(hist, "hist", 8));
+  RVQ_TRY(need(msr, "msr", 8));
+  if (n > 0) {
+    RVQ_TRY(need(ids, "ids", 4));
+    RVQ_TRY(need(out, "out", 16));
+    RVQ_TRY(need(x, "x", 16));
+  }
+  if (bad_ids && !aligned(bad_ids, 4))
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "bad_ids must be 4-byte aligned");
+  size_t need_bytes = 0;
+  RVQ_TRY(rvq_level_stats_workspace_size(n, L, K, d, 1, &need_bytes));
+  RVQ_TRY(need(workspace, "workspace", 256));
+  if (workspace_bytes < need_bytes)
+    return fail(RVQ_ERR_WORKSPACE_TOO_SMALL, "level-stats workspace needs %zu bytes (got %zu)",
+                need_bytes, workspace_bytes);
+  char *ws = (char *)workspace;
+  uint32_t *hpart = (uint32_t *)ws;
+  double *mpart = (double *)(ws + align256(hist_partial_bytes(n, L, K)));
+  HIP_TRY(launch_hist(ids, n, L, K, hist, hpart, bad_ids, stream), "histogram launch");
+  HIP_TRY(launch_msr(x, x_dtype == RVQ_BF16, ids, n, d, codebooks, L, K, msr, mpart, out,
+                     out_dtype == RVQ_BF16 ? 2 : 1, stream),
+          "decode and msr launch");
   return RVQ_OK;
 }
 

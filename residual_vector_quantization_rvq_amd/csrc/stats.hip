@@ -8,6 +8,12 @@
 // Visual Coding and 3D").  Both are exact or fixed-order reductions: counts
 // are integers, and the fp64 sums are reduced in an order that depends only
 // on n, so results are bitwise reproducible.
+//
+// The mean-squared-residual pass gathers every level's codeword of every
+// row, which is exactly what decoding needs; with an output buffer it also
+// writes the full reconstruction (sum of the codewords in level order, in
+// fp32, skipping out-of-range IDs), bit for bit what the decode kernel
+// writes, so decode and statistics of the same IDs cost one gather pass.
 #include "common.h"
 
 namespace rvq {
@@ -146,12 +152,34 @@ __device__ __forceinline__ double sq4(double acc, float4 r) {
   return fma((double)r.w, (double)r.w, acc);
 }
 
-template <bool VEC>
+// Decoded output of the fused pass: OUT 0 none, 1 fp32, 2 bf16 (rounded to
+// nearest even); stored non-temporally like the decode kernel's.
+typedef float msr_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t msr_u32x2 __attribute__((ext_vector_type(2)));
+template <int OUT>
+__device__ __forceinline__ void store_dec4(void *out, int64_t row, int d4, int i4, float4 v) {
+  if constexpr (OUT == 1) {
+    const msr_f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<msr_f32x4 *>(out) + row * d4 + i4);
+  } else if constexpr (OUT == 2) {
+    const uint32_t lo = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+    const msr_u32x2 w = {lo, hi};
+    __builtin_nontemporal_store(w, reinterpret_cast<msr_u32x2 *>(out) + row * d4 + i4);
+  }
+}
+template <int OUT>
+__device__ __forceinline__ void store_dec1(void *out, int64_t i, float v) {
+  if constexpr (OUT == 1) reinterpret_cast<float *>(out)[i] = v;
+  else if constexpr (OUT == 2) reinterpret_cast<uint16_t *>(out)[i] = f32_to_bf16_bits(v);
+}
+
+template <bool VEC, int OUT>
 __global__ __launch_bounds__(256) void msr_rows_kernel(const void *__restrict__ x, int x_bf16,
                                                        const int32_t *__restrict__ ids, int64_t n,
                                                        int d, const float *__restrict__ cb, int L,
                                                        int K, double *__restrict__ partial,
-                                                       int64_t nblocks) {
+                                                       int64_t nblocks, void *__restrict__ out) {
   __shared__ double wsum[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -166,14 +194,19 @@ __global__ __launch_bounds__(256) void msr_rows_kernel(const void *__restrict__ 
       const int64_t row = r0 + j;  // wave-uniform
       if (row >= n) break;
       const int32_t *rid = ids + row * L;
+      // the decoded row (sum of the codewords in level order) is complete
+      // in the last level chunk
+      const bool dec = OUT != 0 && lc + kMsrLevelChunk >= L;
       if constexpr (VEC) {
         for (int i4 = lane; i4 < d4; i4 += 64) {
           float4 r = load_x4(x, x_bf16, row, d4, i4);
+          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
           for (int l = 0; l < lc; ++l) {
             const int id = rid[l];
             if (id >= 0 && id < K) {
               const float4 c = cb4[((int64_t)l * K + id) * d4 + i4];
               r.x -= c.x; r.y -= c.y; r.z -= c.z; r.w -= c.w;
+              if (OUT != 0) { acc.x += c.x; acc.y += c.y; acc.z += c.z; acc.w += c.w; }
             }
           }
           float4 v[kMsrLevelChunk];
@@ -190,26 +223,40 @@ __global__ __launch_bounds__(256) void msr_rows_kernel(const void *__restrict__ 
             if (lc + u < L) {
               r.x -= v[u].x; r.y -= v[u].y; r.z -= v[u].z; r.w -= v[u].w;
               sq[u] = sq4(sq[u], r);
+              if (OUT != 0 && ok[u]) {
+                acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+              }
             }
           }
+          if (dec) store_dec4<OUT>(out, row, d4, i4, acc);
         }
       } else {
         for (int i = lane; i < d; i += 64) {
           float r = x_bf16 ? bf16_bits_to_f32(((const uint16_t *)x)[row * d + i])
                            : ((const float *)x)[row * d + i];
+          float acc = 0.f;
           for (int l = 0; l < lc; ++l) {
             const int id = rid[l];
-            if (id >= 0 && id < K) r -= cb[((int64_t)l * K + id) * d + i];
+            if (id >= 0 && id < K) {
+              const float c = cb[((int64_t)l * K + id) * d + i];
+              r -= c;
+              if (OUT != 0) acc += c;
+            }
           }
 #pragma unroll
           for (int u = 0; u < kMsrLevelChunk; ++u) {
             const int l = lc + u;
             if (l < L) {
               const int id = rid[l];
-              if (id >= 0 && id < K) r -= cb[((int64_t)l * K + id) * d + i];
+              if (id >= 0 && id < K) {
+                const float c = cb[((int64_t)l * K + id) * d + i];
+                r -= c;
+                if (OUT != 0) acc += c;
+              }
               sq[u] = fma((double)r, (double)r, sq[u]);
             }
           }
+          if (dec) store_dec1<OUT>(out, row * d + i, acc);
         }
       }
     }
@@ -255,18 +302,27 @@ size_t msr_partial_bytes(int64_t n, int L) {
 }
 
 hipError_t launch_msr(const void *x, bool x_bf16, const int32_t *ids, int64_t n, int d,
-                      const float *cb, int L, int K, double *msr, double *partial, hipStream_t s) {
+                      const float *cb, int L, int K, double *msr, double *partial, void *out,
+                      int out_kind, hipStream_t s) {
   const int64_t blocks = n > 0 ? ceil_div(n, kMsrRowsPerBlock) : 0;
   // float4 columns need d % 4 == 0 and 16-byte (fp32) / 8-byte (bf16) row starts,
   // which the aligned base pointers then give for every row
   const bool vec = (d & 3) == 0;
   if (blocks > 0) {
-    if (vec)
-      msr_rows_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-          x, x_bf16 ? 1 : 0, ids, n, d, cb, L, K, partial, blocks);
-    else
-      msr_rows_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-          x, x_bf16 ? 1 : 0, ids, n, d, cb, L, K, partial, blocks);
+    const dim3 grid((unsigned)blocks), block(256);
+#define RVQ_MSR(V, O)                                                                    \
+  msr_rows_kernel<V, O><<<grid, block, 0, s>>>(x, x_bf16 ? 1 : 0, ids, n, d, cb, L, K, \
+                                               partial, blocks, out)
+    if (vec) {
+      if (out_kind == 1) RVQ_MSR(true, 1);
+      else if (out_kind == 2) RVQ_MSR(true, 2);
+      else RVQ_MSR(true, 0);
+    } else {
+      if (out_kind == 1) RVQ_MSR(false, 1);
+      else if (out_kind == 2) RVQ_MSR(false, 2);
+      else RVQ_MSR(false, 0);
+    }
+#undef RVQ_MSR
   }
   msr_final_kernel<<<dim3((unsigned)L), dim3(256), 0, s>>>(partial, blocks, n, msr);
   return hipGetLastError();

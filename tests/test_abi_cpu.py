@@ -13,8 +13,8 @@ LIB = os.path.join(ROOT, "residual_vector_quantization_rvq_amd", "librvq.so")
 @pytest.fixture(scope="module")
 def rvq():
     if not os.path.exists(LIB):
-        from residual_vector_quantization_rvq_amd import _build
-        _build.build()
+        import __graft_entry__
+        __graft_entry__._builder().build()
     import residual_vector_quantization_rvq_amd as m
     return m
 
@@ -131,3 +131,23 @@ def test_prepare_rejects_small_buffer(rvq):
     p = ctypes.c_void_p
     assert lib.rvq_prepare_codebooks(p(256), 2, 3, 4, p(256), 16, None) == 3
     assert lib.rvq_prepare_codebooks(None, 2, 3, 4, p(256), 1 << 20, None) == 1
+
+
+def test_decode_level_stats_rejects_bad_arguments(rvq):
+    lib = rvq.raw_library()
+    p = ctypes.c_void_p
+    # (ids, n, cb, L, K, d, out, out_dtype, hist, x, x_dtype, msr, bad, ws, ws_bytes, stream)
+    args = [p(256), 4, p(256), 2, 3, 4, p(256), 1, p(256), p(256), 0, p(256), None, p(256),
+            1 << 20, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.rvq_decode_level_stats(*a)
+    assert call(a7=5) == 1                 # unknown out dtype
+    assert call(a10=9) == 1                # unknown x dtype
+    assert call(a11=None) == 1             # msr required
+    assert call(a6=None) == 1              # out required when n > 0
+    assert call(a9=p(8)) == 1              # x misaligned
+    assert call(a14=1) == 3                # workspace too small
+    assert call(a3=65) == 2                # L above the gather limit

@@ -16,7 +16,8 @@ CSRC = os.path.join(ROOT, "residual_vector_quantization_rvq_amd", "csrc")
 
 
 def _device_asm(src: str, out_dir: str) -> str:
-    from residual_vector_quantization_rvq_amd import _build
+    import __graft_entry__
+    _build = __graft_entry__._builder()
     out = os.path.join(out_dir, os.path.basename(src) + ".s")
     subprocess.run([_build.HIPCC, *_build.FLAGS, "-S", "--cuda-device-only", src, "-o", out],
                    check=True, stdout=subprocess.PIPE, stderr=subprocess.PIPE)

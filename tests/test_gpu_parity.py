@@ -256,6 +256,41 @@ def test_invalid_ids_with_msr_are_counted_once(rvq, dev, d, x_dtype):
     parity.check_msr(msr.cpu().numpy(), w.x, x_dtype, np.where(ok, ids_h, w.K).astype(np.int32), ext)
 
 
+# decode + level statistics in one pass: d = 1152 and 64 take the float4
+# path, d = 70 the scalar one; L = 10 needs two level chunks of the msr pass
+DECODE_STATS = [
+    (60, 1000, 1152, 8, 512, "bf16", torch.bfloat16),
+    (61, 333, 70, 10, 300, "f32", torch.float32),
+    (62, 257, 64, 10, 100, "f32", torch.bfloat16),
+    (63, 129, 70, 3, 50, "bf16", torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_STATS,
+                         ids=lambda c: f"s{c[0]}_n{c[1]}_d{c[2]}_L{c[3]}_K{c[4]}_{c[5]}")
+def test_decode_level_stats_matches_separate_calls(rvq, dev, case):
+    seed, n, d, L, K, x_dtype, out_dtype = case
+    w = workloads.random_problem(seed, n, d, L, K, x_dtype=x_dtype)
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids_h = np.random.default_rng(seed).integers(0, K, size=(n, L)).astype(np.int32)
+    ids_h[3, 1] = -1
+    ids_h[n - 1, L - 1] = K
+    ids = torch.from_numpy(ids_h).to(dev)
+    bad_a = torch.zeros(1, dtype=torch.int32, device=dev)
+    bad_b = torch.zeros(1, dtype=torch.int32, device=dev)
+    out_a = rvq.rvq_decode(ids, cb, out_dtype)
+    hist_a, msr_a = rvq.rvq_level_stats(ids, K, x, cb, bad_ids=bad_a)
+    out_b, hist_b, msr_b = rvq.rvq_decode_level_stats(ids, x, cb, out_dtype, bad_ids=bad_b)
+    torch.cuda.synchronize()
+    # the same bits as the two separate calls, and out-of-range IDs counted once
+    int_t = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(out_a.view(int_t), out_b.view(int_t))
+    assert torch.equal(hist_a, hist_b)
+    assert torch.equal(msr_a.view(torch.int64), msr_b.view(torch.int64))
+    assert int(bad_a.item()) == 2 and int(bad_b.item()) == 2
+
+
 def test_prefix_decode_levels(rvq, dev):
     w = workloads.random_problem(43, 90, 72, 5, 64)
     ids_h = np.random.default_rng(6).integers(0, w.K, size=(90, 5)).astype(np.int32)
