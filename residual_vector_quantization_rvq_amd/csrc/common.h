@@ -32,16 +32,17 @@ __device__ __forceinline__ bool lex_lt(float sa, int ia, float sb, int ib) {
 // two smallest under lex_lt.  Indices in the two lists must be distinct.
 __device__ __forceinline__ void merge_top2(float &s1, int &i1, float &s2, int &i2,
                                            float t1, int j1, float t2, int j2) {
-  if (lex_lt(t1, j1, s1, i1)) {
-    bool keep_s1 = lex_lt(s1, i1, t2, j2);
-    s2 = keep_s1 ? s1 : t2;
-    i2 = keep_s1 ? i1 : j2;
-    s1 = t1;
-    i1 = j1;
-  } else if (lex_lt(t1, j1, s2, i2)) {
-    s2 = t1;
-    i2 = j1;
-  }
+  // selects only: written as two branches through references, the list is
+  // kept in scratch memory
+  const bool first = lex_lt(t1, j1, s1, i1);   // t1 becomes the best
+  const bool keep1 = lex_lt(s1, i1, t2, j2);   // ... and s1 or t2 the second
+  const bool second = lex_lt(t1, j1, s2, i2);  // else t1 may become the second
+  const float n2 = first ? (keep1 ? s1 : t2) : (second ? t1 : s2);
+  const int m2 = first ? (keep1 ? i1 : j2) : (second ? j1 : i2);
+  s1 = first ? t1 : s1;
+  i1 = first ? j1 : i1;
+  s2 = n2;
+  i2 = m2;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {

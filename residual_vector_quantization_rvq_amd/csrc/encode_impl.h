@@ -376,57 +376,6 @@ __device__ __forceinline__ void build_bfrags_bf16(RowFrags<KS> &bfr, const uint1
   });
 }
 
-// Exact fp32 rescoring of the two candidates and residual update for one
-// row; lanes L and L+32 (h = 0, 1) each take features ks*16 + h*8 + e in
-// order ks, e, accumulating (r - c)^2 with fmaf, and the row's distance is
-// (half 0) + (half 1).  Returns the chosen index.  One pass over the row:
-// r - c1 is written to dst as it goes (the screening's best is almost
-// always the winner), and rows where c2 wins are rewritten with r - c2.
-// dst must not alias src.
-__device__ __forceinline__ int rescore_update(const float *src, float *dst, bool store,
-                                              int64_t row, int dp, const float *cb_l, int c1,
-                                              int c2, bool v2, int h) {
-  float p1 = 0.f, p2 = 0.f;
-  const int kend = dp >> 4;
-#pragma unroll 4
-  for (int ks = 0; ks < kend; ++ks) {
-    const int i0 = ks * 16 + h * 8;
-    float r[8], a[8], b[8], v[8];
-    read8(src, row, dp, i0, true, r);
-    read8(cb_l, c1, dp, i0, true, a);
-    read8(cb_l, c2, dp, i0, true, b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = r[e] - a[e];
-      const float u = r[e] - b[e];
-      p1 = fmaf(t, t, p1);
-      p2 = fmaf(u, u, p2);
-      v[e] = t;
-    }
-    if (store) write8(dst, row, dp, i0, v);
-  }
-  const float q1 = __shfl_xor(p1, 32, 64);
-  const float q2 = __shfl_xor(p2, 32, 64);
-  const float d1 = h ? q1 + p1 : p1 + q1;
-  const float d2 = h ? q2 + p2 : p2 + q2;
-  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
-  if (store && __ballot(take2)) {
-    if (take2) {
-#pragma unroll 4
-      for (int ks = 0; ks < kend; ++ks) {
-        const int i0 = ks * 16 + h * 8;
-        float r[8], b[8], v[8];
-        read8(src, row, dp, i0, true, r);
-        read8(cb_l, c2, dp, i0, true, b);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = r[e] - b[e];
-        write8(dst, row, dp, i0, v);
-      }
-    }
-  }
-  return take2 ? c2 : c1;
-}
-
 // First two candidates of a row's top-2 list as valid codeword indices.
 __device__ __forceinline__ void candidates(int i1, int i2, int K, int &c1, int &c2, bool &v2) {
   c1 = (i1 >= 0 && i1 < K) ? i1 : 0;  // finite inputs always give a valid first candidate
@@ -1070,32 +1019,117 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
 }
 
-// Split mode, after every split of a level wrote its list: merge the lists
-// (a total order, so any merge order gives the same result) and run the
-// same rescoring and update as the fused kernel.
+// Split mode, after every split of a level wrote its list: one wave per
+// row, four rows per workgroup.  The wave merges the row's lists in split
+// order (a total order, so the result is that of the fused kernel's merge),
+// then rescores the two candidates exactly as the fused kernel does: for
+// candidate c and half h, one lane accumulates (r - c)^2 over features
+// ks*16 + h*8 + e, in order ks, e, with fmaf, and the distance is
+// (half 0) + (half 1).  The smaller distance wins, the lower index on a tie.
+// Every lane loads 16-byte pieces of the row and of both candidates, all in
+// flight at once; the four accumulating lanes read them back from this
+// wave's area of LDS, and the residual r - c is written from the registers.
 template <int S>
 __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int level, int splits) {
+  constexpr int kRow4 = S * kStageCols / 4;  // float4 capacity of a row (dp <= 64 S)
+  constexpr int NV = (kRow4 + 63) / 64;      // float4 of a row per lane
+  __shared__ float4 area[4][3][kRow4];       // per wave: row, candidate 1, candidate 2
   const int lane = threadIdx.x & 63;
-  const int h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerWG + wave * 32 + (lane & 31);
-  const bool live = row < a.n;
-  const int64_t rowc = live ? row : a.n - 1;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= a.n) return;
+  const int dp4 = a.dp >> 2;
+  // (selects, not a run-time index into the argument struct, which would
+  // copy it to scratch)
+  const float *src = level == 0 ? a.src0 : (level & 1) ? a.rbuf[1] : a.rbuf[0];
+  const float4 *rs = reinterpret_cast<const float4 *>(src + row * a.dp);
+  float4 r[NV], x1[NV], x2[NV];
+  static_for<0, NV>([&](auto V_) {
+    constexpr int v = decltype(V_)::value;
+    const int i = lane + 64 * v;
+    if (i < dp4) r[v] = rs[i];
+  });
+
   float S1 = __builtin_inff(), S2 = __builtin_inff();
   int I1 = kNoIndex, I2 = kNoIndex;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float4 p = a.part[rowc * splits + sp];
-    merge_top2(S1, I1, S2, I2, p.x, __float_as_int(p.y), p.z, __float_as_int(p.w));
+  const float4 *pp = a.part + row * splits;
+  for (int s0 = 0; s0 < splits; s0 += 64) {
+    float4 e = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s0 + lane < splits) e = pp[s0 + lane];
+    const int m = splits - s0 < 64 ? splits - s0 : 64;
+    for (int j = 0; j < m; ++j) {
+      const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.x), j));
+      const int j1 = __builtin_amdgcn_readlane(__float_as_int(e.y), j);
+      const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.z), j));
+      const int j2 = __builtin_amdgcn_readlane(__float_as_int(e.w), j);
+      merge_top2(S1, I1, S2, I2, t1, j1, t2, j2);
+    }
   }
   int c1, c2;
   bool v2;
-  candidates(I1, I2, a.K, c1, c2, v2);
-  const bool last = level == a.L - 1;
-  const float *src = level == 0 ? a.src0 : a.rbuf[level & 1];
-  float *dst = last ? a.res_final : a.rbuf[(level + 1) & 1];
+  candidates(I1, I2, a.K, c1, c2, v2);  // c2 == c1 when there is no second
   const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
-  const int id = rescore_update(src, dst, live && dst != nullptr, rowc, a.dp, cb_l, c1, c2, v2, h);
-  if (live && h == 0) a.ids[row * a.L + level] = id;
+  const float4 *p1 = reinterpret_cast<const float4 *>(cb_l + (int64_t)c1 * a.dp);
+  const float4 *p2 = reinterpret_cast<const float4 *>(cb_l + (int64_t)c2 * a.dp);
+  static_for<0, NV>([&](auto V_) {
+    constexpr int v = decltype(V_)::value;
+    const int i = lane + 64 * v;
+    if (i < dp4) {
+      x1[v] = p1[i];
+      x2[v] = p2[i];
+    }
+  });
+  static_for<0, NV>([&](auto V_) {
+    constexpr int v = decltype(V_)::value;
+    const int i = lane + 64 * v;
+    if (i < dp4) {
+      area[wave][0][i] = r[v];
+      area[wave][1][i] = x1[v];
+      area[wave][2][i] = x2[v];
+    }
+  });
+  // the area is this wave's alone: order its writes before the reads of
+  // other lanes of the same wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float p = 0.f;
+  if (lane < 4) {
+    const int h = lane & 1;
+    const float4 *rl = &area[wave][0][h * 2];
+    const float4 *xl = &area[wave][1 + (lane >> 1)][h * 2];
+    const int kend = a.dp >> 4;
+#pragma unroll 4
+    for (int ks = 0; ks < kend; ++ks) {
+      const float4 ra = rl[ks * 4], rb = rl[ks * 4 + 1];
+      const float4 xa = xl[ks * 4], xb = xl[ks * 4 + 1];
+      const float rv[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = rv[e] - xv[e];
+        p = fmaf(t, t, p);
+      }
+    }
+  }
+  const float d1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 0)) +
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 1));
+  const float d2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 2)) +
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 3));
+  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
+  float *dst = level == a.L - 1 ? a.res_final : (level & 1) ? a.rbuf[0] : a.rbuf[1];
+  if (dst != nullptr) {
+    float4 *ds = reinterpret_cast<float4 *>(dst + row * a.dp);
+    static_for<0, NV>([&](auto V_) {
+      constexpr int v = decltype(V_)::value;
+      const int i = lane + 64 * v;
+      if (i < dp4) {
+        const float4 c = take2 ? x2[v] : x1[v];
+        ds[i] = make_float4(r[v].x - c.x, r[v].y - c.y, r[v].z - c.z, r[v].w - c.w);
+      }
+    });
+  }
+  if (lane == 0) a.ids[row * a.L + level] = take2 ? c2 : c1;
 }
 
 template <int S>
@@ -1114,7 +1148,7 @@ hipError_t launch_stage_count(const EncodePlan &p, const EncodeArgs &a, hipEvent
         a, p.tiles, l, p.splits, p.tiles_per_split);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[2 * l + 1], s)) != hipSuccess) return e;
-    split_update_kernel<S><<<dim3(p.row_blocks), dim3(NT), 0, s>>>(a, l, p.splits);
+    split_update_kernel<S><<<dim3((unsigned)ceil_div(a.n, 4)), dim3(NT), 0, s>>>(a, l, p.splits);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
