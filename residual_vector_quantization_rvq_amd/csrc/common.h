@@ -137,6 +137,11 @@ struct EncodeArgs {
   float *residual_out;  // caller's [n][d] output or null
   int32_t *ids;
   float4 *part;
+  // Split mode: bf16 B-fragments of the rows the next sweep reads (the
+  // input, then each level's residual), in blocks of 32 rows: the 16 bytes
+  // of lane L for k-step ks of block b are at ((b * dp/16 + ks) * 64 + L),
+  // holding features ks*16 + (L/32)*8 .. +7 of row 32 b + L%32.
+  uint4 *xfrag;
   // set by launch_encode
   const float *src0;    // level-0 rows, fp32 stride dp (x itself or a staged copy)
   const uint16_t *x16;  // fused mode with bf16 rows of stride dp: level 0 reads them directly

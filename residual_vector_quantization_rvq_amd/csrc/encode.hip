@@ -41,6 +41,30 @@ __global__ __launch_bounds__(256) void unfragment_kernel(const float *__restrict
   }
 }
 
+// bf16 B-fragments of the level-0 rows (split mode), from the fp32 rows of
+// stride dp: one thread per 16-byte piece, piece (b, ks, L) holding features
+// ks*16 + (L/32)*8 .. +7 of row 32 b + L%32 (zeros for rows past n, up to
+// the end of the last 128-row block).
+__global__ __launch_bounds__(256) void fragment_rows_kernel(const float *__restrict__ src,
+                                                            int64_t n, int dp,
+                                                            uint4 *__restrict__ frag,
+                                                            int64_t pieces) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= pieces) return;
+  const int lane = (int)(o & 63);
+  const int ksp = dp >> 4;
+  const int64_t rest = o >> 6;
+  const int ks = (int)(rest % ksp);
+  const int64_t row = (rest / ksp) * 32 + (lane & 31);
+  u32x4 q = {0u, 0u, 0u, 0u};
+  if (row < n) {
+    float v[8];
+    read8(src, row, dp, ks * 16 + (lane >> 5) * 8, true, v);
+    q = to_bf16x8(v);
+  }
+  frag[o] = make_uint4(q[0], q[1], q[2], q[3]);
+}
+
 // residual_out [n][d] from the padded fp32 residual [n][dp].
 __global__ __launch_bounds__(256) void unpad_kernel(const float *__restrict__ src, int64_t n,
                                                     int d, int dp, float *__restrict__ out) {
@@ -112,6 +136,12 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   float *final_buf = a.rbuf[a.L & 1];
   const bool convert = a.residual_out && (p.fused || a.dp != a.d);
   a.res_final = convert ? final_buf : a.residual_out;
+  if (!p.fused) {
+    // every block a sweep workgroup reads (4 per 128 rows)
+    const int64_t pieces = ceil_div(a.n, kRowsPerWG) * 4 * (a.dp >> 4) * 64;
+    fragment_rows_kernel<<<dim3((unsigned)ceil_div(pieces, 256)), dim3(256), 0, s>>>(
+        a.src0, a.n, a.dp, a.xfrag, pieces);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_stages(p, a, events, s);

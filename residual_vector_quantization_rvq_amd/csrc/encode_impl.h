@@ -353,6 +353,31 @@ __device__ __forceinline__ void read_src(const uint16_t *src, int64_t row, int d
   read8_bf16(src, row, dp, i0, v);
 }
 
+// The same fragments from the bf16 fragment copy of a block of 32 rows
+// (split mode): k-step ks of lane L is the 16 bytes at blk[ks * 64 + L], so
+// every load of a wave is 1 KB of consecutive bytes.  K-steps past the row
+// (ks >= ksp) are zero.
+template <int KS>
+__device__ __forceinline__ void build_bfrags_frag(RowFrags<KS> &bfr, const uint4 *blk, int ksp,
+                                                  int lane) {
+  static_for<0, (KS + 15) / 16>([&](auto G_) {
+    constexpr int g = decltype(G_)::value;
+    constexpr int n = KS - g * 16 < 16 ? KS - g * 16 : 16;
+    u32x4 f[16];
+    static_for<0, n>([&](auto U_) {
+      constexpr int ks = g * 16 + decltype(U_)::value;
+      const bool active = ks < ksp;
+      const uint4 q = blk[(active ? ks : 0) * 64 + lane];
+      f[decltype(U_)::value] = active ? u32x4{q.x, q.y, q.z, q.w} : u32x4{0u, 0u, 0u, 0u};
+    });
+    static_for<0, n>([&](auto U_) {
+      constexpr int ks = g * 16 + decltype(U_)::value;
+      bfr.template set<ks>(f[decltype(U_)::value]);
+    });
+    opaque(blk);
+  });
+}
+
 // The same fragments straight from bf16 rows (stride dp): the stored bits
 // are the fragment.
 template <int KS>
@@ -811,21 +836,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const uint32_t ring_lds = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4 *)ring);
   const uint32_t lane_lds = ring_lds + (uint32_t)lane * 16u;
 
+  const uint4 *ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l_begin * T + t0) * tile_u4;
+  // prologue of the first level: stages 0 .. kAhead-1
+  auto prologue = [&]() {
+    static_for<0, kAhead>([&](auto K_) {
+      constexpr int k = decltype(K_)::value;
+      if (k < nst) issue_stage(ls, tile_u4, k / S, k % S, k, ring_lds, wave, lane);
+    });
+  };
   RowFrags<KS> bfr;
-  if (l_begin == 0 && a.x16)
-    build_bfrags_bf16<KS>(bfr, a.x16, rowc, a.dp, h);
-  else
-    build_bfrags<KS>(bfr, l_begin == 0 ? a.src0 : a.rbuf[l_begin & 1], rowc, a.dp, h);
+  if (FUSED) {
+    if (a.x16)
+      build_bfrags_bf16<KS>(bfr, a.x16, rowc, a.dp, h);
+    else
+      build_bfrags<KS>(bfr, a.src0, rowc, a.dp, h);
+    prologue();
+  } else {
+    // one sweep per level and workgroup: the ring fills while the
+    // fragments load
+    prologue();
+    const int ksp = a.dp >> 4;
+    build_bfrags_frag<KS>(bfr, a.xfrag + ((int64_t)rb * 4 + wave) * ksp * 64, ksp, lane);
+  }
   // B-fragment of the norm k-step: ones at k = 0, 1 (lanes of half 0)
   u32x4 bnorm = {0u, 0u, 0u, 0u};
   if (h == 0) bnorm[0] = 0x3F803F80u;  // two bf16 ones
-
-  const uint4 *ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l_begin * T + t0) * tile_u4;
-  // prologue of the first level: stages 0 .. kAhead-1
-  static_for<0, kAhead>([&](auto K_) {
-    constexpr int k = decltype(K_)::value;
-    if (k < nst) issue_stage(ls, tile_u4, k / S, k % S, k, ring_lds, wave, lane);
-  });
 
   for (int l = l_begin; l < l_end; ++l) {
     ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l * T + t0) * tile_u4;
@@ -1126,6 +1161,24 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
       if (i < dp4) {
         const float4 c = take2 ? x2[v] : x1[v];
         ds[i] = make_float4(r[v].x - c.x, r[v].y - c.y, r[v].z - c.z, r[v].w - c.w);
+      }
+    });
+  }
+  if (level + 1 < a.L) {
+    // bf16 fragment copy for the next level's sweep: the 4 features of a
+    // float4 are half q of lane (h*32 + row%32)'s 16 bytes of k-step ks
+    uint2 *fr = reinterpret_cast<uint2 *>(a.xfrag + (row >> 5) * (a.dp >> 4) * 64);
+    const int rl = (int)(row & 31);
+    static_for<0, NV>([&](auto V_) {
+      constexpr int v = decltype(V_)::value;
+      const int i = lane + 64 * v;
+      if (i < dp4) {
+        const float4 c = take2 ? x2[v] : x1[v];
+        const bf16x2 lo = {(__bf16)(r[v].x - c.x), (__bf16)(r[v].y - c.y)};
+        const bf16x2 hi = {(__bf16)(r[v].z - c.z), (__bf16)(r[v].w - c.w)};
+        const int ks = i >> 2, hq = i & 3;
+        fr[((ks * 64 + (hq >> 1) * 32 + rl) << 1) + (hq & 1)] =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
     });
   }

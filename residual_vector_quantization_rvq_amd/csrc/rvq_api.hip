@@ -89,11 +89,12 @@ PreparedLayout prepared_layout(int32_t L, int32_t K, int32_t d) {
 }
 
 struct EncodeLayout {
-  size_t r0_off, r1_off, part_off, total;
+  size_t r0_off, r1_off, part_off, frag_off, total;
 };
 // Workspace: two fp32 residual buffers [n][dp] (level l reads one and
 // writes the other) and, for the split plan, one top-2 list per row and
-// codeword tile [n][tiles] (the largest split count).
+// codeword tile [n][tiles] (the largest split count) and the bf16
+// B-fragments of the rows the next sweep reads [n][dp].
 EncodeLayout encode_layout(int64_t n, int32_t d, int32_t K) {
   EncodeLayout w;
   const size_t tiles = (size_t)(padded_k(K) / kTileCw);
@@ -104,7 +105,8 @@ EncodeLayout encode_layout(int64_t n, int32_t d, int32_t K) {
   w.r0_off = 0;
   w.r1_off = rbytes;
   w.part_off = 2 * rbytes;
-  w.total = w.part_off + align256((size_t)n * tiles * sizeof(float4));
+  w.frag_off = w.part_off + align256((size_t)n * tiles * sizeof(float4));
+  w.total = w.frag_off + align256((size_t)round_up(n, kRowsPerWG) * row_stride(d) * 2);
   if (w.total == 0) w.total = 256;
   return w;
 }
@@ -226,6 +228,7 @@ rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int3
   a.residual_out = residual_out;
   a.ids = ids;
   a.part = (float4 *)(ws + wl.part_off);
+  a.xfrag = (uint4 *)(ws + wl.frag_off);
   const EncodePlan plan = plan_encode(n, d, K, num_cus());
   HIP_TRY(launch_encode(plan, a, events, stream), "encode launch");
   if (launches) *launches = plan.fused ? 1 : L;

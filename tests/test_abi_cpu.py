@@ -54,12 +54,14 @@ def test_prepared_size_layout(rvq):
 
 
 def test_encode_workspace_size(rvq):
-    # two fp32 residuals [n rounded up to 128][d rounded up to 16] and one
-    # top-2 list per row and 128-codeword tile
+    # two fp32 residuals [n rounded up to 128][d rounded up to 16], one
+    # top-2 list per row and 128-codeword tile, and a bf16 copy of the rows
     al = lambda v: (v + 255) // 256 * 256
     n, d, L, K = 1000, 64, 4, 256
-    assert rvq.rvq_encode_workspace_size(n, d, L, K) == 2 * al(1024 * 64 * 4) + al(n * 2 * 16)
-    assert rvq.rvq_encode_workspace_size(10, 70, 2, 300) == 2 * al(128 * 80 * 4) + al(10 * 3 * 16)
+    assert rvq.rvq_encode_workspace_size(n, d, L, K) == (2 * al(1024 * 64 * 4) + al(n * 2 * 16)
+                                                        + al(1024 * 64 * 2))
+    assert rvq.rvq_encode_workspace_size(10, 70, 2, 300) == (2 * al(128 * 80 * 4) + al(10 * 3 * 16)
+                                                            + al(128 * 80 * 2))
     assert rvq.rvq_encode_workspace_size(0, d, L, K) == 256
 
 
