@@ -1054,21 +1054,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
 }
 
+// c ? a : b by components (a select of whole array elements becomes a
+// select of their addresses, which keeps the arrays in scratch memory)
+__device__ __forceinline__ float4 select4(bool c, float4 a, float4 b) {
+  return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 // Split mode, after every split of a level wrote its list: one wave per
-// row, four rows per workgroup.  The wave merges the row's lists in split
-// order (a total order, so the result is that of the fused kernel's merge),
-// then rescores the two candidates exactly as the fused kernel does: for
+// row, four rows per workgroup.  The wave merges the row's lists, then
+// rescores the two candidates exactly as the fused kernel does: for
 // candidate c and half h, one lane accumulates (r - c)^2 over features
 // ks*16 + h*8 + e, in order ks, e, with fmaf, and the distance is
 // (half 0) + (half 1).  The smaller distance wins, the lower index on a tie.
 // Every lane loads 16-byte pieces of the row and of both candidates, all in
-// flight at once; the four accumulating lanes read them back from this
-// wave's area of LDS, and the residual r - c is written from the registers.
+// flight at once, and forms r - c for both; the four accumulating lanes read
+// these back from this wave's area of LDS, and the winner's r - c is written
+// from the registers.
 template <int S>
 __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int level, int splits) {
   constexpr int kRow4 = S * kStageCols / 4;  // float4 capacity of a row (dp <= 64 S)
   constexpr int NV = (kRow4 + 63) / 64;      // float4 of a row per lane
-  __shared__ float4 area[4][3][kRow4];       // per wave: row, candidate 1, candidate 2
+  __shared__ float4 area[4][2][kRow4];       // per wave: r - c1, r - c2
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -1085,24 +1091,29 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
     if (i < dp4) r[v] = rs[i];
   });
 
+  // Lane j merges the lists of splits j, j + 64, ..., then a butterfly
+  // merges the lanes' lists.  Every split holds at least one tile, so its
+  // list has two real, distinct codewords, and with finite scores the two
+  // smallest of all of them under the total order are unique: any merge
+  // order, the fused kernel's included, gives the same pair.
   float S1 = __builtin_inff(), S2 = __builtin_inff();
   int I1 = kNoIndex, I2 = kNoIndex;
   const float4 *pp = a.part + row * splits;
-  for (int s0 = 0; s0 < splits; s0 += 64) {
-    float4 e = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (s0 + lane < splits) e = pp[s0 + lane];
-    const int m = splits - s0 < 64 ? splits - s0 : 64;
-    for (int j = 0; j < m; ++j) {
-      const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.x), j));
-      const int j1 = __builtin_amdgcn_readlane(__float_as_int(e.y), j);
-      const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.z), j));
-      const int j2 = __builtin_amdgcn_readlane(__float_as_int(e.w), j);
-      merge_top2(S1, I1, S2, I2, t1, j1, t2, j2);
-    }
+  for (int sp = lane; sp < splits; sp += 64) {
+    const float4 e = pp[sp];
+    merge_top2(S1, I1, S2, I2, e.x, __float_as_int(e.y), e.z, __float_as_int(e.w));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u1 = __shfl_xor(S1, off, 64), u2 = __shfl_xor(S2, off, 64);
+    const int j1 = __shfl_xor(I1, off, 64), j2 = __shfl_xor(I2, off, 64);
+    merge_top2(S1, I1, S2, I2, u1, j1, u2, j2);
   }
   int c1, c2;
   bool v2;
   candidates(I1, I2, a.K, c1, c2, v2);  // c2 == c1 when there is no second
+  c1 = __builtin_amdgcn_readfirstlane(c1);  // (the same in every lane)
+  c2 = __builtin_amdgcn_readfirstlane(c2);
   const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
   const float4 *p1 = reinterpret_cast<const float4 *>(cb_l + (int64_t)c1 * a.dp);
   const float4 *p2 = reinterpret_cast<const float4 *>(cb_l + (int64_t)c2 * a.dp);
@@ -1114,13 +1125,17 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
       x2[v] = p2[i];
     }
   });
+  // r - c for both candidates, elementwise in every lane (the residual
+  // of whichever wins), then into this wave's area for the accumulating lanes
+  float4 t1[NV], t2[NV];
   static_for<0, NV>([&](auto V_) {
     constexpr int v = decltype(V_)::value;
     const int i = lane + 64 * v;
     if (i < dp4) {
-      area[wave][0][i] = r[v];
-      area[wave][1][i] = x1[v];
-      area[wave][2][i] = x2[v];
+      t1[v] = make_float4(r[v].x - x1[v].x, r[v].y - x1[v].y, r[v].z - x1[v].z, r[v].w - x1[v].w);
+      t2[v] = make_float4(r[v].x - x2[v].x, r[v].y - x2[v].y, r[v].z - x2[v].z, r[v].w - x2[v].w);
+      area[wave][0][i] = t1[v];
+      area[wave][1][i] = t2[v];
     }
   });
   // the area is this wave's alone: order its writes before the reads of
@@ -1130,21 +1145,15 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float p = 0.f;
   if (lane < 4) {
-    const int h = lane & 1;
-    const float4 *rl = &area[wave][0][h * 2];
-    const float4 *xl = &area[wave][1 + (lane >> 1)][h * 2];
+    // lane 2c + h: candidate c + 1, half h
+    const float4 *tl = &area[wave][lane >> 1][(lane & 1) * 2];
     const int kend = a.dp >> 4;
 #pragma unroll 4
     for (int ks = 0; ks < kend; ++ks) {
-      const float4 ra = rl[ks * 4], rb = rl[ks * 4 + 1];
-      const float4 xa = xl[ks * 4], xb = xl[ks * 4 + 1];
-      const float rv[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      const float4 ta = tl[ks * 4], tb = tl[ks * 4 + 1];
+      const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = rv[e] - xv[e];
-        p = fmaf(t, t, p);
-      }
+      for (int e = 0; e < 8; ++e) p = fmaf(tv[e], tv[e], p);
     }
   }
   const float d1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 0)) +
@@ -1158,10 +1167,7 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
     static_for<0, NV>([&](auto V_) {
       constexpr int v = decltype(V_)::value;
       const int i = lane + 64 * v;
-      if (i < dp4) {
-        const float4 c = take2 ? x2[v] : x1[v];
-        ds[i] = make_float4(r[v].x - c.x, r[v].y - c.y, r[v].z - c.z, r[v].w - c.w);
-      }
+      if (i < dp4) ds[i] = select4(take2, t2[v], t1[v]);
     });
   }
   if (level + 1 < a.L) {
@@ -1173,9 +1179,9 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
       constexpr int v = decltype(V_)::value;
       const int i = lane + 64 * v;
       if (i < dp4) {
-        const float4 c = take2 ? x2[v] : x1[v];
-        const bf16x2 lo = {(__bf16)(r[v].x - c.x), (__bf16)(r[v].y - c.y)};
-        const bf16x2 hi = {(__bf16)(r[v].z - c.z), (__bf16)(r[v].w - c.w)};
+        const float4 t = select4(take2, t2[v], t1[v]);
+        const bf16x2 lo = {(__bf16)t.x, (__bf16)t.y};
+        const bf16x2 hi = {(__bf16)t.z, (__bf16)t.w};
         const int ks = i >> 2, hq = i & 3;
         fr[((ks * 64 + (hq >> 1) * 32 + rl) << 1) + (hq & 1)] =
             make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
