@@ -69,6 +69,10 @@ RAGGED = [
     (36, 200, 64, 5, 2, "bf16"),
     (37, 1000, 128, 4, 2048, "bf16"),
     (38, 77, 1280, 3, 700, "f32"),
+    # more than 64 (and 128) codeword tiles per row in the per-level split
+    # plan: a lane of the update merges several splits' lists
+    (39, 100, 64, 2, 10000, "f32"),
+    (40, 5, 48, 2, 20000, "bf16"),
 ]
 
 
