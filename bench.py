@@ -154,9 +154,10 @@ def _time_ms(torch, fn, reps: int) -> float:
 def secondary(torch, rvq, workloads, dev) -> dict:
     """The other configured workloads, each against its own roofline (not
     part of the step above): the single 32x32 image (1024 rows, K=4096, the
-    small-batch encoder mode), and the decode-heavy workload (4,194,304 x 8
-    IDs decoded to bf16; counts over them; mean squared residual of a
-    65,536-row fp32 subset encoded at L=8)."""
+    small-batch encoder mode), the decode-heavy workload (4,194,304 x 8 IDs
+    decoded to bf16; counts over them; mean squared residual of a
+    65,536-row fp32 subset encoded at L=8), and the offline bulk tokenisation
+    (1,048,576 bf16 rows of width 1280, L=16, K=16384; encode only)."""
     import numpy as np
     out = {}
     w = workloads.single_image()
@@ -205,6 +206,23 @@ def secondary(torch, rvq, workloads, dev) -> dict:
     gathered = w.N * (4 * w.D + 4 * L + 4 * L * w.D)
     out["decode_heavy_msr"] = {"N": w.N, "L": L, "D": w.D, "ms": round(ms, 4),
                                "gather_counted_GBps": round(gathered / (ms * 1e-3) / 1e9, 1)}
+    del xs, sids, ws2, ws, ids, cb
+    # offline bulk tokenisation, encode only, at full size
+    w = workloads.bulk_tokenisation()
+    x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prep = rvq.rvq_prepare_codebooks(cb)
+    wsp = torch.empty(rvq.rvq_encode_workspace_size(w.N, w.D, w.L, w.K), dtype=torch.uint8,
+                      device=dev)
+    ids = rvq.rvq_encode(x, cb, prep, workspace=wsp)
+    torch.cuda.synchronize(dev)
+    ms = _time_ms(torch, lambda: rvq.rvq_encode(x, cb, prep, workspace=wsp, ids_out=ids), 3)
+    fl = 2.0 * w.N * w.K * w.D * w.L
+    out["bulk_tokenisation_encode"] = {
+        "N": w.N, "D": w.D, "K": w.K, "L": w.L, "x_dtype": "bf16", "ms": round(ms, 2),
+        "vectors_per_s": round(w.N / (ms * 1e-3), 1),
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+        "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     return out
 
 
@@ -216,7 +234,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the single-image encode and decode-heavy measurements")
+                    help="skip the single-image, decode-heavy and bulk-tokenisation measurements")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain copy of this many MiB "
                          "(the calibration dispatch for HBM byte counters)")
