@@ -21,6 +21,19 @@ namespace rvq {
 namespace {
 
 constexpr int kHistLdsMaxK = 16384;  // LDS counters: K * 4 bytes <= 64 KB
+// All levels in one workgroup: L * K 16-bit counters, two to a 32-bit LDS
+// word (128 KB), over chunks of at most 65535 rows so no counter overflows.
+constexpr int kHistPackedMaxLK = 65536;
+constexpr int64_t kHistPackedRows = 65535;
+
+int64_t hist_packed_chunks(int64_t n) {
+  int64_t c = ceil_div(n, 512);   // at least 512 rows per workgroup
+  if (c > 256) c = 256;           // about one workgroup per compute unit
+  const int64_t need = ceil_div(n, kHistPackedRows);
+  if (c < need) c = need;
+  if (c < 1) c = 1;
+  return c;
+}
 
 int64_t hist_chunks(int64_t n, int L) {
   int64_t c = ceil_div(n, 8192);
@@ -68,6 +81,96 @@ __global__ __launch_bounds__(256) void hist_partial_kernel(const int32_t *__rest
   for (int k = threadIdx.x; k < K; k += 256) dst[k] = cnt[k];
 }
 
+// Workgroup per chunk of rows, every level: the chunk's IDs are read once,
+// contiguously, and counted in 16-bit LDS counters of (level, codeword);
+// partial[chunk] receives the counter words as they are.  The counters take
+// 128 KB, so one workgroup fills a compute unit: 16 waves, each thread
+// with eight loads in flight before its atomics.
+constexpr int kHistPackedThreads = 1024;
+__global__ __launch_bounds__(kHistPackedThreads) void hist_packed_kernel(
+    const int32_t *__restrict__ ids, int64_t n, int L, int K, int64_t rows_per_chunk,
+    uint32_t *__restrict__ partial, uint32_t *__restrict__ bad) {
+  constexpr int T = kHistPackedThreads, U = 8;
+  __shared__ uint32_t cnt[kHistPackedMaxLK / 2];
+  const int words = (L * K + 1) >> 1;
+  for (int w = threadIdx.x; w < words; w += T) cnt[w] = 0;
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_chunk;
+  int64_t r1 = r0 + rows_per_chunk;
+  if (r1 > n) r1 = n;
+  const int32_t *src = ids + r0 * L;
+  // (rows_per_chunk * L < 2^32 - 2^16: at most 65535 rows and L <= 65536)
+  const uint32_t count = r1 > r0 ? (uint32_t)((r1 - r0) * L) : 0u;
+  uint32_t nbad = 0;
+  // the level of element e is e % L, carried along as e steps by T
+  const uint32_t step = (uint32_t)T % (uint32_t)L;
+  uint32_t l = threadIdx.x % (uint32_t)L;
+  for (uint32_t base = threadIdx.x; base < count; base += T * U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = base + u * T < count ? src[base + u * T] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + u * T < count) {
+        if (v[u] >= 0 && v[u] < K) {
+          const uint32_t c = l * (uint32_t)K + (uint32_t)v[u];
+          atomicAdd(&cnt[c >> 1], 1u << ((c & 1u) << 4));
+        } else {
+          ++nbad;
+        }
+      }
+      l += step;
+      if (l >= (uint32_t)L) l -= (uint32_t)L;
+    }
+  }
+  if (bad) {
+    const unsigned long long m = __ballot(nbad != 0);
+    if (m) {
+      uint32_t t = nbad;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+      if ((threadIdx.x & 63) == 0) atomicAdd(bad, t);
+    }
+  }
+  __syncthreads();
+  uint32_t *dst = partial + (int64_t)blockIdx.x * words;
+  for (int w = threadIdx.x; w < words; w += T) dst[w] = cnt[w];
+}
+
+// hist[l][k] = sum over chunks of the 16-bit counter (l, k) of partial[chunk].
+// A workgroup takes 16 counter words (32 counters): thread (g, w) sums word
+// w of chunks g, g + 16, ..., then the 16 partial sums of each word are
+// added in LDS (integers: the order does not matter).
+__global__ __launch_bounds__(256) void hist_packed_reduce_kernel(
+    const uint32_t *__restrict__ partial, int64_t chunks, int L, int K,
+    int64_t *__restrict__ hist) {
+  __shared__ int64_t lo_sum[16][16], hi_sum[16][16];
+  const int wl = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int64_t lk = (int64_t)L * K;
+  const int64_t words = (lk + 1) >> 1;
+  const int64_t w = (int64_t)blockIdx.x * 16 + wl;
+  int64_t lo = 0, hi = 0;
+  if (w < words) {
+#pragma unroll 8
+    for (int64_t c = g; c < chunks; c += 16) {
+      const uint32_t v = partial[c * words + w];
+      lo += v & 0xffffu;
+      hi += v >> 16;
+    }
+  }
+  lo_sum[g][wl] = lo;
+  hi_sum[g][wl] = hi;
+  __syncthreads();
+  if (g == 0 && w < words) {
+    for (int j = 1; j < 16; ++j) {
+      lo += lo_sum[j][wl];
+      hi += hi_sum[j][wl];
+    }
+    hist[2 * w] = lo;
+    if (2 * w + 1 < lk) hist[2 * w + 1] = hi;
+  }
+}
+
 // hist[l][k] = sum over chunks of partial[chunk][l][k], chunks in order.
 __global__ __launch_bounds__(256) void hist_reduce_kernel(const uint32_t *__restrict__ partial,
                                                           int64_t chunks, int L, int K,
@@ -100,6 +203,8 @@ __global__ __launch_bounds__(256) void hist_atomic_kernel(const int32_t *__restr
 }
 
 size_t hist_partial_bytes(int64_t n, int L, int K) {
+  if ((int64_t)L * K <= kHistPackedMaxLK)
+    return (size_t)hist_packed_chunks(n) * (size_t)(((int64_t)L * K + 1) >> 1) * sizeof(uint32_t);
   if (K > kHistLdsMaxK) return 0;
   return (size_t)hist_chunks(n, L) * (size_t)L * (size_t)K * sizeof(uint32_t);
 }
@@ -107,7 +212,14 @@ size_t hist_partial_bytes(int64_t n, int L, int K) {
 hipError_t launch_hist(const int32_t *ids, int64_t n, int L, int K, int64_t *hist,
                        uint32_t *partial, uint32_t *bad, hipStream_t s) {
   const int64_t lk = (int64_t)L * K;
-  if (K <= kHistLdsMaxK) {
+  if (lk <= kHistPackedMaxLK) {
+    const int64_t chunks = hist_packed_chunks(n);
+    const int64_t rpc = ceil_div(n > 0 ? n : 1, chunks);
+    hist_packed_kernel<<<dim3((unsigned)chunks), dim3(kHistPackedThreads), 0, s>>>(
+        ids, n, L, K, rpc, partial, bad);
+    hist_packed_reduce_kernel<<<dim3((unsigned)ceil_div((lk + 1) >> 1, 16)), dim3(256), 0, s>>>(
+        partial, chunks, L, K, hist);
+  } else if (K <= kHistLdsMaxK) {
     const int64_t chunks = hist_chunks(n, L);
     const int64_t rpc = ceil_div(n > 0 ? n : 1, chunks);
     hist_partial_kernel<<<dim3((unsigned)(chunks * L)), dim3(256), (size_t)K * sizeof(uint32_t), s>>>(

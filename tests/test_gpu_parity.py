@@ -240,6 +240,41 @@ def test_invalid_ids_are_counted_and_skipped(rvq, dev):
     np.testing.assert_array_equal(hist.cpu().numpy(), want)
 
 
+HIST = [
+    # n, L, K, kind.  L*K <= 65536: every level in one workgroup's 16-bit LDS
+    # counters (several chunks, a hot codeword; an odd L*K); L*K > 65536 with
+    # K <= 16384: per-level LDS counters; K > 16384: global atomics.  The
+    # last case is 257 chunks of exactly 65535 rows with one ID everywhere,
+    # so a 16-bit counter reaches its largest value.
+    (70000, 8, 8192, "hot"),
+    (5, 3, 7, "random"),
+    (3000, 8, 16384, "random"),
+    (3000, 2, 40000, "random"),
+    (65535 * 257, 1, 2, "zeros"),
+]
+
+
+@pytest.mark.parametrize("case", HIST, ids=lambda c: f"n{c[0]}_L{c[1]}_K{c[2]}_{c[3]}")
+def test_histogram_paths(rvq, dev, case):
+    n, L, K, kind = case
+    g = np.random.default_rng(n + 7 * L + K)
+    if kind == "zeros":
+        ids_h = np.zeros((n, L), dtype=np.int32)
+    else:
+        ids_h = g.integers(0, K, size=(n, L)).astype(np.int32)
+        if kind == "hot":
+            ids_h[g.random(n) < 0.1] = 0
+        ids_h[0, L - 1] = -1
+        ids_h[n - 1, 0] = K
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    hist, _ = rvq.rvq_level_stats(torch.from_numpy(ids_h).to(dev), K, bad_ids=bad)
+    torch.cuda.synchronize()
+    ok = (ids_h >= 0) & (ids_h < K)
+    want = np.stack([np.bincount(ids_h[ok[:, l], l], minlength=K) for l in range(L)])
+    np.testing.assert_array_equal(hist.cpu().numpy(), want)
+    assert int(bad.item()) == int((~ok).sum())
+
+
 @pytest.mark.parametrize("d,x_dtype", [(36, "f32"), (37, "f32"), (40, "bf16")])
 def test_invalid_ids_with_msr_are_counted_once(rvq, dev, d, x_dtype):
     # d = 36 and 40 take the float4 path, d = 37 the scalar one; an invalid ID
