@@ -226,6 +226,15 @@ def secondary(torch, rvq, workloads, dev) -> dict:
     return out
 
 
+def copy_calibration(torch, dev, mib: int) -> None:
+    """One plain elementwise copy that reads and writes mib MiB: the dispatch
+    that calibrates the HBM byte counters."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize(dev)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +244,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the single-image, decode-heavy and bulk-tokenisation measurements")
+    ap.add_argument("--secondary-only", action="store_true",
+                    help="run only the secondary measurements (no timed step, no oracle "
+                         "baseline) and print them as one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain copy of this many MiB "
                          "(the calibration dispatch for HBM byte counters)")
@@ -251,6 +263,12 @@ def main() -> int:
     import workloads
 
     dev = torch.device("cuda:0")
+    if args.secondary_only:
+        rec = {"secondary": secondary(torch, rvq, workloads, dev)}
+        if args.copy_mib > 0:
+            copy_calibration(torch, dev, args.copy_mib)
+        print(json.dumps(rec), flush=True)
+        return 0
     w = workloads.native_batch()
     N, D, L, K = w.N, w.D, w.L, w.K
     x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -344,11 +362,7 @@ def main() -> int:
         torch.cuda.empty_cache()
         rec["secondary"] = secondary(torch, rvq, workloads, dev)
     if args.copy_mib > 0:
-        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize(dev)
-        del src, dst
+        copy_calibration(torch, dev, args.copy_mib)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
