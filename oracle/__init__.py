@@ -37,8 +37,10 @@ _lib: Optional[ctypes.CDLL] = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc (no fast-math, no FP contraction)."""
-    if force or not os.path.exists(_LIB):
+    """Compile the C oracle with gcc (no fast-math, no FP contraction); with
+    force=False only when the library is missing or older than its source."""
+    stale = not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    if force or stale:
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
                "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
@@ -57,8 +59,9 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.rvq_oracle_hist.argtypes = [p, i64, i32, i32, p]
     lib.rvq_oracle_row_sq_residual.argtypes = [p, p, i64, i32, p, i32, i32, p, i32]
     lib.rvq_oracle_teacher_forced.argtypes = [p, p, i64, i32, p, i32, i32, p, p, i32]
+    lib.rvq_oracle_embed.argtypes = [p, p, i64, i32, p, i64, p, i32, i32, p, i32]
     for f in ("rvq_oracle_encode", "rvq_oracle_decode", "rvq_oracle_hist",
-              "rvq_oracle_row_sq_residual", "rvq_oracle_teacher_forced"):
+              "rvq_oracle_row_sq_residual", "rvq_oracle_teacher_forced", "rvq_oracle_embed"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -132,6 +135,30 @@ def decode(ids: np.ndarray, codebooks: np.ndarray, levels: Optional[int] = None,
     out = np.empty((n, d), dtype=np.float64)
     _check(lib.rvq_oracle_decode(_ptr(ids), n, _ptr(cb), L, K, d, levels, _ptr(out),
                                  int(threads)), "decode")
+    return out
+
+
+def embed(ids: np.ndarray, level_tables: np.ndarray, is_visual: Optional[np.ndarray] = None,
+          text_table: Optional[np.ndarray] = None, table_dtype: str = "f32",
+          threads: int = 0) -> np.ndarray:
+    """fp64 token embeddings [T, D] of a mixed sequence: a visual token sums
+    its level rows in level order, a text token is row ids[t, 0] of the text
+    table.  Tables are fp32, or bf16 bit patterns with table_dtype="bf16"."""
+    lib = _load()
+    vis = as_f64(level_tables, table_dtype)
+    L, K, D = vis.shape
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    if ids.ndim != 2 or ids.shape[1] != L:
+        raise ValueError("ids must be [T, L]")
+    T = ids.shape[0]
+    flags = None if is_visual is None else np.ascontiguousarray(is_visual, dtype=np.uint8)
+    txt = None if text_table is None else as_f64(text_table, table_dtype)
+    V = 0 if txt is None else txt.shape[0]
+    if txt is not None and txt.shape[1] != D:
+        raise ValueError("text table width differs from the level tables'")
+    out = np.empty((T, D), dtype=np.float64)
+    _check(lib.rvq_oracle_embed(_ptr(ids), _ptr(flags), T, L, _ptr(txt), V, _ptr(vis), K, D,
+                                _ptr(out), int(threads)), "embed")
     return out
 
 

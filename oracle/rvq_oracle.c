@@ -156,6 +156,49 @@ int rvq_oracle_decode(const int32_t *ids, int64_t n, const double *cb,
     return ORACLE_OK;
 }
 
+/*
+ * Unified token embedding of a mixed sequence ("LongCat-2.5 Native
+ * Multimodality for Agentic Tasks", section "Visual Primitive Modeling":
+ * visual tokens are multi-level discrete tokens handled in one token format
+ * with text, and the visual codebook embeddings are learned with the
+ * backbone).  A visual token t takes the sum over levels, in level order,
+ * of row ids[t][l] of level l's embedding table vis[L][K][D]; a text token
+ * takes row ids[t][0] of text[V][D] (ids[t][1..L-1] unused).  is_visual
+ * may be null: every token is visual.  Returns ORACLE_ERR_ARG on an ID out
+ * of range.
+ */
+int rvq_oracle_embed(const int32_t *ids, const uint8_t *is_visual, int64_t T, int32_t L,
+                     const double *text, int64_t V, const double *vis, int32_t K, int32_t D,
+                     double *out, int32_t threads)
+{
+    if (bad_shape(T, D, L, K) || V < 0) return ORACLE_ERR_ARG;
+    if (T > 0 && (!ids || !vis || !out)) return ORACLE_ERR_ARG;
+    for (int64_t t = 0; t < T; ++t) {
+        if (is_visual && !is_visual[t]) {
+            if (ids[t * L] < 0 || (int64_t)ids[t * L] >= V || !text) return ORACLE_ERR_ARG;
+        } else {
+            for (int32_t l = 0; l < L; ++l)
+                if (ids[t * L + l] < 0 || ids[t * L + l] >= K) return ORACLE_ERR_ARG;
+        }
+    }
+    if (threads < 1) threads = omp_get_max_threads();
+#pragma omp parallel for num_threads(threads) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double *o = out + t * D;
+        if (is_visual && !is_visual[t]) {
+            const double *e = text + (int64_t)ids[t * L] * D;
+            for (int32_t i = 0; i < D; ++i) o[i] = e[i];
+        } else {
+            for (int32_t i = 0; i < D; ++i) o[i] = 0.0;
+            for (int32_t l = 0; l < L; ++l) {
+                const double *e = vis + ((int64_t)l * K + ids[t * L + l]) * D;
+                for (int32_t i = 0; i < D; ++i) o[i] = o[i] + e[i];
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Per-level usage counts: hist[l][k] = #{n : ids[n][l] == k}. */
 int rvq_oracle_hist(const int32_t *ids, int64_t n, int32_t L, int32_t K, int64_t *hist)
 {

@@ -170,6 +170,48 @@ def test_decode_matches_torch_embedding_bag():
     np.testing.assert_array_equal(oracle.decode(ids, cb, levels=1), cb[0][ids[:, 0]].astype(np.float64))
 
 
+def test_embed_hand_worked_example():
+    # level tables and a text table of small integers; the expected rows are
+    # worked by hand: text -> the text row of ids[t, 0]; visual -> level-0 row
+    # of ids[t, 0] plus level-1 row of ids[t, 1]
+    vis = np.array([[[1, 2], [3, 4], [5, 6]], [[10, 20], [30, 40], [50, 60]]], dtype=np.float32)
+    text = np.array([[100, 200], [300, 400]], dtype=np.float32)
+    ids = np.array([[1, 0], [2, 0], [0, 2], [0, 2]], dtype=np.int32)
+    flags = np.array([0, 1, 1, 0], dtype=np.uint8)
+    want = np.array([[300, 400], [15, 26], [51, 62], [100, 200]], dtype=np.float64)
+    np.testing.assert_array_equal(oracle.embed(ids, vis, flags, text), want)
+
+
+def test_embed_visual_tokens_equal_decode():
+    # a visual token's embedding is the decode of its IDs with the level
+    # tables as codebooks (the decode is pinned against torch's embedding bag)
+    rng = np.random.default_rng(10)
+    L, K, D, T = 4, 19, 12, 50
+    vis = rng.standard_normal((L, K, D)).astype(np.float32)
+    ids = rng.integers(0, K, size=(T, L)).astype(np.int32)
+    np.testing.assert_array_equal(oracle.embed(ids, vis), oracle.decode(ids, vis))
+    np.testing.assert_array_equal(oracle.embed(ids, vis, np.ones(T, dtype=np.uint8)),
+                                  oracle.decode(ids, vis))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_embed_text_tokens_are_table_rows(dtype):
+    rng = np.random.default_rng(11)
+    L, K, D, V, T = 3, 7, 10, 23, 40
+    vis = rng.standard_normal((L, K, D)).astype(np.float32)
+    text = rng.standard_normal((V, D)).astype(np.float32)
+    if dtype == "bf16":
+        vis, text = workloads.bf16_bits_from_f32(vis), workloads.bf16_bits_from_f32(text)
+    ids = rng.integers(0, K, size=(T, L)).astype(np.int32)
+    flags = (rng.random(T) < 0.5).astype(np.uint8)
+    ids[flags == 0, 0] = rng.integers(0, V, size=int((flags == 0).sum()))
+    got = oracle.embed(ids, vis, flags, text, table_dtype=dtype)
+    t64, v64 = oracle.as_f64(text, dtype), oracle.as_f64(vis, dtype)
+    np.testing.assert_array_equal(got[flags == 0], t64[ids[flags == 0, 0]])
+    vsum = sum(v64[l][ids[flags == 1, l]] for l in range(L))
+    np.testing.assert_allclose(got[flags == 1], vsum, rtol=1e-15, atol=1e-15)
+
+
 def test_residual_equals_input_minus_reconstruction():
     w = workloads.random_problem(21, n=40, d=48, L=6, K=64)
     out = oracle.encode(w.x, w.codebooks)

@@ -24,6 +24,14 @@ MUTANTS = {
     "decode_transposed_ids": ("((int64_t)l * K + ids[row * L + l]) * d;\n            for (int32_t i = 0; i < d; ++i) o[i]",
                               "((int64_t)l * K + ids[l * n + row]) * d;\n            for (int32_t i = 0; i < d; ++i) o[i]"),
     "hist_transposed": ("hist[(int64_t)l * K + id] += 1;", "hist[(int64_t)id * L + l] += 1;"),
+    "embed_text_from_level_table": ("const double *e = text + (int64_t)ids[t * L] * D;",
+                                    "const double *e = vis + (int64_t)ids[t * L] * D;"),
+    "embed_text_last_id": ("const double *e = text + (int64_t)ids[t * L] * D;",
+                           "const double *e = text + (int64_t)ids[t * L + L - 1] * D;"),
+    "embed_level_stride": ("const double *e = vis + ((int64_t)l * K + ids[t * L + l]) * D;",
+                           "const double *e = vis + ((int64_t)l + ids[t * L + l]) * D;"),
+    "embed_drops_first_level": ("            for (int32_t l = 0; l < L; ++l) {\n                const double *e = vis",
+                                "            for (int32_t l = 1; l < L; ++l) {\n                const double *e = vis"),
     "msr_skips_level": ("for (int32_t i = 0; i < d; ++i) r[i] = r[i] - c[i];\n                    ms[row * L + l]",
                         "if (l) for (int32_t i = 0; i < d; ++i) r[i] = r[i] - c[i];\n                    ms[row * L + l]"),
 }
@@ -41,6 +49,10 @@ PIN_FUNCS = [
     pins.test_hist_matches_bincount,
     pins.test_msr_is_mean_squared_error_of_prefix_reconstruction,
     pins.test_teacher_forced_excess,
+    pins.test_embed_hand_worked_example,
+    pins.test_embed_visual_tokens_equal_decode,
+    lambda: pins.test_embed_text_tokens_are_table_rows("f32"),
+    lambda: pins.test_embed_text_tokens_are_table_rows("bf16"),
 ] + [(lambda c=c: pins.test_matches_exact_rational_greedy(c)) for c in pins._tiny_problems()]
 
 
