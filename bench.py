@@ -156,8 +156,10 @@ def secondary(torch, rvq, workloads, dev) -> dict:
     part of the step above): the single 32x32 image (1024 rows, K=4096, the
     small-batch encoder mode), the decode-heavy workload (4,194,304 x 8 IDs
     decoded to bf16; counts over them; mean squared residual of a
-    65,536-row fp32 subset encoded at L=8), and the offline bulk tokenisation
-    (1,048,576 bf16 rows of width 1280, L=16, K=16384; encode only)."""
+    65,536-row fp32 subset encoded at L=8), the unified token embedding of a
+    mixed text / visual sequence (about 40K tokens, bf16 tables of width
+    4096), and the offline bulk tokenisation (1,048,576 bf16 rows of width
+    1280, L=16, K=16384; encode only)."""
     import numpy as np
     out = {}
     w = workloads.single_image()
@@ -207,6 +209,29 @@ def secondary(torch, rvq, workloads, dev) -> dict:
     out["decode_heavy_msr"] = {"N": w.N, "L": L, "D": w.D, "ms": round(ms, 4),
                                "gather_counted_GBps": round(gathered / (ms * 1e-3) / 1e9, 1)}
     del xs, sids, ws2, ws, ids, cb
+    # unified token embedding of a mixed text / visual sequence (bf16 tables)
+    m = workloads.mixed_sequence()
+    T, L = m.ids.shape
+    Dm = m.level_tables.shape[2]
+    ids = torch.from_numpy(m.ids).to(dev)
+    vis = torch.from_numpy(m.is_visual).to(dev)
+    ttab = torch.from_numpy(m.text_table.view(np.int16)).view(torch.bfloat16).to(dev)
+    ltab = torch.from_numpy(m.level_tables.view(np.int16)).view(torch.bfloat16).to(dev)
+    emb = torch.empty((T, Dm), dtype=torch.bfloat16, device=dev)
+    rvq.rvq_embed_tokens(ids, ltab, vis, ttab, torch.bfloat16, out=emb)
+    torch.cuda.synchronize(dev)
+    ms = _time_ms(torch, lambda: rvq.rvq_embed_tokens(ids, ltab, vis, ttab, torch.bfloat16,
+                                                       out=emb), 10)
+    nv = int(m.is_visual.sum())
+    # IDs and flags read, every gathered table row, the output written
+    counted = T * (4 * L + 1) + (nv * L + (T - nv)) * 2 * Dm + T * 2 * Dm
+    out["embed_mixed_sequence"] = {
+        "T": T, "visual": nv, "text": T - nv, "L": L, "K": m.level_tables.shape[1],
+        "V": m.text_table.shape[0], "D_model": Dm, "tables": "bf16", "out": "bf16",
+        "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "gather_counted_GBps": round(counted / (ms * 1e-3) / 1e9, 1),
+        "gather_counted_frac_8TBps": round(counted / (ms * 1e-3) / 8e12, 4)}
+    del ids, vis, ttab, ltab, emb
     # offline bulk tokenisation, encode only, at full size
     w = workloads.bulk_tokenisation()
     x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -243,7 +268,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the single-image, decode-heavy and bulk-tokenisation measurements")
+                    help="skip the secondary measurements (single image, decode-heavy, embedding, bulk)")
     ap.add_argument("--secondary-only", action="store_true",
                     help="run only the secondary measurements (no timed step, no oracle "
                          "baseline) and print them as one JSON line")

@@ -217,6 +217,40 @@ rvq_status rvq_decode_level_stats(const int32_t *ids, int64_t n, const float *co
                                   uint32_t *bad_ids, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Unified token embedding of a mixed text / visual sequence.
+ *
+ * Visual signals are multi-level discrete tokens that the backbone takes in
+ * the same token format as text, and the visual codebook embeddings are
+ * learned jointly with the backbone ("LongCat-2.5 Native Multimodality for
+ * Agentic Tasks", section "Visual Primitive Modeling", paragraph "Native
+ * Visual Representation").  Token t of a sequence of T tokens becomes one
+ * row of D values:
+ *   visual token: out[t] = sum over l of level_tables[l][ids[t][l]], added
+ *                 in fp32 in level order (bit for bit rvq_decode's sum when
+ *                 the tables are fp32); an out-of-range ID adds nothing;
+ *   text token:   out[t] = text_table[ids[t][0]] (ids[t][1..L-1] are not
+ *                 read); an out-of-range ID gives a row of zeros.
+ * bf16 outputs are the fp32 values rounded to nearest even.  Each
+ * out-of-range ID that is read is counted once in *bad_ids.
+ *
+ * ids          : device, [T][L] int32.
+ * is_visual    : device, [T] uint8, nonzero for a visual token; NULL means
+ *                every token is visual.
+ * text_table   : device, [V][D] in table_dtype, 16-byte aligned; may be NULL
+ *                when V == 0 (every text ID is then out of range).
+ * level_tables : device, [L][K][D] in table_dtype, 16-byte aligned.
+ * table_dtype  : RVQ_F32 or RVQ_BF16 (both tables).
+ * out          : device, [T][D] in out_dtype (RVQ_F32 or RVQ_BF16), 16-byte
+ *                aligned, fully overwritten.
+ * bad_ids      : device uint32 counter (added to), or NULL.
+ * Limits: 1 <= L <= 64 (RVQ_ERR_UNSUPPORTED above), K >= 1, D >= 1, V >= 0.
+ * ---------------------------------------------------------------------- */
+rvq_status rvq_embed_tokens(const int32_t *ids, const uint8_t *is_visual, int64_t T, int32_t L,
+                            const void *text_table, int64_t V, const void *level_tables,
+                            int32_t K, int32_t D, rvq_dtype table_dtype, void *out,
+                            rvq_dtype out_dtype, uint32_t *bad_ids, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ __all__ = [
     "RVQError", "library_path", "exported_symbols", "RVQ_F32", "RVQ_BF16",
     "rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size", "rvq_encode",
     "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_decode_level_stats",
-    "rvq_status_string",
+    "rvq_embed_tokens", "rvq_status_string",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -71,9 +71,11 @@ _lib.rvq_level_stats.argtypes = [_p, _i64, _i32, _i32, _p, _p, ctypes.c_int, _i3
                                  _p, _sz, _p]
 _lib.rvq_decode_level_stats.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _p, ctypes.c_int, _p, _p,
                                         ctypes.c_int, _p, _p, _p, _sz, _p]
+_lib.rvq_embed_tokens.argtypes = [_p, _p, _i64, _i32, _p, _i64, _p, _i32, _i32, ctypes.c_int,
+                                  _p, ctypes.c_int, _p, _p]
 for _f in ("rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size",
            "rvq_encode", "rvq_encode_profiled", "rvq_decode", "rvq_level_stats_workspace_size",
-           "rvq_level_stats", "rvq_decode_level_stats"):
+           "rvq_level_stats", "rvq_decode_level_stats", "rvq_embed_tokens"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -189,6 +191,42 @@ def rvq_decode(ids: torch.Tensor, codebooks: torch.Tensor, out_dtype: torch.dtyp
         out = torch.empty((n, d), dtype=out_dtype, device=ids.device)
     _check(_lib.rvq_decode(_ptr(ids), n, _ptr(codebooks), L, K, d, levels, _ptr(out),
                            _dtype_code(out.dtype), _ptr(bad_ids), _stream(ids.device)))
+    return out
+
+
+def rvq_embed_tokens(ids: torch.Tensor, level_tables: torch.Tensor,
+                     is_visual: Optional[torch.Tensor] = None,
+                     text_table: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.float32,
+                     bad_ids: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One embedding row per token of a mixed sequence: a visual token sums its
+    rows of the per-level tables [L, K, D], a text token (is_visual == 0) is
+    row ids[t, 0] of text_table [V, D].  Tables are float32 or bfloat16."""
+    _need_cuda("ids", ids)
+    _need_cuda("level_tables", level_tables)
+    L, K, D = level_tables.shape
+    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[1] != L:
+        raise ValueError("ids must be int32 [T, L]")
+    T = ids.shape[0]
+    tdt = _dtype_code(level_tables.dtype)
+    V = 0
+    if text_table is not None:
+        _need_cuda("text_table", text_table)
+        if text_table.dtype != level_tables.dtype or text_table.dim() != 2 or text_table.shape[1] != D:
+            raise ValueError("text_table must be [V, D] in the level tables' dtype")
+        V = text_table.shape[0]
+    if is_visual is not None:
+        _need_cuda("is_visual", is_visual)
+        if is_visual.dtype == torch.bool:
+            is_visual = is_visual.view(torch.uint8)
+        if is_visual.dtype != torch.uint8 or is_visual.shape != (T,):
+            raise ValueError("is_visual must be uint8 or bool [T]")
+    if out is None:
+        out = torch.empty((T, D), dtype=out_dtype, device=ids.device)
+    _check(_lib.rvq_embed_tokens(_ptr(ids), _ptr(is_visual), T, L, _ptr(text_table), V,
+                                 _ptr(level_tables), K, D, tdt, _ptr(out), _dtype_code(out.dtype),
+                                 _ptr(bad_ids), _stream(ids.device)))
     return out
 
 

@@ -150,6 +150,9 @@ struct EncodeArgs {
 hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a, hipEvent_t *events,
                          hipStream_t s);
 
+hipError_t launch_embed(const int32_t *ids, const uint8_t *is_visual, int64_t T, int L,
+                        const void *text, int64_t V, const void *vis, int K, int D, bool tab_bf16,
+                        void *out, bool out_bf16, uint32_t *bad, hipStream_t s);
 hipError_t launch_decode(const int32_t *ids, int64_t n, const float *cb, int L, int K, int d,
                          int levels, void *out, bool out_bf16, uint32_t *bad, hipStream_t s);
 size_t hist_partial_bytes(int64_t n, int L, int K);

@@ -267,6 +267,38 @@ rvq_status rvq_decode(const int32_t *ids, int64_t n, const float *codebooks, int
   return RVQ_OK;
 }
 
+rvq_status rvq_embed_tokens(const int32_t *ids, const uint8_t *is_visual, int64_t T, int32_t L,
+                            const void *text_table, int64_t V, const void *level_tables,
+                            int32_t K, int32_t D, rvq_dtype table_dtype, void *out,
+                            rvq_dtype out_dtype, uint32_t *bad_ids, hipStream_t stream) {
+  if (T < 0) return fail(RVQ_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %lld)", (long long)T);
+  if (L < 1 || K < 1 || D < 1 || V < 0)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "need L, K, D >= 1 and V >= 0 (got %d, %d, %d, %lld)",
+                L, K, D, (long long)V);
+  if (L > kMaxLevelsGather)
+    return fail(RVQ_ERR_UNSUPPORTED, "embedding supports L <= %d (got %d)", kMaxLevelsGather, L);
+  if (T > kMaxRows)
+    return fail(RVQ_ERR_UNSUPPORTED, "T above %lld tokens per call (got %lld)",
+                (long long)kMaxRows, (long long)T);
+  if (table_dtype != RVQ_F32 && table_dtype != RVQ_BF16)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown table_dtype %d", (int)table_dtype);
+  if (out_dtype != RVQ_F32 && out_dtype != RVQ_BF16)
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", (int)out_dtype);
+  RVQ_TRY(need(level_tables, "level_tables", 16));
+  if (V > 0) RVQ_TRY(need(text_table, "text_table", 16));
+  if (T > 0) {
+    RVQ_TRY(need(ids, "ids", 4));
+    RVQ_TRY(need(out, "out", 16));
+  }
+  if (bad_ids && !aligned(bad_ids, 4))
+    return fail(RVQ_ERR_INVALID_ARGUMENT, "bad_ids must be 4-byte aligned");
+  if (T == 0) return RVQ_OK;
+  HIP_TRY(launch_embed(ids, is_visual, T, L, V > 0 ? text_table : nullptr, V, level_tables, K, D,
+                       table_dtype == RVQ_BF16, out, out_dtype == RVQ_BF16, bad_ids, stream),
+          "embed_kernel launch");
+  return RVQ_OK;
+}
+
 rvq_status rvq_level_stats_workspace_size(int64_t n, int32_t L, int32_t K, int32_t d,
                                           int32_t with_msr, size_t *bytes) {
   RVQ_TRY(check_shape(n, with_msr ? d : 1, L, K));

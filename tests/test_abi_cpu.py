@@ -135,6 +135,30 @@ def test_prepare_rejects_small_buffer(rvq):
     assert lib.rvq_prepare_codebooks(None, 2, 3, 4, p(256), 1 << 20, None) == 1
 
 
+def test_embed_tokens_rejects_bad_arguments(rvq):
+    lib = rvq.raw_library()
+    p = ctypes.c_void_p
+    # (ids, is_visual, T, L, text, V, tables, K, D, table_dtype, out, out_dtype, bad, stream)
+    args = [p(256), None, 4, 2, p(256), 5, p(256), 3, 8, 0, p(256), 1, None, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.rvq_embed_tokens(*a)
+    assert call(a9=7) == 1                 # unknown table dtype
+    assert call(a11=4) == 1                # unknown out dtype
+    assert call(a3=0) == 1                 # L >= 1
+    assert call(a3=65) == 2                # L above the gather limit
+    assert call(a5=-1) == 1                # V >= 0
+    assert call(a4=None) == 1              # text table required when V > 0
+    assert call(a6=p(8)) == 1              # level tables misaligned
+    assert call(a10=None) == 1             # out required when T > 0
+    assert call(a12=p(2)) == 1             # bad_ids misaligned
+    assert call(a2=-1) == 1                # T >= 0
+    assert call(a2=0, a0=None, a10=None) == 0   # empty sequence: nothing to do
+    assert call(a2=0, a4=None, a5=0) == 0       # no text table with V == 0
+
+
 def test_decode_level_stats_rejects_bad_arguments(rvq):
     lib = rvq.raw_library()
     p = ctypes.c_void_p

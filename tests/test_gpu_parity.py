@@ -240,6 +240,85 @@ def test_invalid_ids_are_counted_and_skipped(rvq, dev):
     np.testing.assert_array_equal(hist.cpu().numpy(), want)
 
 
+EMBED = [
+    # T, L, K, D, V, table dtype, out dtype, share of text tokens: D a
+    # multiple of 8 (16-byte pieces) or not, L above 8 (two groups of level
+    # gathers), no text table at all
+    (3000, 8, 700, 264, 900, "f32", "f32", 0.3),
+    (1000, 3, 50, 37, 20, "bf16", "bf16", 0.5),
+    (2000, 16, 300, 1024, 5000, "bf16", "f32", 0.2),
+    (500, 1, 10, 64, 0, "f32", "bf16", 0.0),
+]
+
+
+@pytest.mark.parametrize("case", EMBED, ids=lambda c: f"T{c[0]}_L{c[1]}_K{c[2]}_D{c[3]}_V{c[4]}_{c[5]}_{c[6]}")
+def test_embed_tokens(rvq, dev, case):
+    T, L, K, D, V, tdt, odt, frac = case
+    g = np.random.default_rng(T + L + K + D)
+    vis = (0.5 * g.standard_normal((L, K, D))).astype(np.float32)
+    text = g.standard_normal((max(V, 1), D)).astype(np.float32)[:V]
+    conv = workloads.bf16_bits_from_f32 if tdt == "bf16" else (lambda a: a)
+    vis_h, text_h = conv(vis), conv(text)
+    ids = g.integers(0, K, size=(T, L)).astype(np.int32)
+    is_vis = (g.random(T) >= frac).astype(np.uint8)
+    txt = np.flatnonzero(is_vis == 0)
+    ids[txt, 0] = g.integers(0, max(V, 1), size=len(txt))
+    vrows = np.flatnonzero(is_vis)
+    ids[vrows[0], L - 1] = K
+    ids[vrows[-1], 0] = -1
+    if len(txt):
+        ids[txt[0], 0] = V
+        ids[txt[-1], 0] = -3
+
+    def dev_table(a):
+        if tdt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    vis_d = dev_table(vis_h)
+    text_d = dev_table(text_h) if V else None
+    flags_d = torch.from_numpy(is_vis.astype(bool)).to(dev) if frac > 0 else None
+    out_dt = torch.bfloat16 if odt == "bf16" else torch.float32
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = rvq.rvq_embed_tokens(ids_d, vis_d, flags_d, text_d, out_dtype=out_dt, bad_ids=bad)
+    torch.cuda.synchronize()
+
+    # expected: out-of-range IDs point at an appended zero row
+    vis_ok = (ids >= 0) & (ids < K)
+    text_ok = (ids[:, 0] >= 0) & (ids[:, 0] < V)
+    want_bad = int((~vis_ok[vrows]).sum()) + int((~text_ok[txt]).sum())
+    assert int(bad.item()) == want_bad
+    zero = np.zeros((1, D), dtype=vis_h.dtype)
+    vis_x = np.concatenate([vis_h, np.broadcast_to(zero, (L, 1, D))], axis=1)
+    text_x = np.concatenate([text_h, zero], axis=0)
+    ids_c = np.where(vis_ok, ids, K).astype(np.int32)
+    ids_c[txt, 0] = np.where(text_ok[txt], ids[txt, 0], V)
+    ref = oracle.embed(ids_c, vis_x, is_vis, text_x, table_dtype=tdt)
+    v64 = oracle.as_f64(vis_x, tdt)
+    abs_sum = np.zeros((T, D))
+    for l in range(L):
+        abs_sum[vrows] += np.abs(v64[l][ids_c[vrows, l]])
+    bound = max(L - 1, 0) * 2.0 ** -24 * abs_sum
+    if odt == "bf16":
+        got = oracle.widen_bf16(parity.bf16_tensor_bits(out)).astype(np.float64)
+        refr = oracle.round_to_bf16(ref)
+        np.testing.assert_array_equal(got[txt], refr[txt])      # text rows: one rounding
+        step = np.maximum(parity._bf16_step(refr), parity._bf16_step(got))
+        assert np.all(np.abs(got - refr) <= step + bound)
+    else:
+        got = out.cpu().numpy().astype(np.float64)
+        np.testing.assert_array_equal(got[txt], ref[txt])        # text rows: exact
+        assert np.all(np.abs(got - ref) <= bound)
+        if tdt == "f32":
+            # visual tokens: bit for bit the decode of the same IDs
+            dec = rvq.rvq_decode(ids_d[torch.from_numpy(vrows).to(dev)].contiguous(), vis_d)
+            torch.cuda.synchronize()
+            assert torch.equal(out[torch.from_numpy(vrows).to(dev)].view(torch.int32),
+                               dec.view(torch.int32))
+    empty = rvq.rvq_embed_tokens(ids_d[:0], vis_d, None, text_d, out_dtype=out_dt)
+    assert empty.shape == (0, D)
+
+
 HIST = [
     # n, L, K, kind.  L*K <= 65536: every level in one workgroup's 16-bit LDS
     # counters (several chunks, a hot codeword; an odd L*K); L*K > 65536 with

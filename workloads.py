@@ -37,6 +37,7 @@ __all__ = [
     "native_batch",
     "bulk_tokenisation",
     "decode_heavy",
+    "mixed_sequence",
     "random_problem",
     "WORKLOADS",
 ]
@@ -237,6 +238,52 @@ def decode_heavy(seed: int = 5, n_ids: int = 4_194_304, n_msr: int = 65_536) -> 
     ids[hot] = 0
     return Workload("decode_heavy", cb, x, "f32", ids=ids, out_dtype="bf16",
                     notes=f"ids {n_ids}x8 (10% hot rows at ID 0), msr subset {n_msr}x1152 fp32")
+
+
+@dataclasses.dataclass
+class MixedSequence:
+    """A mixed text / visual token sequence and its embedding tables (bf16
+    bit patterns): ids [T, L] int32, is_visual [T] uint8, text_table [V, D],
+    level_tables [L, K, D]."""
+    ids: np.ndarray
+    is_visual: np.ndarray
+    text_table: np.ndarray
+    level_tables: np.ndarray
+    notes: str = ""
+
+
+def mixed_sequence(seed: int = 6, d_model: int = 4096, vocab: int = 65536) -> MixedSequence:
+    """16 images as visual tokens (H and W in patches uniform on 14..84, as in
+    the native batch; L=8 level IDs uniform on 0..8191), each after a text
+    segment of 32..512 tokens (IDs uniform on 0..vocab-1); embedding tables
+    of width d_model, bf16 N(0, 0.02^2).  Draw order: tables (levels, then
+    text), image sizes, segment lengths, then IDs in sequence order."""
+    L, K = 8, 8192
+    g = _rng(seed)
+    level = np.empty((L, K, d_model), dtype=np.uint16)
+    for l in range(L):
+        level[l] = bf16_bits_from_f32((0.02 * g.standard_normal((K, d_model), dtype=np.float32)))
+    text = np.empty((vocab, d_model), dtype=np.uint16)
+    chunk = 8192
+    for s in range(0, vocab, chunk):
+        e = min(vocab, s + chunk)
+        text[s:e] = bf16_bits_from_f32(0.02 * g.standard_normal((e - s, d_model), dtype=np.float32))
+    sizes = g.integers(14, 85, size=(16, 2), dtype=np.int64)
+    counts = sizes[:, 0] * sizes[:, 1]
+    seg = g.integers(32, 513, size=16, dtype=np.int64)
+    T = int(seg.sum() + counts.sum())
+    ids = np.zeros((T, L), dtype=np.int32)
+    vis = np.zeros(T, dtype=np.uint8)
+    t = 0
+    for i in range(16):
+        ids[t:t + seg[i], 0] = g.integers(0, vocab, size=int(seg[i]))
+        t += int(seg[i])
+        ids[t:t + counts[i]] = g.integers(0, K, size=(int(counts[i]), L))
+        vis[t:t + counts[i]] = 1
+        t += int(counts[i])
+    return MixedSequence(ids, vis, text, level,
+                         notes=f"T={T} ({int(counts.sum())} visual, {int(seg.sum())} text), "
+                               f"L=8, K=8192, V={vocab}, D_model={d_model}, bf16 tables")
 
 
 def random_problem(seed: int, n: int, d: int, L: int, K: int, x_dtype: str = "f32",
