@@ -25,8 +25,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers named as device pointers are device memory owned by the
- *     caller (any allocator).  The library allocates no memory and keeps no
- *     global mutable state; scratch memory is a caller-provided workspace.
+ *     caller (any allocator).  The library allocates no device memory and
+ *     keeps no global mutable state; scratch memory is a caller-provided
+ *     workspace.  (The host-side ID cache uses short-lived host buffers, and
+ *     the streaming encoder creates and destroys its own copy streams and
+ *     events within the call.)
  *   - All arrays are dense and row-major.  Codebooks are [L][K][d] fp32;
  *     token IDs are [n][L] int32 (level-minor); rows are [n][d].
  *   - Work is enqueued on `stream` and the call returns without waiting.
@@ -250,6 +253,96 @@ rvq_status rvq_embed_tokens(const int32_t *ids, const uint8_t *is_visual, int64_
                             const void *text_table, int64_t V, const void *level_tables,
                             int32_t K, int32_t D, rvq_dtype table_dtype, void *out,
                             rvq_dtype out_dtype, uint32_t *bad_ids, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Resumable ID cache (host files).
+ *
+ * The visual tokenizer is fixed, so token IDs are computed ahead of time
+ * and cached offline ("LongCat-2.5 Native Multimodality for Agentic Tasks",
+ * paragraph "Offline Visual Preprocessing").  An ID cache file holds the
+ * IDs [n][L] of n rows in chunks of chunk_rows rows (the last chunk may be
+ * shorter), appended in chunk order, each with a CRC-32, so that an
+ * interrupted writer resumes after its last complete chunk.  Host code
+ * only: these calls make no HIP call and touch no device memory; each
+ * opens and closes the file.  Errors (bad arguments, I/O failure, a header
+ * that does not match) return RVQ_ERR_INVALID_ARGUMENT.
+ * ---------------------------------------------------------------------- */
+
+/* Creates the file (header only) when it does not exist.  Otherwise checks
+ * that its header matches (n, L, K, chunk_rows), cuts off a torn or corrupt
+ * tail, and reports in *chunks_done how many leading chunks it holds. */
+rvq_status rvq_idcache_resume(const char *path, int64_t n, int32_t L, int32_t K,
+                              int64_t chunk_rows, int64_t *chunks_done);
+
+/* Appends chunk `chunk`: its rows x L IDs from host memory.  The file must
+ * hold exactly chunks 0 .. chunk-1. */
+rvq_status rvq_idcache_append(const char *path, int64_t n, int32_t L, int32_t K,
+                              int64_t chunk_rows, int64_t chunk, const int32_t *ids);
+
+/* Reads the valid leading chunks into ids (host, [n][L]; the rows of
+ * missing chunks are left as they are) and reports their count. */
+rvq_status rvq_idcache_read(const char *path, int64_t n, int32_t L, int32_t K,
+                            int64_t chunk_rows, int32_t *ids, int64_t *chunks_done);
+
+/* ------------------------------------------------------------------------
+ * Streaming encode of host-resident rows (the offline tokenisation pass).
+ *
+ * Token IDs are computed ahead of training and cached ("LongCat-2.5 Native
+ * Multimodality for Agentic Tasks", paragraph "Offline Visual
+ * Preprocessing").  rvq_stream_encode encodes rows [0, n) of a host array
+ * in chunks of chunk_rows rows: while chunk c is encoded on `stream`, chunk
+ * c+1 is copied in and the IDs of chunk c-1 are copied out, each on a copy
+ * stream of its own that the call creates (default priority) and destroys,
+ * ordered by events.  The IDs are bit for bit those of one rvq_encode call
+ * over all n rows (the encoder is batch-invariant).  The call is
+ * synchronous: it returns when its chunks are done and every stream it used
+ * is idle.
+ * ---------------------------------------------------------------------- */
+
+/* Called on the calling thread once chunk `chunk` (rows row0 .. row0+rows-1)
+ * has its IDs in host memory at `ids` ([rows][L]).  A nonzero return stops
+ * the call after this chunk (which counts as done). */
+typedef int (*rvq_chunk_callback)(void *user, int64_t chunk, int64_t row0, int64_t rows,
+                                  const int32_t *ids);
+
+/* Device workspace bytes for rvq_stream_encode with chunks of chunk_rows rows:
+ * two row buffers, two ID buffers and rvq_encode's workspace. */
+rvq_status rvq_stream_workspace_size(int64_t chunk_rows, int32_t d, int32_t L, int32_t K,
+                                     size_t *bytes);
+
+/*
+ * x_host      : host, [n][d] rows (x_dtype).  Pinned memory (hipHostMalloc)
+ *               lets the copies overlap the encoder; pageable memory works,
+ *               with copies that may not overlap.
+ * codebooks, prepared, L, K : as for rvq_encode (device).
+ * ids_host    : host, [n][L] int32 output; chunks not run are left as they are.
+ * chunk_rows  : rows per chunk (>= 1); chunk c holds rows c*chunk_rows ...
+ * first_chunk : the first chunk to run (earlier ones are skipped: resume).
+ * max_chunks  : run at most this many chunks (<= 0: all that remain).
+ * on_chunk    : callback per finished chunk, or NULL; user is passed to it.
+ * workspace   : device, >= rvq_stream_workspace_size bytes, 256-byte aligned.
+ * stream      : the stream the encoder runs on; work the caller queued on it
+ *               before the call is done before the first copy.
+ * chunks_done : out: chunks 0 .. *chunks_done - 1 are done (those before
+ *               first_chunk included), also when an error is returned.
+ */
+rvq_status rvq_stream_encode(const void *x_host, rvq_dtype x_dtype, int64_t n, int32_t d,
+                             const float *codebooks, const void *prepared, int32_t L, int32_t K,
+                             int32_t *ids_host, int64_t chunk_rows, int64_t first_chunk,
+                             int64_t max_chunks, rvq_chunk_callback on_chunk, void *user,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream,
+                             int64_t *chunks_done);
+
+/* rvq_stream_encode into a resumable ID cache file: rvq_idcache_resume on
+ * `path`, then the chunks the file does not hold yet (at most max_chunks of
+ * them), each appended to the file as it finishes.  Rerun after an
+ * interruption to continue.  *chunks_done: the chunks the file holds. */
+rvq_status rvq_stream_encode_to_cache(const char *path, const void *x_host, rvq_dtype x_dtype,
+                                      int64_t n, int32_t d, const float *codebooks,
+                                      const void *prepared, int32_t L, int32_t K,
+                                      int32_t *ids_host, int64_t chunk_rows, int64_t max_chunks,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                      int64_t *chunks_done);
 
 #ifdef __cplusplus
 }

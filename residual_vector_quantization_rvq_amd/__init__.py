@@ -25,7 +25,9 @@ __all__ = [
     "RVQError", "library_path", "exported_symbols", "RVQ_F32", "RVQ_BF16",
     "rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size", "rvq_encode",
     "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_decode_level_stats",
-    "rvq_embed_tokens", "rvq_status_string",
+    "rvq_embed_tokens", "rvq_idcache_resume", "rvq_idcache_append", "rvq_idcache_read",
+    "rvq_stream_workspace_size", "rvq_stream_encode", "rvq_stream_encode_to_cache",
+    "rvq_status_string",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -73,9 +75,22 @@ _lib.rvq_decode_level_stats.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _p, ctyp
                                         ctypes.c_int, _p, _p, _p, _sz, _p]
 _lib.rvq_embed_tokens.argtypes = [_p, _p, _i64, _i32, _p, _i64, _p, _i32, _i32, ctypes.c_int,
                                   _p, ctypes.c_int, _p, _p]
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+_lib.rvq_idcache_resume.argtypes = [ctypes.c_char_p, _i64, _i32, _i32, _i64, _pi64]
+_lib.rvq_idcache_append.argtypes = [ctypes.c_char_p, _i64, _i32, _i32, _i64, _i64, _p]
+_lib.rvq_idcache_read.argtypes = [ctypes.c_char_p, _i64, _i32, _i32, _i64, _p, _pi64]
+_CHUNK_CB = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                             ctypes.c_int64, ctypes.c_void_p)
+_lib.rvq_stream_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _psz]
+_lib.rvq_stream_encode.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _i64,
+                                   _i64, _i64, _p, _p, _p, _sz, _p, _pi64]
+_lib.rvq_stream_encode_to_cache.argtypes = [ctypes.c_char_p, _p, ctypes.c_int, _i64, _i32, _p,
+                                            _p, _i32, _i32, _p, _i64, _i64, _p, _sz, _p, _pi64]
 for _f in ("rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size",
            "rvq_encode", "rvq_encode_profiled", "rvq_decode", "rvq_level_stats_workspace_size",
-           "rvq_level_stats", "rvq_decode_level_stats", "rvq_embed_tokens"):
+           "rvq_level_stats", "rvq_decode_level_stats", "rvq_embed_tokens", "rvq_idcache_resume",
+           "rvq_idcache_append", "rvq_idcache_read", "rvq_stream_workspace_size",
+           "rvq_stream_encode", "rvq_stream_encode_to_cache"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -228,6 +243,109 @@ def rvq_embed_tokens(ids: torch.Tensor, level_tables: torch.Tensor,
                                  _ptr(level_tables), K, D, tdt, _ptr(out), _dtype_code(out.dtype),
                                  _ptr(bad_ids), _stream(ids.device)))
     return out
+
+
+def rvq_idcache_resume(path: str, n: int, L: int, K: int, chunk_rows: int) -> int:
+    """Create the ID cache file, or check and trim an existing one; returns the
+    number of leading chunks it holds."""
+    done = ctypes.c_int64()
+    _check(_lib.rvq_idcache_resume(os.fsencode(path), n, L, K, chunk_rows, ctypes.byref(done)))
+    return done.value
+
+
+def rvq_idcache_append(path: str, n: int, L: int, K: int, chunk_rows: int, chunk: int,
+                       ids) -> None:
+    """Append chunk ``chunk``: a host int32 array (numpy or CPU tensor) of its
+    rows x L IDs."""
+    import numpy as np
+    a = np.ascontiguousarray(ids.numpy() if isinstance(ids, torch.Tensor) else ids, dtype=np.int32)
+    _check(_lib.rvq_idcache_append(os.fsencode(path), n, L, K, chunk_rows, chunk,
+                                   a.ctypes.data_as(ctypes.c_void_p)))
+
+
+def rvq_idcache_read(path: str, n: int, L: int, K: int, chunk_rows: int):
+    """(ids [n, L] int32 numpy array, number of valid leading chunks); rows of
+    missing chunks are -1."""
+    import numpy as np
+    ids = np.full((n, L), -1, dtype=np.int32)
+    done = ctypes.c_int64()
+    _check(_lib.rvq_idcache_read(os.fsencode(path), n, L, K, chunk_rows,
+                                 ids.ctypes.data_as(ctypes.c_void_p), ctypes.byref(done)))
+    return ids, done.value
+
+
+def rvq_stream_workspace_size(chunk_rows: int, d: int, L: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.rvq_stream_workspace_size(chunk_rows, d, L, K, ctypes.byref(out)))
+    return out.value
+
+
+def _stream_args(x_host: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
+                 chunk_rows: int, ids_out: Optional[torch.Tensor],
+                 workspace: Optional[torch.Tensor]):
+    if x_host.is_cuda or not x_host.is_contiguous() or x_host.dim() != 2:
+        raise ValueError("x_host must be a contiguous [n, d] host tensor")
+    _need_cuda("codebooks", codebooks)
+    _need_cuda("prepared", prepared)
+    L, K, d = codebooks.shape
+    n = x_host.shape[0]
+    if x_host.shape[1] != d:
+        raise ValueError("x_host width differs from the codebooks'")
+    if ids_out is None:
+        ids_out = torch.empty((n, L), dtype=torch.int32, pin_memory=x_host.is_pinned())
+    if ids_out.is_cuda or ids_out.dtype != torch.int32 or ids_out.shape != (n, L):
+        raise ValueError("ids_out must be a host int32 [n, L] tensor")
+    if workspace is None:
+        workspace = torch.empty(rvq_stream_workspace_size(chunk_rows, d, L, K),
+                                dtype=torch.uint8, device=codebooks.device)
+    return n, d, L, K, ids_out, workspace
+
+
+def rvq_stream_encode(x_host: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
+                      chunk_rows: int, ids_out: Optional[torch.Tensor] = None,
+                      first_chunk: int = 0, max_chunks: int = 0, on_chunk=None,
+                      workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, int]:
+    """Encode host rows chunk by chunk with overlapped copies; returns the host
+    IDs [n, L] and the number of chunks done.  on_chunk(chunk, row0, rows)
+    is called after each chunk's IDs are in ids; a true return stops."""
+    n, d, L, K, ids_out, workspace = _stream_args(x_host, codebooks, prepared, chunk_rows,
+                                                  ids_out, workspace)
+    errors = []
+
+    def relay(_user, chunk, row0, rows, _ids):
+        try:
+            return 1 if on_chunk(int(chunk), int(row0), int(rows)) else 0
+        except BaseException as e:  # an exception cannot cross the C frame
+            errors.append(e)
+            return 1
+    cb = _CHUNK_CB(relay) if on_chunk is not None else None
+    done = ctypes.c_int64()
+    _check(_lib.rvq_stream_encode(_ptr(x_host), _dtype_code(x_host.dtype), n, d, _ptr(codebooks),
+                                  _ptr(prepared), L, K, _ptr(ids_out), chunk_rows, first_chunk,
+                                  max_chunks, ctypes.cast(cb, ctypes.c_void_p) if cb else None,
+                                  None, _ptr(workspace), workspace.numel(),
+                                  _stream(codebooks.device), ctypes.byref(done)))
+    if errors:
+        raise errors[0]
+    return ids_out, done.value
+
+
+def rvq_stream_encode_to_cache(path: str, x_host: torch.Tensor, codebooks: torch.Tensor,
+                               prepared: torch.Tensor, chunk_rows: int,
+                               ids_out: Optional[torch.Tensor] = None, max_chunks: int = 0,
+                               workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, int]:
+    """rvq_stream_encode into the resumable ID cache at path (continues a
+    partial file); returns the host IDs of the chunks run and the number of
+    chunks the file holds."""
+    n, d, L, K, ids_out, workspace = _stream_args(x_host, codebooks, prepared, chunk_rows,
+                                                  ids_out, workspace)
+    done = ctypes.c_int64()
+    _check(_lib.rvq_stream_encode_to_cache(os.fsencode(path), _ptr(x_host),
+                                           _dtype_code(x_host.dtype), n, d, _ptr(codebooks),
+                                           _ptr(prepared), L, K, _ptr(ids_out), chunk_rows,
+                                           max_chunks, _ptr(workspace), workspace.numel(),
+                                           _stream(codebooks.device), ctypes.byref(done)))
+    return ids_out, done.value
 
 
 def rvq_level_stats_workspace_size(n: int, L: int, K: int, d: int, with_msr: bool) -> int:

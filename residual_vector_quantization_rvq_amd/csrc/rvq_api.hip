@@ -14,9 +14,12 @@
 using namespace rvq;
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
 
+namespace rvq {
+// Records the message that rvq_last_error returns (per thread) and returns
+// st; shared by the library's host sources.
 rvq_status fail(rvq_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 rvq_status fail(rvq_status st, const char *fmt, ...) {
   va_list ap;
@@ -25,6 +28,9 @@ rvq_status fail(rvq_status st, const char *fmt, ...) {
   va_end(ap);
   return st;
 }
+}  // namespace rvq
+
+namespace {
 
 rvq_status hip_fail(hipError_t e, const char *what) {
   return fail(RVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

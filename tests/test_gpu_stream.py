@@ -1,0 +1,83 @@
+"""The streaming encoder and the resumable ID cache on the GPU: chunked
+encoding of host rows gives bit for bit the IDs of one rvq_encode call (the
+encoder is batch-invariant, which test_gpu_parity checks against the oracle),
+and interrupted runs resume to the same result."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rvq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import residual_vector_quantization_rvq_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def problem(rvq):
+    # the native-resolution batch: 30,834 bf16 rows, L=8, K=8192
+    dev = torch.device("cuda:0")
+    w = workloads.native_batch()
+    x_host = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prepared = rvq.rvq_prepare_codebooks(cb)
+    ref = rvq.rvq_encode(x_host.to(dev), cb, prepared).cpu()
+    torch.cuda.synchronize()
+    return w, x_host, cb, prepared, ref
+
+
+@pytest.mark.parametrize("pinned,chunk", [(True, 5000), (False, 12000), (True, 40000)])
+def test_stream_encode_matches_one_call(rvq, problem, pinned, chunk):
+    w, x_host, cb, prepared, ref = problem
+    x = x_host.pin_memory() if pinned else x_host
+    seen = []
+    ids, done = rvq.rvq_stream_encode(x, cb, prepared, chunk,
+                                      on_chunk=lambda c, r0, r: seen.append((c, r0, r)))
+    nchunks = -(-w.N // chunk)
+    print(f"[stream] pinned={pinned} chunk={chunk}: {done} chunks")
+    assert done == nchunks
+    assert seen == [(c, c * chunk, min(chunk, w.N - c * chunk)) for c in range(nchunks)]
+    assert torch.equal(ids, ref)
+
+
+def test_stream_encode_stop_and_resume(rvq, problem):
+    w, x_host, cb, prepared, ref = problem
+    x = x_host.pin_memory()
+    chunk = 4000                          # 8 chunks, the last of 2834 rows
+    ids, done = rvq.rvq_stream_encode(x, cb, prepared, chunk, on_chunk=lambda c, r0, r: c == 2)
+    assert done == 3
+    assert torch.equal(ids[:3 * chunk], ref[:3 * chunk])
+    _, done = rvq.rvq_stream_encode(x, cb, prepared, chunk, ids_out=ids, first_chunk=3,
+                                    max_chunks=2)
+    assert done == 5
+    _, done = rvq.rvq_stream_encode(x, cb, prepared, chunk, ids_out=ids, first_chunk=5)
+    assert done == 8
+    assert torch.equal(ids, ref)
+
+
+def test_stream_encode_to_cache_resumes(rvq, problem, tmp_path):
+    w, x_host, cb, prepared, ref = problem
+    x = x_host.pin_memory()
+    chunk, L, K = 3000, w.L, w.K           # 11 chunks
+    path = str(tmp_path / "ids.rvq")
+    _, done = rvq.rvq_stream_encode_to_cache(path, x, cb, prepared, chunk, max_chunks=4)
+    assert done == 4
+    # a torn last record, as after a crash mid-write: that chunk is redone
+    with open(path, "r+b") as f:
+        f.truncate(os.path.getsize(path) - 100)
+    assert rvq.rvq_idcache_resume(path, w.N, L, K, chunk) == 3
+    _, done = rvq.rvq_stream_encode_to_cache(path, x, cb, prepared, chunk)
+    assert done == 11
+    got, done = rvq.rvq_idcache_read(path, w.N, L, K, chunk)
+    assert done == 11
+    np.testing.assert_array_equal(got, ref.numpy())
+    # nothing left to do
+    _, done = rvq.rvq_stream_encode_to_cache(path, x, cb, prepared, chunk)
+    assert done == 11
