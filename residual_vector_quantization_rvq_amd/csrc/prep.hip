@@ -32,27 +32,35 @@ __global__ __launch_bounds__(256) void prepare_tile_kernel(const float *__restri
   const bool vec = (d & 3) == 0;
   uint4 *tile = stream + ((int64_t)l * T + t) * (tile_bytes(S) / 16);
   float acc = 0.f;
-  for (int s = 0; s < S; ++s) {
+  // two stages (eight k-steps) per pass: all sixteen loads are issued before
+  // the first is used; the squares are still summed in feature order
+  for (int s0 = 0; s0 < S; s0 += 2) {
+    float v[8][8];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + (u >> 2), ks = u & 3;
       const int d0 = s * kStageCols + ks * 16 + h * 8;
-      float v[8];
-      if (real && vec && d0 + 8 <= d) {
+      if (s < S && real && vec && d0 + 8 <= d) {
         const float4 a = *reinterpret_cast<const float4 *>(src + d0);
         const float4 b = *reinterpret_cast<const float4 *>(src + d0 + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+        v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (real && d0 + e < d) ? src[d0 + e] : 0.f;
+        for (int e = 0; e < 8; ++e) v[u][e] = (s < S && real && d0 + e < d) ? src[d0 + e] : 0.f;
       }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + (u >> 2), ks = u & 3;
+      if (s >= S) break;
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        acc = fmaf(v[e], v[e], acc);
-        acc = fmaf(v[e + 1], v[e + 1], acc);
-        w[e >> 1] = (uint32_t)f32_to_bf16_bits(-2.0f * v[e]) |
-                    ((uint32_t)f32_to_bf16_bits(-2.0f * v[e + 1]) << 16);
+        acc = fmaf(v[u][e], v[u][e], acc);
+        acc = fmaf(v[u][e + 1], v[u][e + 1], acc);
+        w[e >> 1] = (uint32_t)f32_to_bf16_bits(-2.0f * v[u][e]) |
+                    ((uint32_t)f32_to_bf16_bits(-2.0f * v[u][e + 1]) << 16);
       }
       tile[256 + s * 1024 + (j * 4 + ks) * 64 + lane] = make_uint4(w[0], w[1], w[2], w[3]);
     }

@@ -240,6 +240,53 @@ def test_invalid_ids_are_counted_and_skipped(rvq, dev):
     np.testing.assert_array_equal(hist.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("d", [200, 70])
+def test_prepared_stream_layout(rvq, dev, d):
+    # The prepared stream holds, per level and 128-codeword tile, a norm
+    # k-step (per sub-tile j, lanes < 32: bf16 hi and lo of ||c||^2 of
+    # codeword j*32 + lane) and then, per stage of 64 features, 16 blocks
+    # (j, ks) in which lane L holds the bf16 of -2c for codeword j*32 + L%32,
+    # features s*64 + ks*16 + (L/32)*8 .. +7.  K = 300 pads the last tile;
+    # d = 200 pads k-steps (vector loads), d = 70 takes scalar loads.
+    L, K = 2, 300
+    Kp, T = 384, 3
+    S = -(-d // 64)
+    S = min(c for c in (1, 2, 4, 8, 12, 16, 18, 20) if c >= S)
+    g = np.random.default_rng(d)
+    cb = g.standard_normal((L, K, d)).astype(np.float32)
+    prep = rvq.rvq_prepare_codebooks(torch.from_numpy(cb).to(dev)).cpu().numpy()
+    al = lambda v: (v + 255) // 256 * 256
+    norms = prep[:L * Kp * 4].view(np.float32).reshape(L, Kp)
+    tb = 4096 + S * 16384
+    soff = al(L * Kp * 4)
+    stream = prep[soff:soff + L * T * tb].reshape(L, T, tb)
+    cpad = np.zeros((L, Kp, S * 64), dtype=np.float32)
+    cpad[:, :K, :d] = cb
+    want = workloads.bf16_bits_from_f32(-2.0 * cpad)          # exact scaling, one rounding
+    lane = np.arange(64)
+    for l in range(L):
+        for t in range(T):
+            blocks = stream[l, t, 4096:].view(np.uint16).reshape(S, 4, 4, 64, 8)  # s, j, ks, lane, e
+            for s_ in range(S):
+                for j in range(4):
+                    for ks in range(4):
+                        rows = t * 128 + j * 32 + lane % 32
+                        cols = s_ * 64 + ks * 16 + (lane // 32)[:, None] * 8 + np.arange(8)
+                        np.testing.assert_array_equal(blocks[s_, j, ks], want[l][rows[:, None], cols])
+            nb = stream[l, t, :4096].view(np.uint16).reshape(4, 64, 8)
+            assert (nb[:, 32:] == 0).all() and (nb[:, :32, 2:] == 0).all()
+            k = t * 128 + np.arange(128).reshape(4, 32)
+            nv = norms[l][k]
+            hi = workloads.bf16_bits_from_f32(nv)
+            np.testing.assert_array_equal(nb[:, :32, 0], hi)
+            lo = np.where(k < K, workloads.bf16_bits_from_f32(nv - workloads.f32_from_bf16_bits(hi)), 0)
+            np.testing.assert_array_equal(nb[:, :32, 1], lo)
+    real = np.arange(Kp) < K
+    exact = (cb.astype(np.float64) ** 2).sum(axis=2)
+    np.testing.assert_allclose(norms[:, real], exact, rtol=2e-6)
+    np.testing.assert_array_equal(norms[:, ~real], np.float32(3.0e38))
+
+
 EMBED = [
     # T, L, K, D, V, table dtype, out dtype, share of text tokens: D a
     # multiple of 8 (16-byte pieces) or not, L above 8 (two groups of level
