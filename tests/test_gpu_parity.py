@@ -516,6 +516,12 @@ FUSED = [
     (46, 20000, 700, 3, 1000, "f32"),
     (47, 20100, 512, 2, 100, "bf16"),
     (48, 19800, 1152, 1, 300, "bf16"),
+    # the other stage counts of the fused encoder: 1 (at the fused threshold,
+    # 154 row blocks), 2 (a k-step past the row), 4, 16 (K one past a tile)
+    (49, 19712, 64, 2, 300, "f32"),
+    (50, 20000, 100, 3, 200, "bf16"),
+    (51, 19800, 256, 2, 150, "f32"),
+    (52, 19750, 1000, 2, 129, "bf16"),
 ]
 
 
