@@ -159,6 +159,39 @@ def test_embed_tokens_rejects_bad_arguments(rvq):
     assert call(a2=0, a4=None, a5=0) == 0       # no text table with V == 0
 
 
+def test_stream_encode_rejects_bad_arguments(rvq):
+    lib = rvq.raw_library()
+    p = ctypes.c_void_p
+    done = ctypes.c_int64(-1)
+    need = ctypes.c_size_t()
+    assert lib.rvq_stream_workspace_size(1000, 64, 4, 256, ctypes.byref(need)) == 0
+    enc = ctypes.c_size_t()
+    assert lib.rvq_encode_workspace_size(1000, 64, 4, 256, ctypes.byref(enc)) == 0
+    al = lambda v: (v + 255) // 256 * 256
+    # two row buffers (4-byte features), two ID buffers, the encoder's workspace
+    assert need.value == 2 * al(1000 * 64 * 4) + 2 * al(1000 * 4 * 4) + enc.value
+    assert lib.rvq_stream_workspace_size(0, 64, 4, 256, ctypes.byref(need)) == 1
+    # (x, x_dtype, n, d, cb, prepared, L, K, ids, chunk_rows, first, max, cb, user, ws,
+    #  ws_bytes, stream, chunks_done)
+    args = [p(256), 0, 5000, 64, p(256), p(256), 4, 256, p(256), 1000, 0, 0, None, None,
+            p(256), 1 << 30, None, ctypes.byref(done)]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.rvq_stream_encode(*a)
+    assert call(a17=None) == 1             # chunks_done required
+    assert call(a1=7) == 1                 # unknown x dtype
+    assert call(a9=0) == 1                 # chunk_rows >= 1
+    assert call(a10=-1) == 1               # first_chunk >= 0
+    assert call(a0=None) == 1              # host rows required
+    assert call(a14=p(8)) == 1             # workspace misaligned
+    assert call(a15=1024) == 3             # workspace too small
+    assert call(a2=0) == 0 and done.value == 0          # nothing to do
+    assert call(a10=5) == 0 and done.value == 5         # every chunk already done
+    assert call(a10=9) == 0 and done.value == 5         # resume point past the end
+
+
 def test_decode_level_stats_rejects_bad_arguments(rvq):
     lib = rvq.raw_library()
     p = ctypes.c_void_p
