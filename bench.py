@@ -114,13 +114,13 @@ def cpu_baseline(w, target_s: float = 15.0) -> dict:
     threads = min(cores, env_threads) if env_threads > 0 else cores
     rng = np.random.default_rng(12345)
 
-    def run(rows):
+    def run(rows, nthreads=threads):
         sub = w.rows(np.sort(rng.choice(w.N, rows, replace=False)))
         t0 = time.perf_counter()
-        ref = oracle.encode(sub.x, sub.codebooks, x_dtype=sub.x_dtype, threads=threads)
-        oracle.decode(ref["ids"], sub.codebooks, threads=threads)
+        ref = oracle.encode(sub.x, sub.codebooks, x_dtype=sub.x_dtype, threads=nthreads)
+        oracle.decode(ref["ids"], sub.codebooks, threads=nthreads)
         oracle.hist(ref["ids"], sub.K)
-        oracle.msr(sub.x, ref["ids"], sub.codebooks, x_dtype=sub.x_dtype, threads=threads)
+        oracle.msr(sub.x, ref["ids"], sub.codebooks, x_dtype=sub.x_dtype, threads=nthreads)
         return time.perf_counter() - t0
 
     # two probes separate the per-row cost from the fixed cost of a call
@@ -132,9 +132,22 @@ def cpu_baseline(w, target_s: float = 15.0) -> dict:
     rows = int(min(16384, max(r2, (target_s - fixed) / per_row)))
     rows = max(threads, rows // threads * threads)
     t = run(rows)
+    # one thread, on about a quarter of one thread's share of that sample
+    rows1 = max(4, rows // threads // 4)
+    t1c = run(rows1, 1)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": rows / t, "unit": "vectors/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} seeded rows of the {w.N}-row native-resolution batch "
-                      f"(D={w.D}, K={w.K}, L={w.L}); fp64 encode+decode+counts+msr, {t:.1f} s"}
+                      f"(D={w.D}, K={w.K}, L={w.L}); fp64 encode+decode+counts+msr, {t:.1f} s",
+            "single_thread_value": round(rows1 / t1c, 2),
+            "single_thread_sample": f"{rows1} rows, {t1c:.1f} s",
+            "full_batch_s_extrapolated": round(w.N * t / rows, 1),
+            "cpu_model": model}
 
 
 def _time_ms(torch, fn, reps: int) -> float:
