@@ -190,7 +190,16 @@ def secondary(torch, rvq, workloads, dev) -> dict:
         "vectors_per_s": round(w.N / (ms * 1e-3), 1),
         "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
         "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    del x, cb, prep, ids, wsp
+    # ... then decoded back to fp32
+    rec = torch.empty((w.N, w.D), dtype=torch.float32, device=dev)
+    rvq.rvq_decode(ids, cb, torch.float32, out=rec)
+    torch.cuda.synchronize(dev)
+    ms = _time_ms(torch, lambda: rvq.rvq_decode(ids, cb, torch.float32, out=rec), 20)
+    gathered = w.N * (4 * w.L + 4 * w.L * w.D + 4 * w.D)
+    out["single_image_decode"] = {
+        "N": w.N, "L": w.L, "D": w.D, "out": "fp32", "ms": round(ms, 4),
+        "gather_counted_GBps": round(gathered / (ms * 1e-3) / 1e9, 1)}
+    del x, cb, prep, ids, wsp, rec
     w = workloads.decode_heavy()
     cb = torch.from_numpy(w.codebooks).to(dev)
     ids = torch.from_numpy(w.ids).to(dev)
