@@ -3,6 +3,7 @@ declared in include/rvq.h, sizes workspaces as documented and rejects bad
 arguments on the host before any HIP call."""
 import ctypes
 import os
+import subprocess
 
 import pytest
 
@@ -26,6 +27,29 @@ def test_exports_every_declared_symbol(rvq):
     lib = ctypes.CDLL(rvq.library_path())
     for name in names:
         assert hasattr(lib, name), f"{name} declared in rvq.h but not exported"
+
+
+def test_header_is_plain_c(rvq, tmp_path):
+    # a C11 program (gcc, no C++) includes rvq.h, links librvq.so and calls
+    # host-side entry points
+    src = tmp_path / "use.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"rvq.h\"\n"
+        "int main(void) {\n"
+        "  size_t b = 0;\n"
+        "  rvq_status st = rvq_prepared_size(1, 128, 640, &b);\n"
+        "  rvq_status bad = rvq_decode(NULL, 4, NULL, 2, 3, 4, 2, NULL, RVQ_F32, NULL, NULL);\n"
+        "  printf(\"%d %zu %d %s\\n\", (int)st, b, (int)bad, rvq_last_error());\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(rvq.library_path())
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src),
+                    "-L", libdir, "-lrvq", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    al = lambda v: (v + 255) // 256 * 256
+    assert out[0] == "0" and int(out[1]) == al(128 * 4) + al(4096 + 12 * 16384)
+    assert out[2] == "1" and "NULL" in " ".join(out[3:])
 
 
 def test_status_strings(rvq):
