@@ -114,13 +114,17 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
 rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K, size_t *bytes);
 
 /*
- * x            : device, [n][d] rows in x_dtype (fp32 or bf16), 16-byte aligned.
+ * x            : device, [n][d] rows in x_dtype (fp32 or bf16), aligned to
+ *                the element size; rows that do not start 16-byte aligned
+ *                (e.g. a slice of a larger batch) are first copied to the
+ *                workspace.
  * codebooks    : device, [L][K][d] fp32 (the exact values used for rescoring
  *                and for the residual update), 16-byte aligned.
  * prepared     : device, filled by rvq_prepare_codebooks for these codebooks.
  * ids          : device, [n][L] int32 output; ids[row*L + l] in [0, K).
  * residual_out : device, [n][d] fp32 output x - sum_l codebooks[l][ids[l]],
- *                or NULL when not wanted.  16-byte aligned.
+ *                or NULL when not wanted.  4-byte aligned (16-byte alignment
+ *                can save a final copy).
  * d            : 1..1280 (RVQ_ERR_UNSUPPORTED above: a row's features stay
  *                resident in registers during the sweep).  One level of
  *                codewords, K x (d rounded up to 16) fp32, must be below

@@ -118,11 +118,14 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   EncodeArgs a = a_in;
   const unsigned row_waves = (unsigned)ceil_div(a.n, 4);
   a.x16 = nullptr;
-  if (p.fused && a.x_bf16 && a.dp == a.d) {
+  // rows read with 16-byte accesses must start 16-byte aligned; others (a
+  // slice of a larger batch, say) go through the staging copy
+  const bool x_al = ((uintptr_t)a.x & 15) == 0;
+  if (p.fused && a.x_bf16 && a.dp == a.d && x_al) {
     // level 0 of the fused encoder reads the bf16 rows directly
     a.x16 = (const uint16_t *)a.x;
     a.src0 = nullptr;
-  } else if (a.x_bf16 || a.dp != a.d) {
+  } else if (a.x_bf16 || a.dp != a.d || !x_al) {
     stage_input_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(a.x, a.x_bf16, a.n, a.d, a.dp,
                                                            a.rbuf[0]);
     a.src0 = a.rbuf[0];
@@ -132,9 +135,10 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   // The last level reads rbuf[(L-1) & 1] and writes the final residual to
   // rbuf[L & 1]: fragment-major in fused mode (converted afterwards), rows of
   // stride dp in split mode (written straight to the caller's buffer when
-  // d == dp).
+  // d == dp and the buffer is 16-byte aligned).
   float *final_buf = a.rbuf[a.L & 1];
-  const bool convert = a.residual_out && (p.fused || a.dp != a.d);
+  const bool out_al = ((uintptr_t)a.residual_out & 15) == 0;
+  const bool convert = a.residual_out && (p.fused || a.dp != a.d || !out_al);
   a.res_final = convert ? final_buf : a.residual_out;
   if (!p.fused) {
     // every block a sweep workgroup reads (4 per 128 rows)

@@ -204,10 +204,10 @@ rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int3
   RVQ_TRY(need(codebooks, "codebooks", 16));
   RVQ_TRY(need(prepared, "prepared", 256));
   if (n > 0) {
-    RVQ_TRY(need(x, "x", 16));
+    RVQ_TRY(need(x, "x", x_dtype == RVQ_BF16 ? 2 : 4));
     RVQ_TRY(need(ids, "ids", 4));
-    if (residual_out && !aligned(residual_out, 16))
-      return fail(RVQ_ERR_INVALID_ARGUMENT, "residual_out must be 16-byte aligned");
+    if (residual_out && !aligned(residual_out, 4))
+      return fail(RVQ_ERR_INVALID_ARGUMENT, "residual_out must be 4-byte aligned");
   }
   const EncodeLayout wl = encode_layout(n, d, K);
   RVQ_TRY(need(workspace, "workspace", 256));

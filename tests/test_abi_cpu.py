@@ -122,11 +122,12 @@ def test_encode_rejects_bad_arguments_before_any_hip_call(rvq):
     # fake, never-dereferenced addresses: validation must fail first
     assert _call_encode(rvq, x_dtype=7) == 1
     assert _call_encode(rvq, x=0) == 1
-    assert _call_encode(rvq, x=8) == 1          # misaligned
+    assert _call_encode(rvq, x=258) == 1        # fp32 rows not 4-byte aligned
+    assert _call_encode(rvq, x=257, x_dtype=1) == 1   # bf16 rows not 2-byte aligned
     assert _call_encode(rvq, cb=0) == 1
     assert _call_encode(rvq, prep=128) == 1     # prepared must be 256-byte aligned
     assert _call_encode(rvq, ids=0) == 1
-    assert _call_encode(rvq, res=260) == 1      # residual_out misaligned
+    assert _call_encode(rvq, res=258) == 1      # residual_out not 4-byte aligned
     assert _call_encode(rvq, ws=0) == 1
     assert _call_encode(rvq, ws_bytes=10) == 3
     assert "workspace" in rvq.raw_library().rvq_last_error().decode()

@@ -485,6 +485,40 @@ def test_determinism_and_batch_invariance(rvq, dev):
     assert torch.equal(ids4, ids1[699:700])
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_unaligned_row_slices_encode_like_the_batch(rvq, dev, dt):
+    # row slices starting at any row (most not 16-byte aligned, d = 201):
+    # they go through the staging copy and give the batch's bits, in both
+    # encoder modes; a residual_out that is only 4-byte aligned too
+    w = workloads.random_problem(53, 20480, 201, 3, 400, x_dtype=dt)
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prep = rvq.rvq_prepare_codebooks(cb)
+    ids, res = rvq.rvq_encode(x, cb, prep, residual=True)
+    for a, b in [(1, 20480), (7, 300), (12345, 12346), (3, 19711 + 3)]:
+        xs = x[a:b]
+        assert xs.is_contiguous()
+        sub = rvq.rvq_encode(xs, cb, prep)
+        torch.cuda.synchronize()
+        assert torch.equal(sub, ids[a:b]), (a, b)
+    buf = torch.empty((1000 * 201 + 1,), dtype=torch.float32, device=dev)
+    res_view = buf[1:].view(1000, 201)                     # 4-byte, not 16-byte, aligned
+    lib = rvq.raw_library()
+    ws = torch.empty(rvq.rvq_encode_workspace_size(1000, 201, 3, 400), dtype=torch.uint8,
+                     device=dev)
+    ids2 = torch.empty((1000, 3), dtype=torch.int32, device=dev)
+    import ctypes
+    st = lib.rvq_encode(ctypes.c_void_p(x[5:1005].data_ptr()), 1 if dt == "bf16" else 0, 1000,
+                        201, ctypes.c_void_p(cb.data_ptr()), ctypes.c_void_p(prep.data_ptr()), 3,
+                        400, ctypes.c_void_p(ids2.data_ptr()), ctypes.c_void_p(res_view.data_ptr()),
+                        ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                        ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(ids2, ids[5:1005])
+    assert torch.equal(res_view.contiguous().view(torch.int32), res[5:1005].view(torch.int32))
+
+
 def test_batch_invariance_across_encoder_modes(rvq, dev):
     # 20,480 rows fill the GPU (all levels in one launch); 200 rows use the
     # per-level split plan; both must give the same bits.  d = 200 is not a
