@@ -104,8 +104,13 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
  * products taken on the matrix cores from bf16 copies of r and c with fp32
  * accumulation; the two best-scoring codewords are then rescored exactly in
  * fp32 as sum_i (r_i - c_i)^2 and the smaller wins (lower index on a tie).
- * The screening keeps each score to 2^-19 relative precision, so which two
- * codewords are rescored is decided at that precision.
+ * Which two codewords are rescored is decided by that bf16 screening: each
+ * dot product carries the rounding of bf16 operands (each score is then
+ * kept to 2^-19 relative in the ranking).  When three or more codewords lie
+ * within the screening error of one another, the nearest may not be among
+ * the two rescored.  Relative to ||r||^2 that error shrinks with the width:
+ * at d = 1152 no decision whose exact gap exceeds 1e-4 ||r||^2 was missed in
+ * 32,000 sampled decisions, while at d = 50 one in about 20,000 was.
  * The chosen codeword is subtracted from the fp32 residual, which feeds the
  * next level.
  * ---------------------------------------------------------------------- */
