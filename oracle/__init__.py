@@ -31,6 +31,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rvq_oracle.c")
+_SRC_SCREEN = os.path.join(_HERE, "rvq_screen.c")
 _LIB = os.path.join(_HERE, "librvq_oracle.so")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -39,12 +40,13 @@ _lib: Optional[ctypes.CDLL] = None
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc (no fast-math, no FP contraction); with
     force=False only when the library is missing or older than its source."""
-    stale = not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    stale = not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(_SRC_SCREEN))
     if force or stale:
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
                "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-               "-o", tmp, _SRC, "-lm"]
+               "-o", tmp, _SRC, _SRC_SCREEN, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -60,8 +62,13 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.rvq_oracle_row_sq_residual.argtypes = [p, p, i64, i32, p, i32, i32, p, i32]
     lib.rvq_oracle_teacher_forced.argtypes = [p, p, i64, i32, p, i32, i32, p, p, i32]
     lib.rvq_oracle_embed.argtypes = [p, p, i64, i32, p, i64, p, i32, i32, p, i32]
+    lib.rvq_oracle_screen_encode.argtypes = [p, i64, i32, p, i32, i32, p, p, p, p, p, i32]
+    lib.rvq_oracle_screen_round_bf16.argtypes = [p, i64, p]
+    lib.rvq_oracle_screen_sq_chain.argtypes = [p, i64, i32, p]
     for f in ("rvq_oracle_encode", "rvq_oracle_decode", "rvq_oracle_hist",
-              "rvq_oracle_row_sq_residual", "rvq_oracle_teacher_forced", "rvq_oracle_embed"):
+              "rvq_oracle_row_sq_residual", "rvq_oracle_teacher_forced", "rvq_oracle_embed",
+              "rvq_oracle_screen_encode", "rvq_oracle_screen_round_bf16",
+              "rvq_oracle_screen_sq_chain"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -240,3 +247,63 @@ def teacher_forced(x: np.ndarray, ids: np.ndarray, codebooks: np.ndarray,
                                          _ptr(excess), _ptr(rho2), int(threads)),
            "teacher_forced")
     return {"excess": excess, "rho2": rho2}
+
+
+# ---- the encoder's decision at its own precision (rvq_screen.c) ----
+
+def as_f32(a: np.ndarray, dtype: str = "f32") -> np.ndarray:
+    """fp32 rows, or bf16 bit patterns widened exactly to fp32."""
+    a = widen_bf16(a) if dtype == "bf16" else np.ascontiguousarray(a, dtype=np.float32)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("oracle inputs must be finite")
+    return a
+
+
+def screen_encode(x: np.ndarray, codebooks: np.ndarray, x_dtype: str = "f32",
+                  follow: Optional[np.ndarray] = None, threads: int = 0) -> dict:
+    """Greedy RVQ with the encoder's decision procedure: bf16 screening, the
+    two best screened codewords rescored in fp32, fp32 residual (rvq_screen.c
+    states each step and the bounds).  Without ``follow`` every level takes
+    the unperturbed decision; with ``follow`` ([n, L] IDs) every level takes
+    the given ID and reports whether it was admissible.  Returns ids,
+    n_options (admissible IDs per decision), admissible (bool) [n, L] and
+    the fp32 residual res [n, d] after the IDs taken."""
+    lib = _load()
+    x32 = as_f32(x, x_dtype)
+    cb = as_f32(codebooks)
+    L, K, d = cb.shape
+    n = x32.shape[0]
+    if x32.ndim != 2 or x32.shape[1] != d:
+        raise ValueError("x must be [n, d] with the codebooks' d")
+    fol = None
+    if follow is not None:
+        fol = np.ascontiguousarray(follow, dtype=np.int32)
+        if fol.shape != (n, L):
+            raise ValueError("follow must be [n, L]")
+    ids = np.empty((n, L), dtype=np.int32)
+    nopt = np.empty((n, L), dtype=np.int32)
+    adm = np.empty((n, L), dtype=np.uint8)
+    res = np.empty((n, d), dtype=np.float32)
+    _check(lib.rvq_oracle_screen_encode(_ptr(x32), n, d, _ptr(cb), L, K, _ptr(fol), _ptr(ids),
+                                        _ptr(nopt), _ptr(adm), _ptr(res), int(threads)),
+           "screen_encode")
+    return {"ids": ids, "n_options": nopt, "admissible": adm.astype(bool), "res": res}
+
+
+def screen_round_bf16(v: np.ndarray) -> np.ndarray:
+    """The screening's bf16 rounding of fp32 values, returned as fp32."""
+    lib = _load()
+    a = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty_like(a)
+    _check(lib.rvq_oracle_screen_round_bf16(_ptr(a), a.size, _ptr(out)), "screen_round_bf16")
+    return out
+
+
+def screen_sq_chain(v: np.ndarray) -> np.ndarray:
+    """fp32 two-half fmaf-chain sum of squares of each row of v [n, d]."""
+    lib = _load()
+    a = np.ascontiguousarray(v, dtype=np.float32)
+    n, d = a.shape
+    out = np.empty(n, dtype=np.float32)
+    _check(lib.rvq_oracle_screen_sq_chain(_ptr(a), n, d, _ptr(out)), "screen_sq_chain")
+    return out

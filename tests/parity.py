@@ -14,6 +14,9 @@ to bf16, plus the error bound of an fp32 sum of L terms taken in level order,
 (L-1) * 2^-24 * sum_l |c_l,i| (this term only matters where the codewords
 cancel to far below their own size, e.g. a sum of O(1) terms that is 1e-6);
 per row, within 2^-8 relative L2 of the fp64 sum.
+Screened (the encoder's decision at its own precision, oracle/rvq_screen.c):
+along the GPU's IDs every decision is admissible, and the fp32 residual is
+bit-exact.
 """
 from __future__ import annotations
 
@@ -52,6 +55,23 @@ def check_strict_prefix(gpu_ids: np.ndarray, ref: dict) -> dict:
     return {"rows": n, "rows_all_strict": int((first == L).sum()),
             "strict_decisions": int(strict.sum()), "decisions": int(strict.size),
             "equal_decisions": int((gpu_ids == ref["ids"]).sum())}
+
+
+def check_screened(x, x_dtype, gpu_ids, gpu_res, codebooks) -> dict:
+    """Screening-precision rule (oracle.screen_encode, following the GPU's
+    own IDs): every decision is one the encoder's procedure admits at its
+    own precision, and the fp32 residual after the GPU's IDs (gpu_res, when
+    given) equals the emulated one bit for bit.  Returns counts: decisions,
+    and how many had a single admissible ID."""
+    scr = oracle.screen_encode(x, codebooks, x_dtype=x_dtype, follow=gpu_ids)
+    bad = np.argwhere(~scr["admissible"])
+    assert bad.size == 0, (f"{len(bad)} decisions the encoder's procedure does not admit; "
+                           f"first: row {bad[0][0]} level {bad[0][1]}")
+    if gpu_res is not None:
+        np.testing.assert_array_equal(np.ascontiguousarray(gpu_res, np.float32).view(np.uint32),
+                                      scr["res"].view(np.uint32))
+    return {"decisions": int(scr["n_options"].size),
+            "unique": int((scr["n_options"] == 1).sum())}
 
 
 def check_teacher_forced(x, x_dtype, gpu_ids, codebooks) -> float:

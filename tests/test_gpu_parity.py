@@ -39,6 +39,7 @@ def _full_parity(rvq, w, dev, tag):
     stats = parity.check_strict_prefix(ids_h, ref)
     parity.check_teacher_forced(w.x, w.x_dtype, ids_h, w.codebooks)
     parity.check_residual(res.cpu().numpy(), w.x, w.x_dtype, ids_h, w.codebooks)
+    scr = parity.check_screened(w.x, w.x_dtype, ids_h, res.cpu().numpy(), w.codebooks)
     out32 = rvq.rvq_decode(ids, cb, torch.float32)
     out16 = rvq.rvq_decode(ids, cb, torch.bfloat16)
     hist, msr = rvq.rvq_level_stats(ids, w.K, x, cb)
@@ -47,7 +48,7 @@ def _full_parity(rvq, w, dev, tag):
     parity.check_decode_bf16(parity.bf16_tensor_bits(out16), ids_h, w.codebooks)
     np.testing.assert_array_equal(hist.cpu().numpy(), oracle.hist(ids_h, w.K))
     parity.check_msr(msr.cpu().numpy(), w.x, w.x_dtype, ids_h, w.codebooks)
-    print(f"[{tag}] {stats}")
+    print(f"[{tag}] {stats} screened {scr}")
     return ids_h, ref
 
 
@@ -94,6 +95,8 @@ def test_single_image(rvq, dev):
     print("[single_image]", parity.check_strict_prefix(ids_h[sel], ref))
     parity.check_teacher_forced(sub.x, "f32", ids_h[sel], w.codebooks)
     parity.check_residual(res.cpu().numpy(), w.x, "f32", ids_h, w.codebooks)
+    print("[single_image] screened",
+          parity.check_screened(sub.x, "f32", ids_h[sel], res.cpu().numpy()[sel], w.codebooks))
     out = rvq.rvq_decode(ids, cb, torch.float32)
     torch.cuda.synchronize()
     parity.check_decode_f32(out.cpu().numpy(), ids_h, w.codebooks)
@@ -111,8 +114,10 @@ def test_native_batch(rvq, dev):
     ref = oracle.encode(sub.x, sub.codebooks, x_dtype="bf16")
     print("[native_batch]", parity.check_strict_prefix(ids_h[sel], ref))
     parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
-    parity.check_residual(res[torch.from_numpy(sel).to(dev)].cpu().numpy(), sub.x, "bf16",
-                          ids_h[sel], w.codebooks)
+    res_sel = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
+    parity.check_residual(res_sel, sub.x, "bf16", ids_h[sel], w.codebooks)
+    print("[native_batch] screened",
+          parity.check_screened(sub.x, "bf16", ids_h[sel], res_sel, w.codebooks))
     out16 = rvq.rvq_decode(ids, cb, torch.bfloat16)
     out32 = rvq.rvq_decode(ids, cb, torch.float32)
     hist, _ = rvq.rvq_level_stats(ids, w.K)
@@ -143,6 +148,8 @@ def test_bulk_tokenisation_sampled(rvq, dev):
     ref = oracle.encode(sub.x, sub.codebooks, x_dtype="bf16")
     print("[bulk_tokenisation]", parity.check_strict_prefix(ids_h[sel], ref))
     parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
+    print("[bulk_tokenisation] screened",
+          parity.check_screened(sub.x, "bf16", ids_h[sel], None, w.codebooks))
 
 
 def test_decode_heavy(rvq, dev):
@@ -285,6 +292,9 @@ def test_prepared_stream_layout(rvq, dev, d):
     exact = (cb.astype(np.float64) ** 2).sum(axis=2)
     np.testing.assert_allclose(norms[:, real], exact, rtol=2e-6)
     np.testing.assert_array_equal(norms[:, ~real], np.float32(3.0e38))
+    # bit for bit the fp32 chain the screening oracle states
+    chain = oracle.screen_sq_chain(cb.reshape(L * K, d)).reshape(L, K)
+    np.testing.assert_array_equal(norms[:, real].view(np.uint32), chain.view(np.uint32))
 
 
 EMBED = [
@@ -538,8 +548,9 @@ def test_batch_invariance_across_encoder_modes(rvq, dev):
     ref = oracle.encode(sub.x, sub.codebooks, x_dtype="bf16")
     print("[modes]", parity.check_strict_prefix(ids_h[sel], ref))
     parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
-    parity.check_residual(res[torch.from_numpy(sel).to(dev)].cpu().numpy(), sub.x, "bf16",
-                          ids_h[sel], w.codebooks)
+    res_sel = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
+    parity.check_residual(res_sel, sub.x, "bf16", ids_h[sel], w.codebooks)
+    parity.check_screened(sub.x, "bf16", ids_h[sel], res_sel, w.codebooks)
 
 
 # Shapes for the all-levels-in-one-launch encoder (n >= 19,712 rows fills the
@@ -581,5 +592,7 @@ def test_fused_mode_shapes(rvq, dev, case):
     ref = oracle.encode(sub.x, sub.codebooks, x_dtype=dt)
     print(f"[fused {w.name}]", parity.check_strict_prefix(ids_h[sel], ref))
     parity.check_teacher_forced(sub.x, dt, ids_h[sel], w.codebooks)
-    parity.check_residual(res[torch.from_numpy(sel).to(dev)].cpu().numpy(), sub.x, dt,
-                          ids_h[sel], w.codebooks)
+    res_sel = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
+    parity.check_residual(res_sel, sub.x, dt, ids_h[sel], w.codebooks)
+    print(f"[fused {w.name}] screened",
+          parity.check_screened(sub.x, dt, ids_h[sel], res_sel, w.codebooks))

@@ -1,5 +1,6 @@
-"""Plant plausible mistakes in a copy of the oracle's C source, build each
-copy on the CPU, and check that the pins in test_oracle.py reject it.  This
+"""Plant plausible mistakes in a copy of the oracle's C sources, build each
+copy on the CPU, and check that the pins in test_oracle.py (and, for the
+screening oracle, test_oracle_screen.py) reject it.  This
 shows the pins are strong enough: a dropped term, a wrong sign, a wrong
 stride or index, or a wrong tie-break anywhere in the oracle fails at least
 one of them."""
@@ -10,6 +11,7 @@ import pytest
 
 import oracle
 import test_oracle as pins
+import test_oracle_screen as screen_pins
 
 MUTANTS = {
     "residual_sign": ("r[i] = r[i] - c[i];", "r[i] = r[i] + c[i];"),
@@ -36,6 +38,44 @@ MUTANTS = {
                         "if (l) for (int32_t i = 0; i < d; ++i) r[i] = r[i] - c[i];\n                    ms[row * L + l]"),
 }
 
+# mistakes in rvq_screen.c, the encoder's decision at its own precision
+SCREEN_MUTANTS = {
+    "screen_norm_without_lo": ("p->hilo[k] = (double)hi + (double)lo;", "p->hilo[k] = (double)hi;"),
+    "screen_one_chain": ("const int b = (f >> 3) & 1;", "const int b = 0;"),
+    "screen_halves_by_bit_4": ("const int b = (f >> 3) & 1;", "const int b = (f >> 4) & 1;"),
+    "screen_rescore_top1_only": ("*own = pair_winner(b1, rescore(r, c1, t, d), b2, rescore(r, c2, t, d));",
+                                 "*own = b1;"),
+    "screen_residual_sign": ("for (int32_t f = 0; f < d; ++f) r[f] = r[f] - c[f];",
+                             "for (int32_t f = 0; f < d; ++f) r[f] = r[f] + c[f];"),
+    "screen_r_not_rounded": ("for (int32_t f = 0; f < d; ++f) br[f] = bf16_round(r[f]);",
+                             "for (int32_t f = 0; f < d; ++f) br[f] = r[f];"),
+    "screen_c_not_rounded": ("p->bc[k * d + f] = bf16_round(c[f]);", "p->bc[k * d + f] = c[f];"),
+    "screen_plus_two": ("const double sk = p->hilo[off + k] - 2.0 * s;",
+                        "const double sk = p->hilo[off + k] + 2.0 * s;"),
+    "screen_tie_to_highest": ("    return a < b ? a : b;\n}", "    return a < b ? b : a;\n}"),
+    "screen_round_half_up": ("u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;",
+                             "u = (u + 0x8000u) & 0xFFFF0000u;"),
+    "screen_follow_never_checked": ("ok |= win[q] == take;", "ok = 1;"),
+    "screen_no_bound": ("D[k] = g * tk + ldexp(fabs(sk) + g * tk, -18) + nr * ldexp(tk, -52);",
+                        "D[k] = 0.0;"),
+}
+
+SCREEN_PIN_FUNCS = [
+    screen_pins.test_bf16_rounding_matches_torch,
+    screen_pins.test_sq_chain_is_exact_on_small_integers,
+    screen_pins.test_sq_chain_equals_rational_fmaf_chains,
+    screen_pins.test_sq_chain_within_fp32_bound,
+    screen_pins.test_hand_worked_screening_misses_the_nearest,
+    screen_pins.test_hand_worked_rescoring_overrides_screening,
+    screen_pins.test_near_equal_scores_admit_either_winner,
+    screen_pins.test_hand_worked_norm_low_part_decides,
+    screen_pins.test_duplicated_codewords_tie_to_lowest_index,
+    screen_pins.test_follow_own_choice_and_admissibility,
+] + [(lambda c=c: screen_pins.test_matches_exact_rational_procedure(c))
+                      for c in range(screen_pins.N_TINY)] + [
+    (lambda a=a: screen_pins.test_equals_fp64_oracle_when_screening_is_exact(*a))
+    for a in [(16, 60, 32, 3, 40), (17, 40, 20, 4, 7), (18, 30, 48, 2, 200)]]
+
 PIN_FUNCS = [
     pins.test_hand_worked_example_encode,
     pins.test_hand_worked_example_decode_hist_msr,
@@ -56,18 +96,30 @@ PIN_FUNCS = [
 ] + [(lambda c=c: pins.test_matches_exact_rational_greedy(c)) for c in pins._tiny_problems()]
 
 
-def _build(tmp_path, name, old, new):
-    with open(oracle._SRC) as f:
-        src = f.read()
-    assert src.count(old) >= 1, f"mutation site for {name} not found"
-    mutated = src.replace(old, new, 1)
+def _build(tmp_path, name, old, new, src=None):
+    src = src or oracle._SRC
+    with open(src) as f:
+        text = f.read()
+    assert text.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = text.replace(old, new, 1)
     c = tmp_path / f"{name}.c"
     so = tmp_path / f"{name}.so"
     c.write_text(mutated)
+    sources = [str(c) if s == src else s for s in (oracle._SRC, oracle._SRC_SCREEN)]
     subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-                    "-ffp-contract=off", "-o", str(so), str(c), "-lm"], check=True,
+                    "-ffp-contract=off", "-o", str(so), *sources, "-lm"], check=True,
                    capture_output=True)
     return oracle.load_library(str(so))
+
+
+def _caught(funcs):
+    failures = 0
+    for f in funcs:
+        try:
+            f()
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    return failures
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -75,17 +127,19 @@ def test_pins_reject_mutant(name, tmp_path, monkeypatch, oracle_lib):
     old, new = MUTANTS[name]
     lib = _build(tmp_path, name, old, new)
     monkeypatch.setattr(oracle, "_lib", lib)
-    failures = 0
-    for f in PIN_FUNCS:
-        try:
-            f()
-        except (AssertionError, ValueError, IndexError):
-            failures += 1
-    assert failures > 0, f"no pin caught mutant {name}"
+    assert _caught(PIN_FUNCS) > 0, f"no pin caught mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(SCREEN_MUTANTS))
+def test_screen_pins_reject_mutant(name, tmp_path, monkeypatch, oracle_lib):
+    old, new = SCREEN_MUTANTS[name]
+    lib = _build(tmp_path, name, old, new, oracle._SRC_SCREEN)
+    monkeypatch.setattr(oracle, "_lib", lib)
+    assert _caught(SCREEN_PIN_FUNCS) > 0, f"no pin caught mutant {name}"
 
 
 def test_unmutated_copy_passes_all_pins(tmp_path, monkeypatch, oracle_lib):
     lib = _build(tmp_path, "identity", "#include <math.h>", "#include <math.h>")
     monkeypatch.setattr(oracle, "_lib", lib)
-    for f in PIN_FUNCS:
+    for f in PIN_FUNCS + SCREEN_PIN_FUNCS:
         f()
