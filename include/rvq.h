@@ -113,10 +113,11 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
  * d = 50, 206 and 450, about 1 in 50,000; each time the missed codeword was
  * nearer than the one returned by 1.3e-4 to 2.3e-4 ||r||^2.  At d = 1152
  * none was found in 32,000 sampled decisions.  The IDs are those of this
- * procedure: with the accumulation order of the dot products the only
- * freedom, each decision (and the fp32 residual it leaves) is determined
- * whenever the two best scores are separated from the third by more than
- * the fp32 accumulation error bound.
+ * procedure.  Only two things in it are unspecified: the order in which
+ * the dot products are accumulated in fp32, and the tag bits in the low
+ * mantissa of the ranking keys.  So a decision, and the fp32 residual it
+ * leaves, is fixed whenever the two best scores lie farther from the third
+ * than those two effects can move a score.
  * The chosen codeword is subtracted from the fp32 residual, which feeds the
  * next level.
  * ---------------------------------------------------------------------- */
