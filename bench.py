@@ -190,6 +190,28 @@ def secondary(torch, rvq, workloads, dev) -> dict:
         "vectors_per_s": round(w.N / (ms * 1e-3), 1),
         "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
         "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    # the same encode replayed from a HIP graph (its 17 launches captured
+    # once), checked against the eager IDs before it is timed
+    ref_ids = ids.clone()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        rvq.rvq_encode(x, cb, prep, workspace=wsp, ids_out=ids)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rvq.rvq_encode(x, cb, prep, workspace=wsp, ids_out=ids)
+    ids.fill_(-1)
+    graph.replay()
+    torch.cuda.synchronize(dev)
+    if not torch.equal(ids, ref_ids):
+        raise RuntimeError("graph-replayed encode differs from the eager one")
+    ms = _time_ms(torch, graph.replay, 20)
+    out["single_image_encode_graph"] = {
+        "ms": round(ms, 4), "vectors_per_s": round(w.N / (ms * 1e-3), 1),
+        "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del graph
     # ... then decoded back to fp32
     rec = torch.empty((w.N, w.D), dtype=torch.float32, device=dev)
     rvq.rvq_decode(ids, cb, torch.float32, out=rec)

@@ -34,6 +34,9 @@
  *     token IDs are [n][L] int32 (level-minor); rows are [n][d].
  *   - Work is enqueued on `stream` and the call returns without waiting.
  *     Concurrent calls on different streams must use different workspaces.
+ *   - The device entry points issue only kernel launches on `stream` (no
+ *     memset, copy, allocation or host synchronisation), so a caller may
+ *     capture them in a HIP graph; the streaming encoder is the exception.
  *   - Arguments are validated on the host before any HIP call; a non-OK
  *     status means nothing was enqueued, except RVQ_ERR_HIP, which reports
  *     a failed launch (the stream may then hold part of the work).
