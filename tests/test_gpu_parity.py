@@ -74,6 +74,9 @@ RAGGED = [
     # plan: a lane of the update merges several splits' lists
     (39, 100, 64, 2, 10000, "f32"),
     (40, 5, 48, 2, 20000, "bf16"),
+    # the largest level count decode and statistics take (64: one wave
+    # gathers a row's IDs)
+    (41, 300, 40, 64, 30, "f32"),
 ]
 
 
@@ -305,6 +308,7 @@ EMBED = [
     (1000, 3, 50, 37, 20, "bf16", "bf16", 0.5),
     (2000, 16, 300, 1024, 5000, "bf16", "f32", 0.2),
     (500, 1, 10, 64, 0, "f32", "bf16", 0.0),
+    (800, 64, 20, 96, 50, "f32", "f32", 0.25),
 ]
 
 
@@ -438,6 +442,7 @@ DECODE_STATS = [
     (61, 333, 70, 10, 300, "f32", torch.float32),
     (62, 257, 64, 10, 100, "f32", torch.bfloat16),
     (63, 129, 70, 3, 50, "bf16", torch.bfloat16),
+    (64, 200, 72, 64, 40, "bf16", torch.bfloat16),
 ]
 
 
