@@ -17,8 +17,16 @@ Sources (pages' titles and sections):
     3D": residual quantization adds detail level by level.
   * same blog, "Offline Visual Preprocessing": a fixed tokenizer.
 
-Per-function pins live in ``tests/test_oracle.py``; every function here is
-pinned (no "parity unpinned" entry).
+``rvq_screen.c`` (the ``screen_*`` functions below) takes each codeword
+decision at the encoder's own precision instead: bf16 screening, the two
+best screened codewords rescored in fp32, fp32 residual, with the matrix
+cores' accumulation order bounded rather than reproduced.  Floating point
+decides the codeword, so the GPU's IDs are compared with this one at equal
+precision, and with the fp64 definition under a stated tolerance.
+
+Per-function pins live in ``tests/test_oracle.py`` and
+``tests/test_oracle_screen.py``; every function here is pinned (no "parity
+unpinned" entry).
 """
 from __future__ import annotations
 
