@@ -73,10 +73,11 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.rvq_oracle_screen_encode.argtypes = [p, i64, i32, p, i32, i32, p, p, p, p, p, i32]
     lib.rvq_oracle_screen_round_bf16.argtypes = [p, i64, p]
     lib.rvq_oracle_screen_sq_chain.argtypes = [p, i64, i32, p]
+    lib.rvq_oracle_screen_scores.argtypes = [p, i64, i32, p, i32, p, p]
     for f in ("rvq_oracle_encode", "rvq_oracle_decode", "rvq_oracle_hist",
               "rvq_oracle_row_sq_residual", "rvq_oracle_teacher_forced", "rvq_oracle_embed",
               "rvq_oracle_screen_encode", "rvq_oracle_screen_round_bf16",
-              "rvq_oracle_screen_sq_chain"):
+              "rvq_oracle_screen_sq_chain", "rvq_oracle_screen_scores"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -315,3 +316,19 @@ def screen_sq_chain(v: np.ndarray) -> np.ndarray:
     out = np.empty(n, dtype=np.float32)
     _check(lib.rvq_oracle_screen_sq_chain(_ptr(a), n, d, _ptr(out)), "screen_sq_chain")
     return out
+
+
+def screen_scores(r: np.ndarray, codebook: np.ndarray) -> tuple:
+    """Exact screening scores S [n, K] of fp32 rows r [n, d] against one
+    codebook [K, d], and the bound D [n, K] on how far the encoder's ranking
+    key may lie from S."""
+    lib = _load()
+    a = np.ascontiguousarray(r, dtype=np.float32)
+    cb = np.ascontiguousarray(codebook, dtype=np.float32)
+    n, d = a.shape
+    K = cb.shape[0]
+    S = np.empty((n, K), dtype=np.float64)
+    D = np.empty((n, K), dtype=np.float64)
+    _check(lib.rvq_oracle_screen_scores(_ptr(a), n, d, _ptr(cb), K, _ptr(S), _ptr(D)),
+           "screen_scores")
+    return S, D

@@ -110,6 +110,26 @@ static void prepare(const float *cb, int32_t L, int32_t K, int32_t d, struct pre
     }
 }
 
+/* Exact screening score of one codeword (step 3) and the bound on how far
+ * the GPU's ranking key can lie from it. */
+static void score_and_bound(const float *br, const float *bc, double hilo, double habs, int32_t d,
+                            double *S, double *D)
+{
+    const double u = ldexp(1.0, -23);
+    const double nr = (double)d + 2.0;
+    const double g = nr * u / (1.0 - nr * u);
+    double s = 0.0, a = 0.0;
+    for (int32_t f = 0; f < d; ++f) {
+        const double q = (double)br[f] * (double)bc[f];
+        s += q;
+        a += fabs(q);
+    }
+    const double sk = hilo - 2.0 * s;
+    const double tk = habs + 2.0 * a;
+    *S = sk;
+    *D = g * tk + ldexp(fabs(sk) + g * tk, -18) + nr * ldexp(tk, -52);
+}
+
 /* Exact fp32 rescoring distance of residual r to codeword c. */
 static float rescore(const float *r, const float *c, float *t, int32_t d)
 {
@@ -141,22 +161,11 @@ static int decide(const float *r, const float *br, const float *cbl, const struc
         *nw = 1;
         return SCREEN_OK;
     }
-    const double u = ldexp(1.0, -23);
-    const double nr = (double)d + 2.0;
-    const double g = nr * u / (1.0 - nr * u);
     int32_t b1 = -1, b2 = -1;  /* two smallest (S, index) */
     for (int32_t k = 0; k < K; ++k) {
-        const float *bc = p->bc + (off + k) * (int64_t)d;
-        double s = 0.0, a = 0.0;
-        for (int32_t f = 0; f < d; ++f) {
-            const double q = (double)br[f] * (double)bc[f];
-            s += q;
-            a += fabs(q);
-        }
-        const double sk = p->hilo[off + k] - 2.0 * s;
-        const double tk = p->habs[off + k] + 2.0 * a;
-        S[k] = sk;
-        D[k] = g * tk + ldexp(fabs(sk) + g * tk, -18) + nr * ldexp(tk, -52);
+        score_and_bound(br, p->bc + (off + k) * (int64_t)d, p->hilo[off + k], p->habs[off + k],
+                        d, &S[k], &D[k]);
+        const double sk = S[k];
         if (b1 < 0 || sk < S[b1]) {
             b2 = b1;
             b1 = k;
@@ -315,4 +324,35 @@ int rvq_oracle_screen_sq_chain(const float *v, int64_t n, int32_t d, float *out)
     if (n < 0 || d < 1 || (n > 0 && (!v || !out))) return SCREEN_ERR_ARG;
     for (int64_t i = 0; i < n; ++i) out[i] = sq_chain(v + i * d, d);
     return SCREEN_OK;
+}
+
+/* Screening scores of rows r [n][d] (fp32) against one codebook cb [K][d]:
+ * S [n][K] the exact score of step 3, D [n][K] the bound on the GPU's key. */
+int rvq_oracle_screen_scores(const float *r, int64_t n, int32_t d, const float *cb, int32_t K,
+                             double *S, double *D)
+{
+    if (n < 0 || d < 1 || K < 1 || (n > 0 && (!r || !cb || !S || !D))) return SCREEN_ERR_ARG;
+    if (n == 0) return SCREEN_OK;
+    struct prepared p;
+    p.hilo = malloc((size_t)K * sizeof(double));
+    p.habs = malloc((size_t)K * sizeof(double));
+    p.bc = malloc((size_t)K * (size_t)d * sizeof(float));
+    float *br = malloc((size_t)d * sizeof(float));
+    int err = SCREEN_OK;
+    if (!p.hilo || !p.habs || !p.bc || !br) {
+        err = SCREEN_ERR_NOMEM;
+    } else {
+        prepare(cb, 1, K, d, &p);
+        for (int64_t i = 0; i < n; ++i) {
+            for (int32_t f = 0; f < d; ++f) br[f] = bf16_round(r[i * d + f]);
+            for (int32_t k = 0; k < K; ++k)
+                score_and_bound(br, p.bc + (int64_t)k * d, p.hilo[k], p.habs[k], d,
+                                &S[i * K + k], &D[i * K + k]);
+        }
+    }
+    free(p.hilo);
+    free(p.habs);
+    free(p.bc);
+    free(br);
+    return err;
 }

@@ -50,14 +50,15 @@ SCREEN_MUTANTS = {
     "screen_r_not_rounded": ("for (int32_t f = 0; f < d; ++f) br[f] = bf16_round(r[f]);",
                              "for (int32_t f = 0; f < d; ++f) br[f] = r[f];"),
     "screen_c_not_rounded": ("p->bc[k * d + f] = bf16_round(c[f]);", "p->bc[k * d + f] = c[f];"),
-    "screen_plus_two": ("const double sk = p->hilo[off + k] - 2.0 * s;",
-                        "const double sk = p->hilo[off + k] + 2.0 * s;"),
+    "screen_plus_two": ("const double sk = hilo - 2.0 * s;", "const double sk = hilo + 2.0 * s;"),
     "screen_tie_to_highest": ("    return a < b ? a : b;\n}", "    return a < b ? b : a;\n}"),
     "screen_round_half_up": ("u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;",
                              "u = (u + 0x8000u) & 0xFFFF0000u;"),
     "screen_follow_never_checked": ("ok |= win[q] == take;", "ok = 1;"),
-    "screen_no_bound": ("D[k] = g * tk + ldexp(fabs(sk) + g * tk, -18) + nr * ldexp(tk, -52);",
-                        "D[k] = 0.0;"),
+    "screen_no_bound": ("*D = g * tk + ldexp(fabs(sk) + g * tk, -18) + nr * ldexp(tk, -52);",
+                        "*D = 0.0;"),
+    "screen_bound_without_key_tag": ("*D = g * tk + ldexp(fabs(sk) + g * tk, -18) + nr * ldexp(tk, -52);",
+                                     "*D = g * tk + nr * ldexp(tk, -52);"),
 }
 
 SCREEN_PIN_FUNCS = [
@@ -74,7 +75,9 @@ SCREEN_PIN_FUNCS = [
 ] + [(lambda c=c: screen_pins.test_matches_exact_rational_procedure(c))
                       for c in range(screen_pins.N_TINY)] + [
     (lambda a=a: screen_pins.test_equals_fp64_oracle_when_screening_is_exact(*a))
-    for a in [(16, 60, 32, 3, 40), (17, 40, 20, 4, 7), (18, 30, 48, 2, 200)]]
+    for a in [(16, 60, 32, 3, 40), (17, 40, 20, 4, 7), (18, 30, 48, 2, 200)]] + [
+    (lambda a=a: screen_pins.test_bound_covers_fp32_accumulation_orders(*a))
+    for a in [(1152, 48), (3, 300), (1, 400)]]
 
 PIN_FUNCS = [
     pins.test_hand_worked_example_encode,

@@ -271,3 +271,58 @@ def test_follow_rejects_out_of_range_ids():
     cb = np.ones((1, 3, 8), np.float32)
     with pytest.raises(ValueError):
         oracle.screen_encode(x, cb, follow=np.int32([[0], [3]]))
+
+
+def _rz32(v64):
+    """fp64 -> fp32 rounded toward zero."""
+    f = v64.astype(np.float32)
+    over = np.abs(f.astype(np.float64)) > np.abs(v64)
+    f[over] = np.nextafter(f[over], np.float32(0))
+    return f
+
+
+@pytest.mark.parametrize("d,K", [(1152, 48), (3, 300), (1, 400)])
+def test_bound_covers_fp32_accumulation_orders(d, K):
+    # The bound D on |key - S| must hold whatever order and rounding the
+    # matrix cores use.  The terms of a score are exact in fp32 (hi, lo and
+    # -2 bf16(r) bf16(c), at most 17 significant bits), so sum them in fp32
+    # in several orders and with round-toward-zero, then replace the 5 low
+    # mantissa bits by a tag at both extremes, as the ranking key does.
+    # (At small d the tag bits, not the accumulation, dominate the bound.)
+    g = np.random.default_rng(21 + d)
+    r = g.standard_normal((6, d)).astype(np.float32)
+    cb = g.standard_normal((K, d)).astype(np.float32)
+    S, D = oracle.screen_scores(r, cb)
+    br = oracle.screen_round_bf16(r).astype(np.float64)
+    bc = oracle.screen_round_bf16(cb).astype(np.float64)
+    nv = oracle.screen_sq_chain(cb)
+    hi = oracle.screen_round_bf16(nv)
+    lo = oracle.screen_round_bf16(nv - hi)
+    worst = 0.0
+    for i in range(r.shape[0]):
+        for k in range(K):
+            terms = np.concatenate([[hi[k], lo[k]], -2.0 * br[i] * bc[k]])
+            t32 = terms.astype(np.float32)
+            assert np.array_equal(t32.astype(np.float64), terms)
+            sums = [np.add.accumulate(t32, dtype=np.float32)[-1],
+                    np.add.accumulate(t32[::-1], dtype=np.float32)[-1],
+                    np.sum(t32, dtype=np.float32)]
+            acc = np.float32(hi[k] + lo[k])                  # one rounding per k-step of 16
+            for j in range(2, len(terms), 16):
+                acc = np.float32(np.float64(acc) + terms[j:j + 16].sum())
+            sums.append(acc)
+            acc = np.float32(0)                              # truncating adder
+            for t in t32:
+                acc = _rz32(np.array([np.float64(acc) + np.float64(t)]))[0]
+            sums.append(acc)
+            for v in sums:
+                bits = np.float32(v).view(np.uint32)
+                for tag in (0, 31):
+                    key = np.uint32((bits & ~np.uint32(31)) | np.uint32(tag)).view(np.float32)
+                    err = abs(float(key) - S[i, k])
+                    assert err <= D[i, k], (i, k, err, D[i, k])
+                    if D[i, k] > 0:
+                        worst = max(worst, err / D[i, k])
+    # the bound is a worst case, not a vacuous one
+    assert 1e-4 < worst <= 1.0
+    assert np.all(D < 1e-3 * (np.abs(S) + 4 * d))
