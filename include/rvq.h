@@ -112,10 +112,10 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
  * kept to 2^-19 relative in the ranking).  When three or more codewords lie
  * within the screening error of one another, the nearest may not be among
  * the two rescored.  This is not confined to small widths: random sweeps
- * over about 160 shapes (widths 32 to 1280) found three such decisions, at
- * d = 50, 206 and 450, about 1 in 50,000; each time the missed codeword was
- * nearer than the one returned by 1.3e-4 to 2.3e-4 ||r||^2.  At d = 1152
- * none was found in 32,000 sampled decisions.  The IDs are those of this
+ * over about 520 shapes (widths 1 to 1280) found five such decisions, at
+ * d = 50, 149, 206, 450 and 1057, about 1 in 100,000; each time the missed
+ * codeword was nearer than the one returned by 1.1e-4 to 2.3e-4 ||r||^2.
+ * At d = 1152 none was found in 32,000 sampled decisions.  The IDs are those of this
  * procedure.  Only two things in it are unspecified: the order in which
  * the dot products are accumulated in fp32, and the tag bits in the low
  * mantissa of the ranking keys.  So a decision, and the fp32 residual it

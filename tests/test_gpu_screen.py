@@ -72,12 +72,14 @@ def test_near_equal_scores(rvq, dev):
 
 
 # Rows where the screening ranked the exact nearest codeword third, so the
-# returned codeword is 1.3e-4 to 2.3e-4 ||r||^2 farther than the nearest:
+# returned codeword is 1.1e-4 to 2.3e-4 ||r||^2 farther than the nearest:
 # (seed, n, d, L, K, dtype, row, level, gap / ||r||^2 at least)
 SWEEP_ROWS = [
     (1017, 23296, 50, 10, 3672, "f32", 16322, 3, 2.3e-4),
     (1027, 2350, 206, 11, 3721, "bf16", 561, 2, 1.3e-4),
     (1042, 1080, 450, 7, 1663, "bf16", 79, 0, 1.5e-4),
+    (1004, 436, 149, 5, 4310, "f32", 100, 2, 1.5e-4),
+    (1011, 21998, 1057, 5, 1712, "f32", 19741, 0, 1.1e-4),
 ]
 
 
