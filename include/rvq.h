@@ -59,7 +59,7 @@ extern "C" {
 typedef enum rvq_status {
     RVQ_OK = 0,
     RVQ_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misaligned pointer */
-    RVQ_ERR_UNSUPPORTED = 2,        /* valid request outside what this build supports */
+    RVQ_ERR_UNSUPPORTED = 2,        /* valid request outside what the library supports */
     RVQ_ERR_WORKSPACE_TOO_SMALL = 3,
     RVQ_ERR_HIP = 4                 /* a HIP launch failed */
 } rvq_status;
