@@ -208,8 +208,12 @@ rvq_status rvq_level_stats_workspace_size(int64_t n, int32_t L, int32_t K, int32
  * hist      : device, [L][K] int64 output, fully overwritten.  Required.
  * msr       : device, [L] fp64 output, or NULL to compute the counts only.
  *             With n == 0 it is all zeros.
- * x         : device, [n][d] rows (x_dtype); required when msr is non-NULL
- *             and n > 0, ignored otherwise.
+ * x         : device, [n][d] rows (x_dtype), aligned to the element size;
+ *             required when msr is non-NULL and n > 0, ignored otherwise.
+ *             Rows that do not start 16-byte (fp32) or 8-byte (bf16)
+ *             aligned, or d not a multiple of 4, take a per-element path:
+ *             the counts are the same and msr may differ in the last bits
+ *             of its fp64 sum.
  * codebooks : device, [L][K][d] fp32; required when msr is non-NULL.
  * bad_ids   : as for rvq_decode.
  * workspace : device, >= rvq_level_stats_workspace_size bytes, 256-byte aligned.

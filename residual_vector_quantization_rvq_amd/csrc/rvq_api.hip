@@ -331,7 +331,7 @@ rvq_status rvq_level_stats(const int32_t *ids, int64_t n, int32_t L, int32_t K, 
       return fail(RVQ_ERR_INVALID_ARGUMENT, "unknown x_dtype %d", (int)x_dtype);
     RVQ_TRY(need(codebooks, "codebooks", 16));
     RVQ_TRY(need(msr, "msr", 8));
-    if (n > 0) RVQ_TRY(need(x, "x", 16));
+    if (n > 0) RVQ_TRY(need(x, "x", x_dtype == RVQ_BF16 ? 2 : 4));
   }
   if (bad_ids && !aligned(bad_ids, 4))
     return fail(RVQ_ERR_INVALID_ARGUMENT, "bad_ids must be 4-byte aligned");
@@ -371,7 +371,7 @@ rvq_status rvq_decode_level_stats(const int32_t *ids, int64_t n, const float *co
   if (n > 0) {
     RVQ_TRY(need(ids, "ids", 4));
     RVQ_TRY(need(out, "out", 16));
-    RVQ_TRY(need(x, "x", 16));
+    RVQ_TRY(need(x, "x", x_dtype == RVQ_BF16 ? 2 : 4));
   }
   if (bad_ids && !aligned(bad_ids, 4))
     return fail(RVQ_ERR_INVALID_ARGUMENT, "bad_ids must be 4-byte aligned");

@@ -418,8 +418,9 @@ hipError_t launch_msr(const void *x, bool x_bf16, const int32_t *ids, int64_t n,
                       int out_kind, hipStream_t s) {
   const int64_t blocks = n > 0 ? ceil_div(n, kMsrRowsPerBlock) : 0;
   // float4 columns need d % 4 == 0 and 16-byte (fp32) / 8-byte (bf16) row starts,
-  // which the aligned base pointers then give for every row
-  const bool vec = (d & 3) == 0;
+  // which an aligned base pointer then gives for every row; rows that start
+  // less aligned (a slice of a larger batch) take the per-element path
+  const bool vec = (d & 3) == 0 && ((uintptr_t)x & (x_bf16 ? 7 : 15)) == 0;
   if (blocks > 0) {
     const dim3 grid((unsigned)blocks), block(256);
 #define RVQ_MSR(V, O)                                                                    \

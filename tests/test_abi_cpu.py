@@ -232,6 +232,7 @@ def test_decode_level_stats_rejects_bad_arguments(rvq):
     assert call(a10=9) == 1                # unknown x dtype
     assert call(a11=None) == 1             # msr required
     assert call(a6=None) == 1              # out required when n > 0
-    assert call(a9=p(8)) == 1              # x misaligned
+    assert call(a9=p(2)) == 1              # fp32 x not 4-byte aligned
+    assert call(a9=p(1), a10=1) == 1       # bf16 x not 2-byte aligned
     assert call(a14=1) == 3                # workspace too small
     assert call(a3=65) == 2                # L above the gather limit

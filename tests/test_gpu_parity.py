@@ -601,3 +601,28 @@ def test_fused_mode_shapes(rvq, dev, case):
     parity.check_residual(res_sel, sub.x, dt, ids_h[sel], w.codebooks)
     print(f"[fused {w.name}] screened",
           parity.check_screened(sub.x, dt, ids_h[sel], res_sel, w.codebooks))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_unaligned_rows_in_level_stats(rvq, dev, dt):
+    # Rows that start one element past an aligned address (a slice of a
+    # larger buffer) take the per-element msr path: the counts and the decode
+    # bits are those of an aligned copy, msr agrees to fp64 rounding.
+    w = workloads.random_problem(65, 700, 96, 4, 300, x_dtype=dt)
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids = rvq.rvq_encode(x, cb)
+    flat = torch.empty(x.numel() + 1, dtype=x.dtype, device=dev)
+    xs = flat[1:].view(x.shape)
+    xs.copy_(x)
+    assert xs.data_ptr() % (16 if dt == "f32" else 8) != 0
+    hist_a, msr_a = rvq.rvq_level_stats(ids, w.K, x, cb)
+    hist_b, msr_b = rvq.rvq_level_stats(ids, w.K, xs, cb)
+    dec_a, h2a, m2a = rvq.rvq_decode_level_stats(ids, x, cb, torch.float32)
+    dec_b, h2b, m2b = rvq.rvq_decode_level_stats(ids, xs, cb, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(hist_a, hist_b) and torch.equal(h2b, hist_b)
+    assert torch.equal(dec_a.view(torch.int32), dec_b.view(torch.int32))
+    assert torch.equal(m2b, msr_b)
+    np.testing.assert_allclose(msr_b.cpu().numpy(), msr_a.cpu().numpy(), rtol=1e-12)
+    parity.check_msr(msr_b.cpu().numpy(), w.x, dt, ids.cpu().numpy(), w.codebooks)
