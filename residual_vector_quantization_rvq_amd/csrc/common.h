@@ -111,9 +111,70 @@ __host__ __device__ inline int64_t stream_bytes(int L, int64_t K, int64_t d) {
   return (int64_t)L * (padded_k(K) / kTileCw) * tile_bytes((int)(padded_d(d) / kStageCols));
 }
 
+// ---- candidate band of the encoder ----
+// The bf16 screening key of codeword k, key_k, lies near the exact score
+// t_k = ||c_k||^2 - 2 r.c_k of the fp32 residual r.  With r_b = bf16(r),
+// dr = r - r_b, dc_k = c_k - bf16(c_k), the identity
+//   r.c - r_b.bf16(c) = dr.c + r_b.dc
+// splits the screening error into a residual-rounding and a codeword-rounding
+// part.  Per row and level the encoder uses the bound
+//   E = min(5 sigma, E_cs) + E_acc + E_norm + E_tag,
+//   sigma = 2 sqrt((||dr||^2 cmax + ||r_b||^2 dmax) / d)   (error scale of a
+//           typical codeword: rounding errors of independent features),
+//   E_cs  = 2 (sqrt(||dr||^2 cmax) + sqrt(||r_b||^2 dmax))  (Cauchy-Schwarz,
+//           a worst case; smaller than 5 sigma only for d < about 25),
+//   E_acc = min(d + 2, 5 sqrt(d + 2)) 2^-23 T,  T = 2 sqrt(||r_b||^2 cmax) + cmax
+//           (fp32 accumulation on the matrix cores),
+//   E_norm = ((d/2 + 1) 2^-24 + 2^-17) cmax   (fp32 norm chain, hi + lo split),
+//   E_tag = 2^-18 T                           (5 tag bits of the key),
+// with cmax = max_k ||c_k||^2 and dmax = max_k ||dc_k||^2 of the level.  Every
+// codeword whose key is within
+//   band = max(0, 2 E - 0.5e-4 ||r_b||^2)
+// of the smallest key is rescored exactly in fp32.  If the nearest codeword
+// k* is more than 1e-4 ||r||^2 closer than every other, then
+// key_k* <= t_k* + E <= t_k1 - 1e-4 ||r||^2 + E <= key_min + band, so k* is
+// a candidate, and the fp32 rescoring then orders it first.
+// Written with explicitly rounded operations so that every kernel computes
+// the same bits from the same inputs.
+constexpr float kBandZ = 5.0f;
+__device__ __forceinline__ float screen_band(float rbn2, float drn2, float cmax, float dmax, int d) {
+  const float fd = (float)d;
+  const float a = __fmul_rn(drn2, cmax);
+  const float b = __fmul_rn(rbn2, dmax);
+  const float sig = __fmul_rn(2.f, __fsqrt_rn(__fdiv_rn(__fadd_rn(a, b), fd)));
+  const float ecs = __fmul_rn(2.f, __fadd_rn(__fsqrt_rn(a), __fsqrt_rn(b)));
+  const float escr = fminf(__fmul_rn(kBandZ, sig), ecs);
+  const float tsum = __fadd_rn(__fmul_rn(2.f, __fsqrt_rn(__fmul_rn(rbn2, cmax))), cmax);
+  const float nacc = fminf(__fadd_rn(fd, 2.f), __fmul_rn(kBandZ, __fsqrt_rn(__fadd_rn(fd, 2.f))));
+  const float eacc = __fmul_rn(__fmul_rn(nacc, 0x1p-23f), tsum);
+  const float enorm =
+      __fmul_rn(__fadd_rn(__fmul_rn(__fadd_rn(__fmul_rn(0.5f, fd), 1.f), 0x1p-24f), 0x1p-17f), cmax);
+  const float etag = __fmul_rn(0x1p-18f, tsum);
+  const float e = __fmul_rn(__fadd_rn(__fadd_rn(escr, eacc), __fadd_rn(enorm, etag)), 1.0f + 0x1p-10f);
+  return fmaxf(0.f, __fsub_rn(__fmul_rn(2.f, e), __fmul_rn(0.5e-4f, rbn2)));
+}
+
+// Per-lane candidate list of the sweep: blocks of 64 codewords whose
+// smallest key came within the band of the running minimum.
+constexpr int kList = 6;
+// Split-mode record per (row, split, lane half), in float4 units: [cnt, 0,
+// 0, 0], then up to kList list entries [k1, k2, base, 0]
+constexpr int kRecF4 = 1 + kList;
+// Candidates the encoder rescores per row and level (the smallest key's
+// codeword included); a level with more is left to the exact scan.
+constexpr int kMaxRescore = 6;
+// repair codes per (row, level): kAuxOk when the band was complete; kAuxScan
+// when it may not have been (the list overflowed, or two blocks each held
+// two keys inside the band), so that the level is taken again by an exact
+// fp32 scan
+constexpr int kAuxOk = -1;
+constexpr int kAuxScan = -2;
+
 // ---- host-side launchers (return hipGetLastError of their launches) ----
+// lstat [L][4]: max ||c||^2 and max ||c - bf16(c)||^2 of each level (the
+// band bound's codebook terms); tstat [L][tiles][2] the per-tile maxima.
 hipError_t launch_prepare(const float *cb, int L, int K, int d, float *norms, uint8_t *stream,
-                          float *cbpad, int dp, hipStream_t s);
+                          float *cbpad, int dp, float *tstat, float *lstat, hipStream_t s);
 
 struct EncodePlan {
   bool fused;          // all levels in one launch
@@ -123,7 +184,14 @@ struct EncodePlan {
   int splits;          // split mode: workgroups per row block per level
   int tiles_per_split;
 };
+// The planner assumes at most this many compute units, so that workspace
+// sizes (which do not know the device) bound every plan.
+constexpr int kPlanMaxCus = 1024;
 EncodePlan plan_encode(int64_t n, int d, int K, int num_cus);
+// Whether some device may run n rows in split mode, and the split-mode
+// records such a plan may write.
+bool split_possible(int64_t n);
+int64_t split_records(int64_t n, int K);
 struct EncodeArgs {
   const void *x;        // caller's rows [n][d], fp32 or bf16
   int x_bf16;
@@ -136,7 +204,10 @@ struct EncodeArgs {
   float *rbuf[2];       // fp32 residuals [n][dp]: level l reads rbuf[l & 1], writes rbuf[(l+1) & 1]
   float *residual_out;  // caller's [n][d] output or null
   int32_t *ids;
-  float4 *part;
+  float4 *part;         // split mode: kRecF4 float4 per (row, split, lane half)
+  const float *lstat;   // [L][4] codebook terms of the band bound
+  float2 *rstat;        // split mode: (||r_b||^2, ||dr||^2) per row of the level's residual
+  int32_t *aux;         // [n][L] repair codes (kAuxOk, kAuxScan)
   // Split mode: bf16 B-fragments of the rows the next sweep reads (the
   // input, then each level's residual), in blocks of 32 rows: the 16 bytes
   // of lane L for k-step ks of block b are at ((b * dp/16 + ks) * 64 + L),

@@ -65,6 +65,137 @@ __global__ __launch_bounds__(256) void fragment_rows_kernel(const float *__restr
   frag[o] = make_uint4(q[0], q[1], q[2], q[3]);
 }
 
+// Band inputs of the level-0 rows for split mode (the fused encoder forms
+// them while building its fragments): two lanes per row, lane h summing
+// bf16(v)^2 and (v - bf16(v))^2 over features ks*16 + h*8 + e in order, then
+// half 0 + half 1, as every encoder kernel sums them.
+__global__ __launch_bounds__(256) void row_stats_kernel(const float *__restrict__ src, int64_t n,
+                                                        int dp, float2 *__restrict__ rstat) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t >> 1;
+  const int h = (int)(t & 1);
+  float srb = 0.f, sdr = 0.f;
+  if (row < n) {
+    for (int ks = 0; ks < (dp >> 4); ++ks) {
+      float v[8];
+      read8(src, row, dp, ks * 16 + h * 8, true, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float b = bf16_bits_to_f32(f32_to_bf16_bits(v[e]));
+        const float u = v[e] - b;
+        srb = fmaf(b, b, srb);
+        sdr = fmaf(u, u, sdr);
+      }
+    }
+  }
+  const float orb = __shfl_xor(srb, 1, 64), odr = __shfl_xor(sdr, 1, 64);
+  if (row < n && h == 0) rstat[row] = make_float2(srb + orb, sdr + odr);
+}
+
+// Levels whose candidate band could not be shown complete (repair code
+// kAuxScan, rare: a band list overflowed, or two blocks each held two keys
+// inside the band) are taken again by an exact scan: the nearest codeword
+// under the rescoring's own fp32 distance (two half sums in feature order,
+// half 0 + half 1) over all K, the lower index on a tie.  One workgroup per
+// 256 rows finds its rows with such a level and redoes each one: the
+// residual is rebuilt from the row and its IDs with the encoder's fp32
+// subtractions, and once an ID changes every later level is scanned too.
+// Changed IDs, and the final residual when the caller asked for it, are
+// rewritten.
+__global__ __launch_bounds__(256) void repair_kernel(EncodeArgs a) {
+  __shared__ float res[kMaxStages * kStageCols];
+  __shared__ int rows[256];
+  __shared__ int nrows;
+  __shared__ float wd[4];
+  __shared__ int wi[4];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 256;
+  if (tid == 0) nrows = 0;
+  __syncthreads();
+  {
+    const int64_t row = r0 + tid;
+    bool f = false;
+    if (row < a.n)
+      for (int l = 0; l < a.L; ++l) f |= a.aux[row * a.L + l] == kAuxScan;
+    if (f) rows[atomicAdd(&nrows, 1)] = tid;
+  }
+  __syncthreads();
+  const int nr = nrows;
+  const int nks = a.dp >> 4;
+  for (int q = 0; q < nr; ++q) {
+    const int64_t row = r0 + rows[q];
+    for (int i = tid; i < a.dp; i += 256) {
+      float v = 0.f;
+      if (i < a.d)
+        v = a.x_bf16 ? bf16_bits_to_f32(((const uint16_t *)a.x)[row * a.d + i])
+                     : ((const float *)a.x)[row * a.d + i];
+      res[i] = v;
+    }
+    __syncthreads();
+    bool changed = false;
+    for (int l = 0; l < a.L; ++l) {
+      const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
+      int id = a.ids[row * a.L + l];
+      if (changed || a.aux[row * a.L + l] == kAuxScan) {
+        float bd = __builtin_inff();
+        int bi = kNoIndex;
+        for (int k = tid; k < a.K; k += 256) {
+          const float *c = cb_l + (int64_t)k * a.dp;
+          float p0 = 0.f, p1 = 0.f;
+          for (int ks = 0; ks < nks; ++ks) {
+            float x0[8], x1[8];
+            read8(c, 0, a.dp, ks * 16, true, x0);
+            read8(c, 0, a.dp, ks * 16 + 8, true, x1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float t = res[ks * 16 + e] - x0[e];
+              const float u = res[ks * 16 + 8 + e] - x1[e];
+              p0 = fmaf(t, t, p0);
+              p1 = fmaf(u, u, p1);
+            }
+          }
+          const float dk = p0 + p1;
+          if (lex_lt(dk, k, bd, bi)) {
+            bd = dk;
+            bi = k;
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float od = __shfl_xor(bd, off, 64);
+          const int oi = __shfl_xor(bi, off, 64);
+          if (lex_lt(od, oi, bd, bi)) {
+            bd = od;
+            bi = oi;
+          }
+        }
+        if ((tid & 63) == 0) {
+          wd[tid >> 6] = bd;
+          wi[tid >> 6] = bi;
+        }
+        __syncthreads();
+        bd = wd[0];
+        bi = wi[0];
+        for (int w = 1; w < 4; ++w)
+          if (lex_lt(wd[w], wi[w], bd, bi)) {
+            bd = wd[w];
+            bi = wi[w];
+          }
+        if (bi != id) {
+          changed = true;
+          if (tid == 0) a.ids[row * a.L + l] = bi;
+          id = bi;
+        }
+      }
+      for (int i = tid; i < a.dp; i += 256) res[i] = res[i] - cb_l[(int64_t)id * a.dp + i];
+      __syncthreads();
+    }
+    if (changed && a.residual_out)
+      for (int i = tid; i < a.d; i += 256) a.residual_out[row * a.d + i] = res[i];
+    __syncthreads();
+  }
+}
+
 // residual_out [n][d] from the padded fp32 residual [n][dp].
 __global__ __launch_bounds__(256) void unpad_kernel(const float *__restrict__ src, int64_t n,
                                                     int d, int dp, float *__restrict__ out) {
@@ -74,12 +205,22 @@ __global__ __launch_bounds__(256) void unpad_kernel(const float *__restrict__ sr
   for (int i = lane; i < d; i += 64) out[row * d + i] = src[row * dp + i];
 }
 
+bool split_possible(int64_t n) { return ceil_div(n, kRowsPerWG) * 10 < (int64_t)kPlanMaxCus * 6; }
+
+int64_t split_records(int64_t n, int K) {
+  const int64_t rb = ceil_div(n, kRowsPerWG);
+  const int64_t tiles = padded_k(K) / kTileCw;
+  const int64_t want = ceil_div(2 * (int64_t)kPlanMaxCus, rb > 0 ? rb : 1);
+  return n * (want < tiles ? want : tiles) * 2;
+}
+
 EncodePlan plan_encode(int64_t n, int d, int K, int num_cus) {
   EncodePlan p{};
   p.stages = (int)(padded_d(d) / kStageCols);
   p.tiles = (int)(padded_k(K) / kTileCw);
   p.row_blocks = (int)ceil_div(n, kRowsPerWG);
-  const int cus = num_cus > 0 ? num_cus : 256;
+  int cus = num_cus > 0 ? num_cus : 256;
+  cus = cus < kPlanMaxCus ? cus : kPlanMaxCus;
   p.fused = (int64_t)p.row_blocks * 10 >= (int64_t)cus * 6;
   if (p.fused) {
     p.splits = 1;
@@ -145,17 +286,22 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
     const int64_t pieces = ceil_div(a.n, kRowsPerWG) * 4 * (a.dp >> 4) * 64;
     fragment_rows_kernel<<<dim3((unsigned)ceil_div(pieces, 256)), dim3(256), 0, s>>>(
         a.src0, a.n, a.dp, a.xfrag, pieces);
+    row_stats_kernel<<<dim3((unsigned)ceil_div(2 * a.n, 256)), dim3(256), 0, s>>>(a.src0, a.n,
+                                                                                a.dp, a.rstat);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_stages(p, a, events, s);
-  if (e != hipSuccess || !convert) return e;
-  if (p.fused)
-    unfragment_kernel<<<dim3((unsigned)ceil_div(a.n, 32)), dim3(256), 0, s>>>(final_buf, a.n, a.d,
-                                                                          a.dp, a.residual_out);
-  else
-    unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(final_buf, a.n, a.d, a.dp,
-                                                       a.residual_out);
+  if (e != hipSuccess) return e;
+  if (convert) {
+    if (p.fused)
+      unfragment_kernel<<<dim3((unsigned)ceil_div(a.n, 32)), dim3(256), 0, s>>>(
+          final_buf, a.n, a.d, a.dp, a.residual_out);
+    else
+      unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(final_buf, a.n, a.d, a.dp,
+                                                         a.residual_out);
+  }
+  repair_kernel<<<dim3((unsigned)ceil_div(a.n, 256)), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

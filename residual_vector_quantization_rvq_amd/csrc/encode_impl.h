@@ -49,10 +49,6 @@ namespace {
 
 constexpr int NT = 256;
 
-__device__ __forceinline__ float pack_key(float score, uint32_t tag) {
-  return __uint_as_float((__float_as_uint(score) & ~31u) | tag);
-}
-
 // Codeword index of a key found in the 64-codeword block whose lane-half
 // base is b (kNoIndex when nothing was found).
 __device__ __forceinline__ int block_index(float key, int b) {
@@ -325,9 +321,11 @@ __device__ __forceinline__ void opaque(T &...v) {
 // B-fragments of one row half: lane half h holds features ks*16 + h*8 + e.
 // Loads are issued eight k-steps at a time before any fragment is pinned,
 // so the waits for them overlap.
+// Also returns the band inputs of the row half: srb = sum bf16(v)^2 and
+// sdr = sum (v - bf16(v))^2 in feature order (k-steps past the row add zeros).
 template <int KS>
 __device__ __forceinline__ void build_bfrags(RowFrags<KS> &bfr, const float *src, int64_t row,
-                                             int dp, int h) {
+                                             int dp, int h, float &srb, float &sdr) {
   static_for<0, (KS + 7) / 8>([&](auto G_) {
     constexpr int g = decltype(G_)::value;
     constexpr int n = KS - g * 8 < 8 ? KS - g * 8 : 8;
@@ -338,9 +336,21 @@ __device__ __forceinline__ void build_bfrags(RowFrags<KS> &bfr, const float *src
     });
     static_for<0, n>([&](auto U_) {
       constexpr int ks = g * 8 + decltype(U_)::value;
-      bfr.template set<ks>(to_bf16x8(v[decltype(U_)::value]));
+      const float(&w)[8] = v[decltype(U_)::value];
+      const u32x4 q = to_bf16x8(w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float b0 = __uint_as_float(q[e] << 16);
+        const float b1 = __uint_as_float(q[e] & 0xffff0000u);
+        const float t0 = w[2 * e] - b0, t1 = w[2 * e + 1] - b1;
+        srb = fmaf(b0, b0, srb);
+        sdr = fmaf(t0, t0, sdr);
+        srb = fmaf(b1, b1, srb);
+        sdr = fmaf(t1, t1, sdr);
+      }
+      bfr.template set<ks>(q);
     });
-    opaque(row);
+    opaque(row, srb, sdr);
   });
 }
 
@@ -380,9 +390,11 @@ __device__ __forceinline__ void build_bfrags_frag(RowFrags<KS> &bfr, const uint4
 
 // The same fragments straight from bf16 rows (stride dp): the stored bits
 // are the fragment.
+// (bf16 rows are their own bf16 copy: srb = sum v^2, and the rounding
+// part sdr stays zero)
 template <int KS>
 __device__ __forceinline__ void build_bfrags_bf16(RowFrags<KS> &bfr, const uint16_t *src,
-                                                  int64_t row, int dp, int h) {
+                                                  int64_t row, int dp, int h, float &srb) {
   static_for<0, (KS + 7) / 8>([&](auto G_) {
     constexpr int g = decltype(G_)::value;
     constexpr int n = KS - g * 8 < 8 ? KS - g * 8 : 8;
@@ -395,17 +407,18 @@ __device__ __forceinline__ void build_bfrags_bf16(RowFrags<KS> &bfr, const uint1
     });
     static_for<0, n>([&](auto U_) {
       constexpr int ks = g * 8 + decltype(U_)::value;
-      bfr.template set<ks>(f[decltype(U_)::value]);
+      const u32x4 &q = f[decltype(U_)::value];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float b0 = __uint_as_float(q[e] << 16);
+        const float b1 = __uint_as_float(q[e] & 0xffff0000u);
+        srb = fmaf(b0, b0, srb);
+        srb = fmaf(b1, b1, srb);
+      }
+      bfr.template set<ks>(q);
     });
-    opaque(row);
+    opaque(row, srb);
   });
-}
-
-// First two candidates of a row's top-2 list as valid codeword indices.
-__device__ __forceinline__ void candidates(int i1, int i2, int K, int &c1, int &c2, bool &v2) {
-  c1 = (i1 >= 0 && i1 < K) ? i1 : 0;  // finite inputs always give a valid first candidate
-  v2 = i2 >= 0 && i2 < K && i2 != i1;
-  c2 = v2 ? i2 : c1;
 }
 
 // ---- LDS ring of codebook stages fed by direct global->LDS loads ----
@@ -574,33 +587,39 @@ __device__ __forceinline__ void rows_f32(int v, int (&rows)[4], int lane) {
   for (int i = 0; i < 4; ++i) rows[i] = __shfl(v, 8 * i + (lane >> 3), 64);
 }
 
-// Exact fp32 rescoring of the two candidates and residual update for the
+// Exact fp32 rescoring of a row's candidates and residual update for the
 // fused encoder, through LDS.  Lanes L and L+32 hold one row (h = 0, 1) and
 // each takes features ks*16 + h*8 + e in order ks, e, accumulating (r - c)^2
-// with fmaf; the row's distance is (half 0) + (half 1).  r - c1 is written as
-// it goes (fragment-major, when STORE) and becomes the next level's
-// B-fragments; rows where c2 wins are redone with every lane taking part.
-// Returns the chosen index.  rsrc: the level's residual (fragment-major
-// buffer, or for level 0 the fp32 / bf16 input rows of stride dp, based at
-// row wbase of this wave, rrow = this lane's row relative to wbase).
-template <int KS, RSrc SRC, bool STORE>
+// with fmaf; the row's distance is (half 0) + (half 1).  The candidates are
+// ca (the smallest key) and nx more, xc(0) .. xc(nx-1).  The first pass
+// scores ca and xc(0), writes r - ca as it goes (fragment-major, when STORE)
+// and makes it the next level's B-fragments; further passes score two more
+// candidates each; the smallest distance wins, the lower index on a tie, and
+// rows where another candidate won are redone with every lane taking part.
+// Returns the winner.  st_rb / st_dr: sum bf16(v)^2 and sum (v - bf16(v))^2
+// over this lane's half of the winner's v = r - c, in the same feature order
+// (the next level's band inputs).  rsrc: the level's residual
+// (fragment-major buffer, or for level 0 the fp32 / bf16 input rows of
+// stride dp, based at row wbase of this wave, rrow = this lane's row
+// relative to wbase).
+template <int KS, RSrc SRC, bool STORE, typename XC>
 __device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc, int rrow,
-                                             float *dst_blk, int dp, const float *cb_l, int c1,
-                                             int c2, bool v2, int lane_in, uint32_t ring_lds,
-                                             int wave) {
+                                             float *dst_blk, int dp, const float *cb_l, int ca,
+                                             int nx, XC &&xc, int lane_in, uint32_t ring_lds,
+                                             int wave, float &st_rb, float &st_dr) {
   // Everything below derives from this opaque copy of the lane index, so the
   // compiler cannot hoist lane-dependent addresses out of the level loop and
   // keep them live through the sweep.
   int lane = lane_in;
   opaque1(lane);
-  const int h = lane >> 5;
-  const int rho = lane & 31;
+  int h = lane >> 5;
+  int rho = lane & 31;
   const int nks = dp >> 4;                // k-steps inside the row
   const int nhg = (nks + 1) >> 1;         // half groups
   const bool odd = nks & 1;               // the last half group has one k-step
   constexpr int kStores = STORE ? 4 : 0;  // stores a full half group issues
 
-  // residual copies (the same in the first pass and the redo)
+  // residual copies (the same in every pass)
   RowCopy rc{};
   uint32_t rc2[2] = {0u, 0u}, rhi2[2] = {0u, 0u};
   if constexpr (SRC == RSrc::kRowF32) {
@@ -620,10 +639,8 @@ __device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc
       rhi2[i] = m >= 2 ? 32u : 0u;  // chunk in the second k-step (odd tails)
     }
   }
-  const uint32_t fm_off = (uint32_t)lane * 16u;
+  uint32_t fm_off = (uint32_t)lane * 16u;
 
-  // Issues the copies of half group hg into buffer b: the residual, then
-  // codewords ca (and cb when TWO).
   // Issues the copies of the next half group (hg, in increasing order within
   // a pass) into buffer b: the residual, then codewords ca (and cb when
   // TWO).  The source bases advance by one half group per call through an
@@ -634,7 +651,7 @@ __device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc
     rnext = static_cast<const char *>(rsrc);
     cnext = reinterpret_cast<const char *>(cb_l);
   };
-  auto issue = [&](int hg, int b, const RowCopy &ca, const RowCopy &cbw, auto TWO_) {
+  auto issue = [&](int hg, int b, const RowCopy &ka, const RowCopy &kb, auto TWO_) {
     constexpr bool TWO = decltype(TWO_)::value;
     const bool part = odd && hg == nhg - 1;
     const uint32_t ar = upd_area(ring_lds, wave, 3 * b);
@@ -651,14 +668,14 @@ __device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc
       rnext += 64;  // 32 bf16 features
     }
     {
-      const uint32_t d = part ? ca.hi : 0u;
-      dma_rows4(cnext, upd_area(ring_lds, wave, 3 * b + 1), ca.off[0] - d, ca.off[1] - d,
-                ca.off[2] - d, ca.off[3] - d);
+      const uint32_t d = part ? ka.hi : 0u;
+      dma_rows4(cnext, upd_area(ring_lds, wave, 3 * b + 1), ka.off[0] - d, ka.off[1] - d,
+                ka.off[2] - d, ka.off[3] - d);
     }
     if constexpr (TWO) {
-      const uint32_t d = part ? cbw.hi : 0u;
-      dma_rows4(cnext, upd_area(ring_lds, wave, 3 * b + 2), cbw.off[0] - d, cbw.off[1] - d,
-                cbw.off[2] - d, cbw.off[3] - d);
+      const uint32_t d = part ? kb.hi : 0u;
+      dma_rows4(cnext, upd_area(ring_lds, wave, 3 * b + 2), kb.off[0] - d, kb.off[1] - d,
+                kb.off[2] - d, kb.off[3] - d);
     }
     cnext += 128;
     asm volatile("" : "+s"(rnext), "+s"(cnext));
@@ -707,70 +724,172 @@ __device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc
     *reinterpret_cast<f32x4 *>(sb + st_off) = f32x4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4 *>(sb + 1024 + st_off) = f32x4{v[4], v[5], v[6], v[7]};
   };
+  // band inputs of the next level: bf16(v)^2 and (v - bf16(v))^2 in feature
+  // order (q packs the bf16 values of v[2e], v[2e+1] in its low, high half)
+  float srb = 0.f, sdr = 0.f;
+  auto stat8 = [&](const float (&v)[8], const u32x4 &q) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float b0 = __uint_as_float(q[e] << 16);
+      const float b1 = __uint_as_float(q[e] & 0xffff0000u);
+      const float t0 = v[2 * e] - b0, t1 = v[2 * e + 1] - b1;
+      srb = fmaf(b0, b0, srb);
+      sdr = fmaf(t0, t0, sdr);
+      srb = fmaf(b1, b1, srb);
+      sdr = fmaf(t1, t1, sdr);
+    }
+  };
 
   // Half groups whose k-steps all lie inside every row this stage count
   // serves need no run-time test; k-steps past the row are never touched
   // (their fragments were built as zeros and stay zero).
   constexpr int kSure = 4 * prev_stage_count(KS / 4);  // k-steps inside every row
   auto sure = [](int hg) { return 2 * hg + 1 < kSure; };
+  auto combine = [&](float p) {
+    const float q = __shfl_xor(p, 32, 64);
+    return h ? q + p : p + q;
+  };
 
-  // First pass: both distances, r - c1 stored and made the next fragments.
+  // First pass: distances of ca and cb0, r - ca stored and made the next
+  // fragments.  Without a second candidate in any row of the wave only ca
+  // is copied.
   int rows[4];
-  rows_f32(c1, rows, lane);
+  const int cb0 = nx > 0 ? xc(0) : ca;
+  rows_f32(ca, rows, lane);
   const RowCopy k1 = row_copy_f32(lane, (int64_t)dp * 4, rows);
-  rows_f32(c2, rows, lane);
+  rows_f32(cb0, rows, lane);
   const RowCopy k2 = row_copy_f32(lane, (int64_t)dp * 4, rows);
   float p1 = 0.f, p2 = 0.f;
   opaque1(st_off);
-  auto first = [&](auto HG_) {
+  auto first = [&](auto HG_, auto TWO_) {
     constexpr int hg = decltype(HG_)::value;
+    constexpr bool TWO = decltype(TWO_)::value;
     constexpr int b = hg & 1;
     // this half group's copies have landed (only the previous half group's
     // stores may be newer)
     if constexpr (hg == 0) wait_vmcnt_upd<0>();
     else wait_vmcnt_upd<kStores>();
-    if (sure(hg + 1) || hg + 1 < nhg) issue(hg + 1, b ^ 1, k1, k2, std::true_type{});
+    if (sure(hg + 1) || hg + 1 < nhg) issue(hg + 1, b ^ 1, k1, k2, TWO_);
     static_for<0, 2>([&](auto J_) {
       constexpr int j = decltype(J_)::value;
       constexpr int ks = 2 * hg + j;
       if (ks < kSure || ks < nks) {
-        float r[8], a[8], c[8], v[8];
+        float r[8], a[8], v[8];
         read_r(b, j, r);
         read_c(upd_area(ring_lds, wave, 3 * b + 1), j, a);
-        read_c(upd_area(ring_lds, wave, 3 * b + 2), j, c);
+        if constexpr (TWO) {
+          float c[8];
+          read_c(upd_area(ring_lds, wave, 3 * b + 2), j, c);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float u = r[e] - c[e];
+            p2 = fmaf(u, u, p2);
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float t = r[e] - a[e];
-          const float u = r[e] - c[e];
           p1 = fmaf(t, t, p1);
-          p2 = fmaf(u, u, p2);
           v[e] = t;
         }
         if constexpr (STORE) store(ks, v);
-        bfr.template set<ks>(to_bf16x8(v));
-        // the distance sums are finished here, in order, so the compiler
-        // cannot defer them and keep every difference alive
-        opaque(p1, p2);
+        const u32x4 q = to_bf16x8(v);
+        stat8(v, q);
+        bfr.template set<ks>(q);
+        // the sums are finished here, in order, so the compiler cannot defer
+        // them and keep every difference alive
+        opaque(p1, p2, srb, sdr);
       }
     });
   };
-  issue(0, 0, k1, k2, std::true_type{});
-  static_for<0, KS / 2>([&](auto G_) {
-    constexpr int hg = decltype(G_)::value;
-    if (sure(hg) || hg < nhg) first(G_);
-  });
-  const float q1 = __shfl_xor(p1, 32, 64);
-  const float q2 = __shfl_xor(p2, 32, 64);
-  const float d1 = h ? q1 + p1 : p1 + q1;
-  const float d2 = h ? q2 + p2 : p2 + q2;
-  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
-  // Rows where the second candidate won are redone.  Every lane of the wave
+  if (__ballot(nx > 0)) {
+    issue(0, 0, k1, k2, std::true_type{});
+    static_for<0, KS / 2>([&](auto G_) {
+      constexpr int hg = decltype(G_)::value;
+      if (sure(hg) || hg < nhg) first(G_, std::true_type{});
+    });
+  } else {
+    issue(0, 0, k1, k1, std::false_type{});
+    static_for<0, KS / 2>([&](auto G_) {
+      constexpr int hg = decltype(G_)::value;
+      if (sure(hg) || hg < nhg) first(G_, std::false_type{});
+    });
+  }
+  int best = ca;
+  float dbest = combine(p1);
+  {
+    const float d2 = combine(p2);
+    if (nx > 0 && lex_lt(d2, cb0, dbest, best)) {
+      best = cb0;
+      dbest = d2;
+    }
+  }
+  // Further candidates, two per pass (distances only), at most two passes
+  // (kMaxRescore candidates in all; a row with more is left to the exact
+  // scan).  Rows with fewer score ca again, which is never taken.  (The
+  // passes are unrolled: as a loop, the compiler keeps more values alive
+  // across it than the registers hold.)
+  static_for<0, 2>([&](auto P_) {
+    const int j = 1 + 2 * decltype(P_)::value;
+    if (!__ballot(nx > j)) return;
+    // (the lane-derived values are re-made opaque each pass, so the compiler
+    // cannot hoist the pass's addresses out of the loop and hold them all)
+    opaque(h, rho, fm_off);
+    const int ea = nx > j ? xc(j) : ca;
+    const int eb = nx > j + 1 ? xc(j + 1) : ea;
+    rows_f32(ea, rows, lane);
+    const RowCopy ke = row_copy_f32(lane, (int64_t)dp * 4, rows);
+    rows_f32(eb, rows, lane);
+    const RowCopy kf = row_copy_f32(lane, (int64_t)dp * 4, rows);
+    float pa = 0.f, pb = 0.f;
+    auto scan = [&](auto HG_) {
+      constexpr int hg = decltype(HG_)::value;
+      constexpr int b = hg & 1;
+      wait_vmcnt_upd<0>();
+      if (sure(hg + 1) || hg + 1 < nhg) issue(hg + 1, b ^ 1, ke, kf, std::true_type{});
+      static_for<0, 2>([&](auto J_) {
+        constexpr int jj = decltype(J_)::value;
+        constexpr int ks = 2 * hg + jj;
+        if (ks < kSure || ks < nks) {
+          float r[8], a[8], c[8];
+          read_r(b, jj, r);
+          read_c(upd_area(ring_lds, wave, 3 * b + 1), jj, a);
+          read_c(upd_area(ring_lds, wave, 3 * b + 2), jj, c);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float t = r[e] - a[e];
+            const float u = r[e] - c[e];
+            pa = fmaf(t, t, pa);
+            pb = fmaf(u, u, pb);
+          }
+          opaque(pa, pb);
+        }
+      });
+    };
+    restart();
+    issue(0, 0, ke, kf, std::true_type{});
+    static_for<0, KS / 2>([&](auto G_) {
+      constexpr int hg = decltype(G_)::value;
+      if (sure(hg) || hg < nhg) scan(G_);
+    });
+    const float da = combine(pa), db = combine(pb);
+    if (nx > j && lex_lt(da, ea, dbest, best)) {
+      best = ea;
+      dbest = da;
+    }
+    if (nx > j + 1 && lex_lt(db, eb, dbest, best)) {
+      best = eb;
+      dbest = db;
+    }
+    });
+  // Rows where another candidate won are redone.  Every lane of the wave
   // takes part (no divergent branch, so fragments are rewritten in place):
-  // a lane whose first candidate won recomputes exactly r - c1 again.
-  if (__ballot(take2)) {
-    const int cs = take2 ? c2 : c1;
-    rows_f32(cs, rows, lane);
+  // a lane whose first candidate won recomputes exactly r - ca again.
+  if (__ballot(best != ca)) {
+    rows_f32(best, rows, lane);
     const RowCopy kc = row_copy_f32(lane, (int64_t)dp * 4, rows);
+    srb = 0.f;
+    sdr = 0.f;
     auto redo = [&](auto HG_) {
       constexpr int hg = decltype(HG_)::value;
       constexpr int b = hg & 1;
@@ -787,7 +906,10 @@ __device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = r[e] - c[e];
           if constexpr (STORE) store(ks, v);
-          bfr.template set<ks>(to_bf16x8(v));
+          const u32x4 q = to_bf16x8(v);
+          stat8(v, q);
+          bfr.template set<ks>(q);
+          opaque(srb, sdr);
         }
       });
     };
@@ -800,7 +922,157 @@ __device__ __forceinline__ int update_staged(RowFrags<KS> &bfr, const void *rsrc
       if (sure(hg) || hg < nhg) redo(G_);
     });
   }
-  return take2 ? c2 : c1;
+  st_rb = srb;
+  st_dr = sdr;
+  return best;
+}
+
+
+// Exact fp32 distances of the 64 codewords of block blk to one row, and the
+// nearest of them (the lower index on a tie); used when a block held two
+// keys inside the band, so that its third and later keys, which the sweep
+// does not keep, may be inside it too.  rget(ks, h, r) reads features
+// ks*16 + h*8 .. +7 of the row.  Lane l takes codewords blk*64 + l%32 and
+// blk*64 + 32 + l%32 over feature half l/32, summed in the rescoring's order
+// (half 0 + half 1), so the winner's distance equals its rescoring.  Every
+// lane returns the same index.
+template <typename RG>
+__device__ __forceinline__ int rescore_block(RG &&rget, int nks, const float *cb_l, int dp, int K,
+                                             int blk, int lane) {
+  const int h = lane >> 5;
+  const int k0 = blk * 64 + (lane & 31), k1 = k0 + 32;
+  const float *c0 = cb_l + (int64_t)(k0 < K ? k0 : K - 1) * dp;
+  const float *c1 = cb_l + (int64_t)(k1 < K ? k1 : K - 1) * dp;
+  float p0 = 0.f, p1 = 0.f;
+  for (int ks = 0; ks < nks; ++ks) {
+    float r[8], x0[8], x1[8];
+    rget(ks, h, r);
+    read8(c0, 0, dp, ks * 16 + h * 8, true, x0);
+    read8(c1, 0, dp, ks * 16 + h * 8, true, x1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = r[e] - x0[e], u = r[e] - x1[e];
+      p0 = fmaf(t, t, p0);
+      p1 = fmaf(u, u, p1);
+    }
+  }
+  const float q0 = __shfl_xor(p0, 32, 64), q1 = __shfl_xor(p1, 32, 64);
+  const float d0 = h ? q0 + p0 : p0 + q0;
+  const float d1 = h ? q1 + p1 : p1 + q1;
+  float bd = k0 < K ? d0 : __builtin_inff();
+  int bi = k0;
+  if (k1 < K && lex_lt(d1, k1, bd, bi)) {
+    bd = d1;
+    bi = k1;
+  }
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const float od = __shfl_xor(bd, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (lex_lt(od, oi, bd, bi)) {
+      bd = od;
+      bi = oi;
+    }
+  }
+  return bi;
+}
+
+// Per-lane candidate list entry: a 64-codeword block's two smallest keys
+// and the block's base (as in block_index).
+struct BandEntry {
+  float k1, k2;
+  int base;
+};
+
+// Per-lane state of the candidate band over one level's blocks: the
+// smallest key so far and the list entries appended since the last reset
+// (more than kList: the list overflowed).
+struct BandState {
+  float R1;
+  int cnt;
+};
+
+__device__ __forceinline__ void band_reset(BandState &b) {
+  b.R1 = __builtin_inff();
+  b.cnt = 0;
+}
+
+// One 64-codeword block of this lane (two smallest keys k1 <= k2, block
+// base): update the running minimum, and append the block to the lane's
+// list when k1 is within the band of the row's running minimum (ref: this
+// lane's minimum and the other half's as last exchanged, which is never
+// below the row's final minimum).  Every block holding a key inside the
+// final band has k1 inside it, and so k1 was inside the band of ref when it
+// came; the list (filtered at the end) therefore holds every such block.
+// A new minimum more than the band below every earlier key of the lane
+// makes all its entries stale, which empties the list; a full list first
+// drops the entries that are no longer inside the band of ref, and only
+// overflows (cnt > kList) when kList entries still are.
+__device__ __forceinline__ void band_block(BandState &b, float k1, float k2, int base, float band,
+                                           float r_other, BandEntry *list) {
+  const float r_old = b.R1;
+  b.R1 = __builtin_amdgcn_fmed3f(b.R1, k1, -__builtin_inff());  // min
+  b.cnt = __fadd_rn(k1, band) < r_old ? 0 : b.cnt;
+  const float lim = __fadd_rn(__builtin_amdgcn_fmed3f(b.R1, r_other, -__builtin_inff()), band);
+  if (k1 <= lim) {
+    if (b.cnt == kList) {
+      int m = 0;
+      for (int j = 0; j < kList; ++j) {
+        const BandEntry e = list[j];
+        if (e.k1 <= lim) list[m++] = e;
+      }
+      b.cnt = m;
+    }
+    if (b.cnt < kList) list[b.cnt] = BandEntry{k1, k2, base};
+    ++b.cnt;
+  }
+}
+
+// The end of a level for one lane: from its list, the smallest key's
+// codeword (ca, key ka; (key, index) order), and the blocks inside the
+// final band thr.  Indices of blocks whose k1 is inside the band but whose
+// k2 is not are compacted, in place, into list[0 .. nx) (base field), as
+// candidates next to ca; a block with k2 inside the band may hold more keys
+// inside it than the two the sweep keeps, so it is reported as fblk (block
+// id, base / 64) and counted in nfail instead.
+__device__ __forceinline__ void band_finish(const BandState &b, BandEntry *list, float &ka,
+                                            int &ia) {
+  ka = __builtin_inff();
+  ia = kNoIndex;
+  const int nl = b.cnt < kList ? b.cnt : kList;
+  for (int j = 0; j < kList; ++j) {
+    if (j < nl) {
+      const BandEntry e = list[j];
+      const int i = block_index(e.k1, e.base);
+      if (lex_lt(e.k1, i, ka, ia)) {
+        ka = e.k1;
+        ia = i;
+      }
+    }
+  }
+}
+__device__ __forceinline__ int band_collect(const BandState &b, BandEntry *list, float thr,
+                                            int ca, int K, int &nfail, int &fblk) {
+  int nx = 0;
+  nfail = 0;
+  fblk = -1;
+  const int nl = b.cnt < kList ? b.cnt : kList;
+  for (int j = 0; j < kList; ++j) {
+    if (j < nl) {
+      const BandEntry e = list[j];
+      if (e.k2 <= thr) {
+        ++nfail;
+        fblk = e.base >> 6;
+      } else if (e.k1 <= thr) {
+        const int i = block_index(e.k1, e.base);
+        if (i != ca && i >= 0 && i < K) {
+          list[nx].base = i;
+          ++nx;
+        }
+      }
+    }
+  }
+  return nx;
 }
 
 }  // namespace
@@ -810,6 +1082,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     EncodeArgs a, int T, int level, int splits, int tiles_per_split) {
   constexpr int KS = 4 * S;
   __shared__ uint4 ring[kSlots * (kSlotBytes / 16)];
+  __shared__ BandEntry clist[NT * kList];  // per-lane candidate lists
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -845,11 +1118,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     });
   };
   RowFrags<KS> bfr;
+  BandEntry *const mylist = clist + tid * kList;
+  // band inputs of the row's residual at the current level: sum bf16(r)^2
+  // and sum (r - bf16(r))^2, each half in feature order, half 0 + half 1
+  float rbn2 = 0.f, drn2 = 0.f;
+  auto halves = [&](float v) {
+    const float o = __shfl_xor(v, 32, 64);
+    return h ? o + v : v + o;
+  };
   if (FUSED) {
+    float srb = 0.f, sdr = 0.f;
     if (a.x16)
-      build_bfrags_bf16<KS>(bfr, a.x16, rowc, a.dp, h);
+      build_bfrags_bf16<KS>(bfr, a.x16, rowc, a.dp, h, srb);
     else
-      build_bfrags<KS>(bfr, a.src0, rowc, a.dp, h);
+      build_bfrags<KS>(bfr, a.src0, rowc, a.dp, h, srb, sdr);
+    rbn2 = halves(srb);
+    drn2 = halves(sdr);
     prologue();
   } else {
     // one sweep per level and workgroup: the ring fills while the
@@ -864,12 +1148,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   for (int l = l_begin; l < l_end; ++l) {
     ls = reinterpret_cast<const uint4 *>(a.stream) + ((int64_t)l * T + t0) * tile_u4;
-    // Running top-2 of this lane as (key, base of the key's 64-codeword
-    // block).  Blocks come in increasing codeword order and a key's tag is
-    // its position in the block, so keeping the earlier entry on equal keys
-    // is the (key, index) order.
-    float R1 = __builtin_inff(), R2 = __builtin_inff();
-    int B1 = kNoIndex, B2 = kNoIndex;
+    // The candidate band of this row at this level (common.h).  Blocks come
+    // in increasing codeword order and a key's tag is its position in the
+    // block, so keeping the earlier entry on equal keys is the (key, index)
+    // order.
+    if (!FUSED) {
+      const float2 st = a.rstat[rowc];
+      rbn2 = st.x;
+      drn2 = st.y;
+    }
+    const float band = screen_band(rbn2, drn2, a.lstat[4 * l], a.lstat[4 * l + 1], a.d);
+    BandState bs;
+    band_reset(bs);
+    float r_other = __builtin_inff();
 
     // byte offsets in the ring of the slots of stages g-1, g and g+1 (the
     // refill of stage g + kAhead goes to the slot of stage g-1)
@@ -949,33 +1240,57 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       // Epilogue: accumulator element i of sub-tile j is codeword
       // j*32 + (i/4)*8 + h*4 + i%4 of the tile for this lane's row.  Per
       // 64-codeword block p (sub-tiles 2p, 2p+1) the tag jj*16 + i is unique.
-      // Each key costs three VALU ops: pack, then the two-smallest update
-      // with med3 (med3(a, b, -inf) is min(a, b)).
-      const float ninf = -__builtin_inff();
+      // Each key costs three VALU ops: pack, then the block's two smallest
+      // keys updated with med3 and min.
+      const uint32_t keep = ~31u;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         float k1 = __builtin_inff(), k2 = __builtin_inff();
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float key = pack_key(acc[2 * p + jj][i], (uint32_t)(jj * 16 + i));
-            k2 = __builtin_amdgcn_fmed3f(k1, k2, key);
-            k1 = __builtin_amdgcn_fmed3f(k1, key, ninf);
-          }
+          // key = score with tag jj*16 + i in its low 5 bits; k2 = the
+          // middle of (k1, k2, key); k1 = min(k1, key).  Written out, one
+          // statement per sub-tile: compiled, each min would first
+          // canonicalise both operands.
+          const f32x16 &c = acc[2 * p + jj];
+          float key;
+#define RVQ_KEY(i, t)                                                   \
+  "v_and_or_b32 %[key], %[a" #i "], %[keep], " #t "\n\t"             \
+  "v_med3_f32 %[k2], %[k1], %[k2], %[key]\n\t"                       \
+  "v_min_f32 %[k1], %[k1], %[key]\n\t"
+#define RVQ_KEY_IN                                                                         \
+  [a0] "v"(c[0]), [a1] "v"(c[1]), [a2] "v"(c[2]), [a3] "v"(c[3]), [a4] "v"(c[4]),         \
+      [a5] "v"(c[5]), [a6] "v"(c[6]), [a7] "v"(c[7]), [a8] "v"(c[8]), [a9] "v"(c[9]),      \
+      [a10] "v"(c[10]), [a11] "v"(c[11]), [a12] "v"(c[12]), [a13] "v"(c[13]),               \
+      [a14] "v"(c[14]), [a15] "v"(c[15]), [keep] "s"(keep)
+          if (jj == 0)
+            asm(RVQ_KEY(0, 0) RVQ_KEY(1, 1) RVQ_KEY(2, 2) RVQ_KEY(3, 3) RVQ_KEY(4, 4) RVQ_KEY(5, 5)
+                    RVQ_KEY(6, 6) RVQ_KEY(7, 7) RVQ_KEY(8, 8) RVQ_KEY(9, 9) RVQ_KEY(10, 10)
+                        RVQ_KEY(11, 11) RVQ_KEY(12, 12) RVQ_KEY(13, 13) RVQ_KEY(14, 14)
+                            RVQ_KEY(15, 15)
+                : [k1] "+v"(k1), [k2] "+v"(k2), [key] "=&v"(key)
+                : RVQ_KEY_IN);
+          else
+            asm(RVQ_KEY(0, 16) RVQ_KEY(1, 17) RVQ_KEY(2, 18) RVQ_KEY(3, 19) RVQ_KEY(4, 20)
+                    RVQ_KEY(5, 21) RVQ_KEY(6, 22) RVQ_KEY(7, 23) RVQ_KEY(8, 24) RVQ_KEY(9, 25)
+                        RVQ_KEY(10, 26) RVQ_KEY(11, 27) RVQ_KEY(12, 28) RVQ_KEY(13, 29)
+                            RVQ_KEY(14, 30) RVQ_KEY(15, 31)
+                : [k1] "+v"(k1), [k2] "+v"(k2), [key] "=&v"(key)
+                : RVQ_KEY_IN);
+#undef RVQ_KEY_IN
+#undef RVQ_KEY
           __builtin_amdgcn_sched_barrier(0);
         }
         const int base = (t0 + tt) * kTileCw + p * 64 + h * 4;
-        const bool c = k1 < R1;
-        const float old = c ? R1 : R2;
-        const int oldb = c ? B1 : B2;
-        const float nw = c ? k2 : k1;
-        R1 = c ? k1 : R1;
-        B1 = c ? base : B1;
-        const bool d = nw < old;
-        R2 = d ? nw : old;
-        B2 = d ? base : oldb;
+        // both keys are formed here, key by key (the compiler would
+        // otherwise sink k2's chain into the rare append and keep all of
+        // the block's keys alive)
+        asm volatile("" : "+v"(k1), "+v"(k2));
+        band_block(bs, k1, k2, base, band, r_other, mylist);
       }
+      // the other half's running minimum, for the next tile's blocks (the
+      // exchange completes under that tile's matrix work)
+      r_other = __shfl_xor(bs.R1, 32, 64);
     };
     using TNo = std::integral_constant<int, 0>;
     using TYes = std::integral_constant<int, 1>;
@@ -994,49 +1309,117 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int tt = 0; tt < ntiles; ++tt) tile(tt, TRun{}, TRun{});
     }
 
-    // Decode the tags, then merge with the other half of the row (lanes L
-    // and L+32 hold the same row over disjoint codewords).
-    float S1 = R1, S2 = R2;
-    int I1 = block_index(R1, B1), I2 = block_index(R2, B2);
-    {
-      const float t1 = __shfl_xor(S1, 32, 64), t2 = __shfl_xor(S2, 32, 64);
-      const int j1 = __shfl_xor(I1, 32, 64), j2 = __shfl_xor(I2, 32, 64);
-      merge_top2(S1, I1, S2, I2, t1, j1, t2, j2);
-    }
-
     if (FUSED) {
+      // smallest key of the row over both halves, (key, index) order
+      float ka;
+      int i1;
+      band_finish(bs, mylist, ka, i1);
+      const float o1 = __shfl_xor(ka, 32, 64);
+      const int oi1 = __shfl_xor(i1, 32, 64);
+      const bool oth = lex_lt(o1, oi1, ka, i1);
+      const float rmin = oth ? o1 : ka;
+      int ca = oth ? oi1 : i1;
+      ca = (ca >= 0 && ca < a.K) ? ca : 0;  // finite inputs always give a valid codeword
+      const float thr = __fadd_rn(rmin, band);
+      // This lane's other candidates, compacted into its list.  A block
+      // whose second key lies inside the band may hold more keys inside it,
+      // so that block is rescored whole below; two such blocks, or an
+      // overflowing list, leave the level to the exact scan after the launch.
+      int nfail, fblk;
+      const int nx = band_collect(bs, mylist, thr, ca, a.K, nfail, fblk);
+      const int onf = __shfl_xor(nfail, 32, 64);
+      const int ofb = __shfl_xor(fblk, 32, 64);
+      const bool ovf = __shfl_xor(bs.cnt, 32, 64) > kList || bs.cnt > kList;
+      int rcode;
+      if (ovf || nfail + onf > 2 || nfail > 1 || onf > 1 ||
+          (nfail == 1 && onf == 1 && fblk != ofb))
+        rcode = kAuxScan;
+      else
+        rcode = nfail ? fblk : (onf ? ofb : kAuxOk);
+
       // every wave is done with the ring: the update may use this wave's
       // areas of it
       barrier_only();
-      int c1, c2;
-      bool v2;
-      candidates(I1, I2, a.K, c1, c2, v2);
       const bool store = l + 1 < a.L || a.res_final != nullptr;
       // this wave's block of 32 rows in the fragment-major buffers
       const int64_t blk_off = ((int64_t)rb * 4 + wave) * 32 * a.dp;
       float *dst = a.rbuf[(l + 1) & 1] + blk_off;
       const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
+      const int64_t w0 = (int64_t)rb * kRowsPerWG + wave * 32;
+      const int64_t wbase = w0 < a.n ? w0 : a.n - 1;
+      const int nks = a.dp >> 4;
+
+      // rows with one block to rescore whole (rare): its nearest codeword
+      // joins the row's candidates
+      int bonus = -1;
+      for (uint64_t need = __ballot(h == 0 && rcode >= 0); need; need &= need - 1) {
+        const int rl = __builtin_ctzll(need);
+        const int blk = __shfl(rcode, rl, 64);
+        int bi;
+        if (l == 0) {
+          const int64_t rr = w0 + rl < a.n ? w0 + rl : a.n - 1;
+          if (a.x16)
+            bi = rescore_block([&](int ks, int hh, float(&r)[8]) {
+              read8_bf16(a.x16, rr, a.dp, ks * 16 + hh * 8, r);
+            }, nks, cb_l, a.dp, a.K, blk, lane);
+          else
+            bi = rescore_block([&](int ks, int hh, float(&r)[8]) {
+              read8(a.src0, rr, a.dp, ks * 16 + hh * 8, true, r);
+            }, nks, cb_l, a.dp, a.K, blk, lane);
+        } else {
+          const float4 *fb = reinterpret_cast<const float4 *>(a.rbuf[l & 1] + blk_off);
+          bi = rescore_block([&](int ks, int hh, float(&r)[8]) {
+            const float4 x = fb[(ks * 2) * 64 + hh * 32 + rl];
+            const float4 y = fb[(ks * 2 + 1) * 64 + hh * 32 + rl];
+            r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+            r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+          }, nks, cb_l, a.dp, a.K, blk, lane);
+        }
+        if ((lane & 31) == rl && bi >= 0 && bi < a.K) bonus = bi;
+      }
+
+      // the row's candidates after ca: half 0's list, half 1's list, then
+      // the rescored block's nearest
+      const int onx = __shfl_xor(nx, 32, 64);
+      const int nx0 = h ? onx : nx;
+      const int nxt = nx + onx;
+      const BandEntry *lst0 = clist + (wave * 64 + (lane & 31)) * kList;
+      const BandEntry *lst1 = lst0 + 32 * kList;
+      auto xc = [&](int j) -> int {
+        if (j < nx0) return lst0[j].base;
+        if (j < nxt) return lst1[j - nx0].base;
+        return bonus;
+      };
+      const int nxa = nxt + (bonus >= 0 ? 1 : 0);
+      if (nxa + 1 > kMaxRescore) rcode = kAuxScan;
+      float srb = 0.f, sdr = 0.f;
       int id;
       if (l == 0) {
         // input rows, based at this wave's first row (clamped into the batch)
-        const int64_t w0 = (int64_t)rb * kRowsPerWG + wave * 32;
-        const int64_t wbase = w0 < a.n ? w0 : a.n - 1;
         const int rrow = (int)(rowc - wbase);
         if (a.x16)
           id = update_staged<KS, RSrc::kRowBF16, true>(bfr, a.x16 + wbase * a.dp, rrow, dst, a.dp,
-                                                       cb_l, c1, c2, v2, lane, ring_lds, wave);
+                                                       cb_l, ca, nxa, xc, lane, ring_lds, wave,
+                                                       srb, sdr);
         else
           id = update_staged<KS, RSrc::kRowF32, true>(bfr, a.src0 + wbase * a.dp, rrow, dst, a.dp,
-                                                      cb_l, c1, c2, v2, lane, ring_lds, wave);
+                                                      cb_l, ca, nxa, xc, lane, ring_lds, wave, srb,
+                                                      sdr);
       } else if (store) {
         id = update_staged<KS, RSrc::kFragMajor, true>(bfr, a.rbuf[l & 1] + blk_off, 0, dst, a.dp,
-                                                       cb_l, c1, c2, v2, lane, ring_lds, wave);
+                                                       cb_l, ca, nxa, xc, lane, ring_lds, wave, srb,
+                                                       sdr);
       } else {
         id = update_staged<KS, RSrc::kFragMajor, false>(bfr, a.rbuf[l & 1] + blk_off, 0, dst,
-                                                         a.dp, cb_l, c1, c2, v2, lane, ring_lds,
-                                                         wave);
+                                                        a.dp, cb_l, ca, nxa, xc, lane, ring_lds,
+                                                        wave, srb, sdr);
       }
-      if (live && h == 0) a.ids[row * a.L + l] = id;
+      rbn2 = halves(srb);
+      drn2 = halves(sdr);
+      if (live && h == 0) {
+        a.ids[row * a.L + l] = id;
+        a.aux[row * a.L + l] = rcode == kAuxScan ? kAuxScan : kAuxOk;
+      }
       if (l + 1 < l_end) {
         // the next level's first stages, into this wave's areas of the ring
         // (its own update is done with them; other waves touch only theirs)
@@ -1048,33 +1431,42 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         });
       }
     } else {
-      if (live && h == 0)
-        a.part[row * splits + sp] = make_float4(S1, __int_as_float(I1), S2, __int_as_float(I2));
+      // this split's record of the row half (merged by split_update_kernel):
+      // [cnt, 0, 0, 0], then the list entries [k1, k2, base, 0]
+      if (live) {
+        float4 *rec = a.part + (((int64_t)row * splits + sp) * 2 + h) * kRecF4;
+        rec[0] = make_float4(__int_as_float(bs.cnt), 0.f, 0.f, 0.f);
+        const int nl = bs.cnt < kList ? bs.cnt : kList;
+        for (int j = 0; j < nl; ++j) {
+          const BandEntry e = mylist[j];
+          rec[1 + j] = make_float4(e.k1, e.k2, __int_as_float(e.base), 0.f);
+        }
+      }
     }
   }
 }
 
-// c ? a : b by components (a select of whole array elements becomes a
-// select of their addresses, which keeps the arrays in scratch memory)
-__device__ __forceinline__ float4 select4(bool c, float4 a, float4 b) {
-  return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
-}
-
-// Split mode, after every split of a level wrote its list: one wave per
-// row, four rows per workgroup.  The wave merges the row's lists, then
-// rescores the two candidates exactly as the fused kernel does: for
+// Split mode, after every split of a level wrote its records: one wave per
+// row, four rows per workgroup.  The wave merges the records of the row's
+// two halves over all splits (the same running minimum, block-second keys
+// and band lists the fused kernel keeps for the whole level), collects the
+// candidates inside the band, rescores a block whose second key lies inside
+// it, and rescores every candidate exactly as the fused kernel does: for
 // candidate c and half h, one lane accumulates (r - c)^2 over features
 // ks*16 + h*8 + e, in order ks, e, with fmaf, and the distance is
-// (half 0) + (half 1).  The smaller distance wins, the lower index on a tie.
-// Every lane loads 16-byte pieces of the row and of both candidates, all in
-// flight at once, and forms r - c for both; the four accumulating lanes read
-// these back from this wave's area of LDS, and the winner's r - c is written
-// from the registers.
+// (half 0) + (half 1).  The smallest distance wins, the lower index on a
+// tie.  Candidates go two at a time: every lane loads 16-byte pieces of the
+// row and of both codewords, all in flight at once, and forms r - c for
+// both; four accumulating lanes read these back from this wave's area of
+// LDS, and the winner's r - c is written from the registers.
 template <int S>
 __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int level, int splits) {
   constexpr int kRow4 = S * kStageCols / 4;  // float4 capacity of a row (dp <= 64 S)
   constexpr int NV = (kRow4 + 63) / 64;      // float4 of a row per lane
-  __shared__ float4 area[4][2][kRow4];       // per wave: r - c1, r - c2
+  constexpr int kMaxCand = 64;
+  __shared__ float4 area[4][2][kRow4];       // per wave: r - c of two candidates
+  __shared__ int cand[4][kMaxCand + 1];
+  __shared__ int ncand[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -1084,90 +1476,187 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   // copy it to scratch)
   const float *src = level == 0 ? a.src0 : (level & 1) ? a.rbuf[1] : a.rbuf[0];
   const float4 *rs = reinterpret_cast<const float4 *>(src + row * a.dp);
-  float4 r[NV], x1[NV], x2[NV];
+  float4 r[NV];
   static_for<0, NV>([&](auto V_) {
     constexpr int v = decltype(V_)::value;
     const int i = lane + 64 * v;
     if (i < dp4) r[v] = rs[i];
   });
 
-  // Lane j merges the lists of splits j, j + 64, ..., then a butterfly
-  // merges the lanes' lists.  Every split holds at least one tile, so its
-  // list has two real, distinct codewords, and with finite scores the two
-  // smallest of all of them under the total order are unique: any merge
-  // order, the fused kernel's included, gives the same pair.
-  float S1 = __builtin_inff(), S2 = __builtin_inff();
-  int I1 = kNoIndex, I2 = kNoIndex;
-  const float4 *pp = a.part + row * splits;
-  for (int sp = lane; sp < splits; sp += 64) {
-    const float4 e = pp[sp];
-    merge_top2(S1, I1, S2, I2, e.x, __float_as_int(e.y), e.z, __float_as_int(e.w));
+  // Lane j reads the records of half j & 1 of splits j/2, j/2 + 32, ...:
+  // the smallest list key of the row ((key, index) order, over both halves),
+  // then with its band, the candidates, the blocks whose second key is
+  // inside the band, and overflow, as the fused kernel finds them from its
+  // one list per half (the union of a half's split lists holds the blocks
+  // its full list would).
+  const int hh = lane & 1;
+  float R1 = __builtin_inff();
+  int I1 = kNoIndex, ovf = 0;
+  for (int sp2 = lane >> 1; sp2 < splits; sp2 += 32) {
+    const float4 *rec = a.part + ((row * splits + sp2) * 2 + hh) * kRecF4;
+    const int c = __float_as_int(rec[0].x);
+    ovf |= c > kList ? 1 : 0;
+    const int nl = c < kList ? c : kList;
+    for (int j = 0; j < nl; ++j) {
+      const float4 e = rec[1 + j];
+      const int i = block_index(e.x, __float_as_int(e.z));
+      if (lex_lt(e.x, i, R1, I1)) {
+        R1 = e.x;
+        I1 = i;
+      }
+    }
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const float u1 = __shfl_xor(S1, off, 64), u2 = __shfl_xor(S2, off, 64);
-    const int j1 = __shfl_xor(I1, off, 64), j2 = __shfl_xor(I2, off, 64);
-    merge_top2(S1, I1, S2, I2, u1, j1, u2, j2);
+    const float oR = __shfl_xor(R1, off, 64);
+    const int oI = __shfl_xor(I1, off, 64);
+    if (lex_lt(oR, oI, R1, I1)) {
+      R1 = oR;
+      I1 = oI;
+    }
   }
-  int c1, c2;
-  bool v2;
-  candidates(I1, I2, a.K, c1, c2, v2);  // c2 == c1 when there is no second
-  c1 = __builtin_amdgcn_readfirstlane(c1);  // (the same in every lane)
-  c2 = __builtin_amdgcn_readfirstlane(c2);
-  const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
-  const float4 *p1 = reinterpret_cast<const float4 *>(cb_l + (int64_t)c1 * a.dp);
-  const float4 *p2 = reinterpret_cast<const float4 *>(cb_l + (int64_t)c2 * a.dp);
-  static_for<0, NV>([&](auto V_) {
-    constexpr int v = decltype(V_)::value;
-    const int i = lane + 64 * v;
-    if (i < dp4) {
-      x1[v] = p1[i];
-      x2[v] = p2[i];
+  const int Im = (I1 >= 0 && I1 < a.K) ? I1 : 0;  // finite inputs always give a valid codeword
+  const float2 st = a.rstat[row];
+  const float band = screen_band(st.x, st.y, a.lstat[4 * level], a.lstat[4 * level + 1], a.d);
+  const float thr = __fadd_rn(R1, band);
+
+  // candidates other than Im (any order; the winner does not depend on it)
+  // and the failing blocks of each half
+  if (lane == 0) ncand[wave] = 0;
+  int nfail = 0, fblk = -1;
+  for (int sp2 = lane >> 1; sp2 < splits; sp2 += 32) {
+    const float4 *rec = a.part + ((row * splits + sp2) * 2 + hh) * kRecF4;
+    const int c = __float_as_int(rec[0].x);
+    const int nl = c < kList ? c : kList;
+    for (int j = 0; j < nl; ++j) {
+      const float4 e = rec[1 + j];
+      const int base = __float_as_int(e.z);
+      if (e.y <= thr) {
+        ++nfail;
+        fblk = base >> 6;
+      } else if (e.x <= thr) {
+        const int idx = block_index(e.x, base);
+        if (idx != Im && idx >= 0 && idx < a.K) {
+          const int pos = atomicAdd(&ncand[wave], 1);
+          if (pos < kMaxCand) cand[wave][pos] = idx;
+        }
+      }
     }
-  });
-  // r - c for both candidates, elementwise in every lane (the residual
-  // of whichever wins), then into this wave's area for the accumulating lanes
-  float4 t1[NV], t2[NV];
-  static_for<0, NV>([&](auto V_) {
-    constexpr int v = decltype(V_)::value;
-    const int i = lane + 64 * v;
-    if (i < dp4) {
-      t1[v] = make_float4(r[v].x - x1[v].x, r[v].y - x1[v].y, r[v].z - x1[v].z, r[v].w - x1[v].w);
-      t2[v] = make_float4(r[v].x - x2[v].x, r[v].y - x2[v].y, r[v].z - x2[v].z, r[v].w - x2[v].w);
-      area[wave][0][i] = t1[v];
-      area[wave][1][i] = t2[v];
-    }
-  });
-  // the area is this wave's alone: order its writes before the reads of
-  // other lanes of the same wave
+  }
+  // per half: failing blocks (counts add; any one of them), overflow
+  int fb_any = fblk;
+#pragma unroll
+  for (int off = 2; off < 64; off <<= 1) {
+    nfail += __shfl_xor(nfail, off, 64);
+    ovf |= __shfl_xor(ovf, off, 64);
+    const int o = __shfl_xor(fb_any, off, 64);
+    fb_any = fb_any >= 0 ? fb_any : o;
+  }
+  const int onf = __shfl_xor(nfail, 1, 64);
+  const int ofb = __shfl_xor(fb_any, 1, 64);
+  ovf |= __shfl_xor(ovf, 1, 64);
+  int rcode;
+  if (ovf || nfail > 1 || onf > 1 || (nfail == 1 && onf == 1 && fb_any != ofb))
+    rcode = kAuxScan;
+  else
+    rcode = nfail ? fb_any : (onf ? ofb : kAuxOk);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float p = 0.f;
-  if (lane < 4) {
-    // lane 2c + h: candidate c + 1, half h
-    const float4 *tl = &area[wave][lane >> 1][(lane & 1) * 2];
-    const int kend = a.dp >> 4;
-#pragma unroll 4
-    for (int ks = 0; ks < kend; ++ks) {
-      const float4 ta = tl[ks * 4], tb = tl[ks * 4 + 1];
-      const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p = fmaf(tv[e], tv[e], p);
-    }
+  int nc = __builtin_amdgcn_readfirstlane(ncand[wave]);
+  if (nc > kMaxCand) {
+    nc = kMaxCand;
+    rcode = kAuxScan;
   }
-  const float d1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 0)) +
-                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 1));
-  const float d2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 2)) +
-                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 3));
-  const bool take2 = v2 && (d2 < d1 || (d2 == d1 && c2 < c1));
+  // (as in the fused kernel: more than kMaxRescore candidates, counting the
+  // rescored block's nearest, leave the level to the exact scan)
+  if (nc + 1 + (rcode >= 0 ? 1 : 0) > kMaxRescore) rcode = kAuxScan;
+  const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
+  if (rcode >= 0) {
+    // a block whose second key is inside the band: its nearest codeword
+    // joins the candidates
+    const float *rrow = src + row * a.dp;
+    const int bi = rescore_block([&](int ks, int h, float(&v)[8]) {
+      read8(rrow, 0, a.dp, ks * 16 + h * 8, true, v);
+    }, a.dp >> 4, cb_l, a.dp, a.K, rcode, lane);
+    if (lane == 0) cand[wave][nc] = bi < a.K ? bi : Im;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    ++nc;
+  }
+
+  // rescoring, two candidates at a time; tw keeps the winner's r - c
+  int best = Im;
+  float dbest = __builtin_inff();
+  float4 tw[NV];
+  for (int j = -1; j < nc; j += 2) {
+    const int ua = __builtin_amdgcn_readfirstlane(j < 0 ? Im : cand[wave][j]);
+    const int ub = __builtin_amdgcn_readfirstlane(j + 1 < nc ? cand[wave][j + 1] : ua);
+    const float4 *p1 = reinterpret_cast<const float4 *>(cb_l + (int64_t)ua * a.dp);
+    const float4 *p2 = reinterpret_cast<const float4 *>(cb_l + (int64_t)ub * a.dp);
+    float4 x1[NV], x2[NV];
+    static_for<0, NV>([&](auto V_) {
+      constexpr int v = decltype(V_)::value;
+      const int i = lane + 64 * v;
+      if (i < dp4) {
+        x1[v] = p1[i];
+        x2[v] = p2[i];
+      }
+    });
+    float4 t1[NV], t2[NV];
+    static_for<0, NV>([&](auto V_) {
+      constexpr int v = decltype(V_)::value;
+      const int i = lane + 64 * v;
+      if (i < dp4) {
+        t1[v] = make_float4(r[v].x - x1[v].x, r[v].y - x1[v].y, r[v].z - x1[v].z, r[v].w - x1[v].w);
+        t2[v] = make_float4(r[v].x - x2[v].x, r[v].y - x2[v].y, r[v].z - x2[v].z, r[v].w - x2[v].w);
+        area[wave][0][i] = t1[v];
+        area[wave][1][i] = t2[v];
+      }
+    });
+    // the area is this wave's alone: order its writes before the reads of
+    // other lanes of the same wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float p = 0.f;
+    if (lane < 4) {
+      // lane 2c + h: candidate c, half h
+      const float4 *tl = &area[wave][lane >> 1][(lane & 1) * 2];
+      const int kend = a.dp >> 4;
+#pragma unroll 4
+      for (int ks = 0; ks < kend; ++ks) {
+        const float4 ta = tl[ks * 4], tb = tl[ks * 4 + 1];
+        const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p = fmaf(tv[e], tv[e], p);
+      }
+    }
+    const float d1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 0)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 1));
+    const float d2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 2)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 3));
+    if (j < 0 || lex_lt(d1, ua, dbest, best)) {
+      best = ua;
+      dbest = d1;
+      static_for<0, NV>([&](auto V_) { tw[decltype(V_)::value] = t1[decltype(V_)::value]; });
+    }
+    if (ub != ua && lex_lt(d2, ub, dbest, best)) {
+      best = ub;
+      dbest = d2;
+      static_for<0, NV>([&](auto V_) { tw[decltype(V_)::value] = t2[decltype(V_)::value]; });
+    }
+    // the accumulating lanes are done with the area before it is rewritten
+    __builtin_amdgcn_wave_barrier();
+  }
   float *dst = level == a.L - 1 ? a.res_final : (level & 1) ? a.rbuf[0] : a.rbuf[1];
   if (dst != nullptr) {
     float4 *ds = reinterpret_cast<float4 *>(dst + row * a.dp);
     static_for<0, NV>([&](auto V_) {
       constexpr int v = decltype(V_)::value;
       const int i = lane + 64 * v;
-      if (i < dp4) ds[i] = select4(take2, t2[v], t1[v]);
+      if (i < dp4) ds[i] = tw[v];
     });
   }
   if (level + 1 < a.L) {
@@ -1179,16 +1668,46 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
       constexpr int v = decltype(V_)::value;
       const int i = lane + 64 * v;
       if (i < dp4) {
-        const float4 t = select4(take2, t2[v], t1[v]);
+        const float4 t = tw[v];
         const bf16x2 lo = {(__bf16)t.x, (__bf16)t.y};
         const bf16x2 hi = {(__bf16)t.z, (__bf16)t.w};
         const int ks = i >> 2, hq = i & 3;
         fr[((ks * 64 + (hq >> 1) * 32 + rl) << 1) + (hq & 1)] =
             make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        area[wave][0][i] = t;
       }
     });
+    // the next level's band inputs, summed as the fused kernel sums them:
+    // lane h over features ks*16 + h*8 + e, in order, then half 0 + half 1
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float srb = 0.f, sdr = 0.f;
+    if (lane < 2) {
+      const float4 *tl = &area[wave][0][lane * 2];
+      const int kend = a.dp >> 4;
+      for (int ks = 0; ks < kend; ++ks) {
+        const float4 ta = tl[ks * 4], tb = tl[ks * 4 + 1];
+        const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float b = bf16_bits_to_f32(f32_to_bf16_bits(tv[e]));
+          const float t = tv[e] - b;
+          srb = fmaf(b, b, srb);
+          sdr = fmaf(t, t, sdr);
+        }
+      }
+    }
+    const float rb0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srb), 0));
+    const float rb1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srb), 1));
+    const float dr0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sdr), 0));
+    const float dr1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sdr), 1));
+    if (lane == 0) a.rstat[row] = make_float2(rb0 + rb1, dr0 + dr1);
   }
-  if (lane == 0) a.ids[row * a.L + level] = take2 ? c2 : c1;
+  if (lane == 0) {
+    a.ids[row * a.L + level] = best;
+    a.aux[row * a.L + level] = rcode == kAuxScan ? kAuxScan : kAuxOk;
+  }
 }
 
 template <int S>

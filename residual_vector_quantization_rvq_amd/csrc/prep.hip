@@ -16,11 +16,14 @@ namespace rvq {
 // stage s, k-step ks), so each wave writes 1 KB contiguous per k-step.  The
 // lane sums the squares of its features in increasing order (fmaf), and
 // ||c||^2 = (half 0) + (half 1).  Padded codewords (index >= K) are zero
-// with norm kPadNorm.
+// with norm kPadNorm.  The tile's largest ||c||^2 and ||c - bf16(c)||^2 over
+// its real codewords go to tstat (terms of the encoder's band bound).
 __global__ __launch_bounds__(256) void prepare_tile_kernel(const float *__restrict__ cb, int L,
                                                            int K, int d, int Kp, int S,
                                                            float *__restrict__ norms,
-                                                           uint4 *__restrict__ stream) {
+                                                           uint4 *__restrict__ stream,
+                                                           float *__restrict__ tstat) {
+  __shared__ float red[2][4];
   const int T = Kp / kTileCw;
   const int l = blockIdx.x / T, t = blockIdx.x % T;
   const int lane = threadIdx.x & 63;
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(256) void prepare_tile_kernel(const float *__restri
   const float *src = cb + ((int64_t)l * K + (real ? k : 0)) * d;
   const bool vec = (d & 3) == 0;
   uint4 *tile = stream + ((int64_t)l * T + t) * (tile_bytes(S) / 16);
-  float acc = 0.f;
+  float acc = 0.f, dacc = 0.f;
   // two stages (eight k-steps) per pass: all sixteen loads are issued before
   // the first is used; the squares are still summed in feature order
   for (int s0 = 0; s0 < S; s0 += 2) {
@@ -59,6 +62,10 @@ __global__ __launch_bounds__(256) void prepare_tile_kernel(const float *__restri
       for (int e = 0; e < 8; e += 2) {
         acc = fmaf(v[u][e], v[u][e], acc);
         acc = fmaf(v[u][e + 1], v[u][e + 1], acc);
+        const float r0 = v[u][e] - bf16_bits_to_f32(f32_to_bf16_bits(v[u][e]));
+        const float r1 = v[u][e + 1] - bf16_bits_to_f32(f32_to_bf16_bits(v[u][e + 1]));
+        dacc = fmaf(r0, r0, dacc);
+        dacc = fmaf(r1, r1, dacc);
         w[e >> 1] = (uint32_t)f32_to_bf16_bits(-2.0f * v[u][e]) |
                     ((uint32_t)f32_to_bf16_bits(-2.0f * v[u][e + 1]) << 16);
       }
@@ -75,6 +82,53 @@ __global__ __launch_bounds__(256) void prepare_tile_kernel(const float *__restri
     norms[(int64_t)l * Kp + k] = nv;
   }
   tile[j * 64 + lane] = make_uint4(w0, 0u, 0u, 0u);
+  // tile maxima over real codewords (both halves hold the same codeword
+  // total, so the halves' maxima agree on the norm)
+  float m0 = real ? nv : 0.f;
+  float m1 = real ? dacc + __shfl_xor(dacc, 32, 64) : 0.f;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
+    m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+  }
+  if (lane == 0) {
+    red[0][j] = m0;
+    red[1][j] = m1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    tstat[((int64_t)l * T + t) * 2] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    tstat[((int64_t)l * T + t) * 2 + 1] =
+        fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  }
+}
+
+// lstat[l] = (max ||c||^2, max ||c - bf16(c)||^2, 0, 0) over level l's tiles.
+__global__ __launch_bounds__(256) void level_stat_kernel(const float *__restrict__ tstat, int T,
+                                                         float *__restrict__ lstat) {
+  __shared__ float red[2][4];
+  const int l = blockIdx.x;
+  float m0 = 0.f, m1 = 0.f;
+  for (int t = threadIdx.x; t < T; t += 256) {
+    m0 = fmaxf(m0, tstat[((int64_t)l * T + t) * 2]);
+    m1 = fmaxf(m1, tstat[((int64_t)l * T + t) * 2 + 1]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
+    m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = m0;
+    red[1][threadIdx.x >> 6] = m1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    lstat[l * 4] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    lstat[l * 4 + 1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    lstat[l * 4 + 2] = 0.f;
+    lstat[l * 4 + 3] = 0.f;
+  }
 }
 
 // fp32 codebook copy with row stride dp and zero padding.
@@ -89,7 +143,7 @@ __global__ __launch_bounds__(256) void pad_codebook_kernel(const float *__restri
 }
 
 hipError_t launch_prepare(const float *cb, int L, int K, int d, float *norms, uint8_t *stream,
-                          float *cbpad, int dp, hipStream_t s) {
+                          float *cbpad, int dp, float *tstat, float *lstat, hipStream_t s) {
   if (cbpad) {
     const int64_t rows = (int64_t)L * K;
     pad_codebook_kernel<<<dim3((unsigned)ceil_div(rows * dp, 256)), dim3(256), 0, s>>>(cb, rows, d,
@@ -98,7 +152,8 @@ hipError_t launch_prepare(const float *cb, int L, int K, int d, float *norms, ui
   const int Kp = (int)padded_k(K), S = (int)(padded_d(d) / kStageCols);
   const int64_t tiles = (int64_t)L * (Kp / kTileCw);
   prepare_tile_kernel<<<dim3((unsigned)tiles), dim3(256), 0, s>>>(
-      cb, L, K, d, Kp, S, norms, reinterpret_cast<uint4 *>(stream));
+      cb, L, K, d, Kp, S, norms, reinterpret_cast<uint4 *>(stream), tstat);
+  level_stat_kernel<<<dim3((unsigned)L), dim3(256), 0, s>>>(tstat, Kp / kTileCw, lstat);
   return hipGetLastError();
 }
 

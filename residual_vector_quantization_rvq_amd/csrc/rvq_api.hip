@@ -79,40 +79,49 @@ rvq_status need(const void *p, const char *name, size_t align) {
 // Row stride of the fp32 rows and codewords the encoder reads.
 int32_t row_stride(int32_t d) { return (int32_t)round_up(d, 16); }
 
-// Prepared buffer: norms [L][Kp] fp32, the fragment stream, and (only when
-// d is not a multiple of 16) an fp32 copy of the codebooks with stride dp.
+// Prepared buffer: norms [L][Kp] fp32, the fragment stream, the codebook
+// terms of the band bound (per tile [L][tiles][2], per level [L][4]) and
+// (only when d is not a multiple of 16) an fp32 copy of the codebooks with
+// stride dp.
 struct PreparedLayout {
-  size_t norms_off, stream_off, cbpad_off, total;
+  size_t norms_off, stream_off, tstat_off, lstat_off, cbpad_off, total;
 };
 PreparedLayout prepared_layout(int32_t L, int32_t K, int32_t d) {
   PreparedLayout p;
   p.norms_off = 0;
   p.stream_off = align256((size_t)L * (size_t)padded_k(K) * sizeof(float));
-  p.cbpad_off = p.stream_off + align256((size_t)stream_bytes(L, K, d));
+  p.tstat_off = p.stream_off + align256((size_t)stream_bytes(L, K, d));
+  p.lstat_off = p.tstat_off + align256((size_t)L * (size_t)(padded_k(K) / kTileCw) * 2 * sizeof(float));
+  p.cbpad_off = p.lstat_off + align256((size_t)L * 4 * sizeof(float));
   const int32_t dp = row_stride(d);
   p.total = p.cbpad_off + (dp != d ? align256((size_t)L * K * dp * sizeof(float)) : 0);
   return p;
 }
 
 struct EncodeLayout {
-  size_t r0_off, r1_off, part_off, frag_off, total;
+  size_t r0_off, r1_off, aux_off, part_off, frag_off, rstat_off, total;
 };
 // Workspace: two fp32 residual buffers [n][dp] (level l reads one and
-// writes the other) and, for the split plan, one top-2 list per row and
-// codeword tile [n][tiles] (the largest split count) and the bf16
-// B-fragments of the rows the next sweep reads [n][dp].
-EncodeLayout encode_layout(int64_t n, int32_t d, int32_t K) {
+// writes the other), the repair codes [n][L] and, when some device may run
+// the split plan for n rows, its records (kRecF4 float4 per row, split and
+// row half, for the largest split count), the bf16 B-fragments of the rows
+// the next sweep reads [n][dp] and the rows' band inputs [n] float2.
+EncodeLayout encode_layout(int64_t n, int32_t d, int32_t L, int32_t K) {
   EncodeLayout w;
-  const size_t tiles = (size_t)(padded_k(K) / kTileCw);
   // rows rounded up to whole workgroups: the fused encoder keeps residuals
   // in fragment-major blocks of 32 rows, one set of 4 per workgroup
   const size_t rbytes =
       align256((size_t)round_up(n, kRowsPerWG) * row_stride(d) * sizeof(float));
   w.r0_off = 0;
   w.r1_off = rbytes;
-  w.part_off = 2 * rbytes;
-  w.frag_off = w.part_off + align256((size_t)n * tiles * sizeof(float4));
-  w.total = w.frag_off + align256((size_t)round_up(n, kRowsPerWG) * row_stride(d) * 2);
+  w.aux_off = 2 * rbytes;
+  w.part_off = w.aux_off + align256((size_t)n * L * sizeof(int32_t));
+  const bool split = split_possible(n);
+  w.frag_off =
+      w.part_off + (split ? align256((size_t)split_records(n, K) * kRecF4 * sizeof(float4)) : 0);
+  w.rstat_off =
+      w.frag_off + (split ? align256((size_t)round_up(n, kRowsPerWG) * row_stride(d) * 2) : 0);
+  w.total = w.rstat_off + (split ? align256((size_t)n * sizeof(float2)) : 0);
   if (w.total == 0) w.total = 256;
   return w;
 }
@@ -179,7 +188,8 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
   const int32_t dp = row_stride(d);
   HIP_TRY(launch_prepare(codebooks, L, K, d, (float *)(base + pl.norms_off),
                          (uint8_t *)(base + pl.stream_off),
-                         dp != d ? (float *)(base + pl.cbpad_off) : nullptr, dp, stream),
+                         dp != d ? (float *)(base + pl.cbpad_off) : nullptr, dp,
+                         (float *)(base + pl.tstat_off), (float *)(base + pl.lstat_off), stream),
           "codebook preparation launch");
   return RVQ_OK;
 }
@@ -188,7 +198,7 @@ rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K,
   RVQ_TRY(check_shape(n, d, L, K));
   RVQ_TRY(check_encode_width(d, K));
   if (!bytes) return fail(RVQ_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
-  *bytes = encode_layout(n, d, K).total;
+  *bytes = encode_layout(n, d, L, K).total;
   return RVQ_OK;
 }
 
@@ -209,7 +219,7 @@ rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int3
     if (residual_out && !aligned(residual_out, 4))
       return fail(RVQ_ERR_INVALID_ARGUMENT, "residual_out must be 4-byte aligned");
   }
-  const EncodeLayout wl = encode_layout(n, d, K);
+  const EncodeLayout wl = encode_layout(n, d, L, K);
   RVQ_TRY(need(workspace, "workspace", 256));
   if (workspace_bytes < wl.total)
     return fail(RVQ_ERR_WORKSPACE_TOO_SMALL, "encode workspace needs %zu bytes (got %zu)",
@@ -235,6 +245,9 @@ rvq_status rvq_encode_profiled(const void *x, rvq_dtype x_dtype, int64_t n, int3
   a.ids = ids;
   a.part = (float4 *)(ws + wl.part_off);
   a.xfrag = (uint4 *)(ws + wl.frag_off);
+  a.lstat = (const float *)((const char *)prepared + pl.lstat_off);
+  a.rstat = (float2 *)(ws + wl.rstat_off);
+  a.aux = (int32_t *)(ws + wl.aux_off);
   const EncodePlan plan = plan_encode(n, d, K, num_cus());
   HIP_TRY(launch_encode(plan, a, events, stream), "encode launch");
   if (launches) *launches = plan.fused ? 1 : L;

@@ -48,7 +48,7 @@ def test_header_is_plain_c(rvq, tmp_path):
                     "-L", libdir, "-lrvq", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
     al = lambda v: (v + 255) // 256 * 256
-    assert out[0] == "0" and int(out[1]) == al(128 * 4) + al(4096 + 12 * 16384)
+    assert out[0] == "0" and int(out[1]) == al(128 * 4) + al(4096 + 12 * 16384) + al(8) + al(16)
     assert out[2] == "1" and "NULL" in " ".join(out[3:])
 
 
@@ -61,31 +61,48 @@ def test_status_strings(rvq):
 def test_prepared_size_layout(rvq):
     # norms [L][K rounded up to 128] fp32, then per level and 128-codeword
     # tile a 4 KB norm k-step and one 16 KB stage per 64 features (stage
-    # counts 1, 2, 4, 8, 12, 16, 18, 20), each part rounded up to 256 bytes
+    # counts 1, 2, 4, 8, 12, 16, 18, 20), the band bound's codebook terms per
+    # tile [L][tiles][2] and per level [L][4] fp32, each part rounded up to
+    # 256 bytes
     al = lambda v: (v + 255) // 256 * 256
     L, K, d = 8, 8192, 1152
-    assert rvq.rvq_prepared_size(L, K, d) == L * K * 4 + L * (K // 128) * (4096 + 18 * 16384)
+    T = K // 128
+    assert rvq.rvq_prepared_size(L, K, d) == (L * K * 4 + L * T * (4096 + 18 * 16384)
+                                              + al(L * T * 8) + al(L * 16))
     # d = 70: 2 stages; rows not a multiple of 16 wide also get an fp32
     # codebook copy with row stride 80
     L, K, d = 3, 300, 70
     assert rvq.rvq_prepared_size(L, K, d) == (al(L * 384 * 4) + al(L * 3 * (4096 + 2 * 16384))
-                                              + al(L * K * 80 * 4))
+                                              + al(L * 3 * 8) + al(L * 16) + al(L * K * 80 * 4))
     # d = 640 needs 10 stages, padded to the next instantiated count (12)
-    assert rvq.rvq_prepared_size(1, 128, 640) == al(128 * 4) + al(4096 + 12 * 16384)
+    assert rvq.rvq_prepared_size(1, 128, 640) == al(128 * 4) + al(4096 + 12 * 16384) + al(8) + al(16)
     with pytest.raises(rvq.RVQError) as e:
         rvq.rvq_prepared_size(1, 128, 1281)
     assert e.value.status == 2
 
 
 def test_encode_workspace_size(rvq):
-    # two fp32 residuals [n rounded up to 128][d rounded up to 16], one
-    # top-2 list per row and 128-codeword tile, and a bf16 copy of the rows
+    # two fp32 residuals [n rounded up to 128][d rounded up to 16], repair
+    # codes [n][L] int32 and, when some device (up to 1024 compute units)
+    # may run n rows in the per-level split plan: 7 float4 records per row,
+    # split and row half for min(tiles, ceil(2048 / row blocks)) splits, a
+    # bf16 copy of the rows and (||r_b||^2, ||dr||^2) per row
     al = lambda v: (v + 255) // 256 * 256
     n, d, L, K = 1000, 64, 4, 256
-    assert rvq.rvq_encode_workspace_size(n, d, L, K) == (2 * al(1024 * 64 * 4) + al(n * 2 * 16)
-                                                        + al(1024 * 64 * 2))
-    assert rvq.rvq_encode_workspace_size(10, 70, 2, 300) == (2 * al(128 * 80 * 4) + al(10 * 3 * 16)
-                                                            + al(128 * 80 * 2))
+    assert rvq.rvq_encode_workspace_size(n, d, L, K) == (
+        2 * al(1024 * 64 * 4) + al(n * L * 4) + al(n * 2 * 2 * 7 * 16) + al(1024 * 64 * 2)
+        + al(n * 8))
+    assert rvq.rvq_encode_workspace_size(10, 70, 2, 300) == (
+        2 * al(128 * 80 * 4) + al(10 * 2 * 4) + al(10 * 3 * 2 * 7 * 16) + al(128 * 80 * 2)
+        + al(10 * 8))
+    # 30,834 rows (241 row blocks): 9 splits at most
+    n = 30834
+    assert rvq.rvq_encode_workspace_size(n, 1152, 8, 8192) == (
+        2 * al(30848 * 1152 * 4) + al(n * 8 * 4) + al(n * 9 * 2 * 7 * 16) + al(30848 * 1152 * 2)
+        + al(n * 8))
+    # 80,000 rows fill any device: no split-plan buffers
+    assert rvq.rvq_encode_workspace_size(80000, 1280, 16, 16384) == (
+        2 * al(80000 * 1280 * 4) + al(80000 * 16 * 4))
     assert rvq.rvq_encode_workspace_size(0, d, L, K) == 256
 
 

@@ -1,0 +1,156 @@
+"""The encoder's candidate band against the fp64 oracle.
+
+The encoder screens codewords with bf16 products and rescores in fp32 every
+codeword whose screening key lies within a bound of the smallest (the bound
+is stated with screen_band in the library's common.h).  These cases are built
+where screening alone picks the wrong codeword, where one 64-codeword block
+holds several candidates, and where the candidates are too many for the
+sweep's list (the level then goes to the exact scan after the launch).  In
+each, the IDs must equal the fp64 oracle's wherever its best-to-second gap
+exceeds 1e-4 ||r||^2, in both encoder modes (1 row: the per-level split
+plan; 20,000 rows: all levels in one launch).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rvq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import residual_vector_quantization_rvq_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def _run(rvq, dev, x, cb):
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    cbd = torch.from_numpy(np.ascontiguousarray(cb)).to(dev)
+    ids, res = rvq.rvq_encode(xd, cbd, rvq.rvq_prepare_codebooks(cbd), residual=True)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), res.cpu().numpy()
+
+
+# 1-D rows and codebooks: (name, row, codebook [K][1], exact nearest).
+# bf16(1 + 2^-8) = 1, so screening sees codewords 0 and 1 as equal and
+# codeword 2 (1 - 2^-8) between them; hi + lo norms order the second case;
+# in the third, the exact distances reverse the screening order.
+HAND = [
+    ("screening_ranks_the_nearest_last", [1 + 2 ** -8], [[1 + 2 ** -8], [1.0], [1 - 2 ** -8]], 0),
+    ("norm_low_part", [1 + 2 ** -8], [[1 + 3 * 2 ** -12], [1 + 2 ** -12], [1 + 2 * 2 ** -12]], 0),
+    ("rescoring_reverses_screening", [1 + 2 ** -6], [[1 + 2 ** -9], [1 + 2 ** -9 + 2 ** -11]], 1),
+]
+
+
+@pytest.mark.parametrize("n", [1, 20000], ids=["split", "fused"])
+@pytest.mark.parametrize("case", HAND, ids=lambda c: c[0])
+def test_hand_worked_cases(rvq, dev, case, n):
+    name, row, book, nearest = case
+    x = np.tile(np.float32(row), (n, 1))
+    cb = np.float32(book)[None]
+    assert oracle.encode(x[:1], cb)["ids"][0, 0] == nearest
+    ids_h, res_h = _run(rvq, dev, x, cb)
+    print(f"[{name} n={n}] gpu {ids_h[0, 0]} nearest {nearest}")
+    assert (ids_h == nearest).all()
+    parity.check_residual(res_h[:1], x[:1], "f32", ids_h[:1], cb)
+
+
+def test_near_equal_scores(rvq, dev):
+    # codewords 1, 1 + 2^-14, 1 + 2^-13 at d = 1024 all round to bf16 1.0;
+    # every fp32 distance here is exact, so the nearest (2) is returned
+    d = 1024
+    x = np.full((1, d), 1 + 2 ** -6, np.float32)
+    cb = np.stack([np.full(d, 1 + e, np.float32) for e in (0.0, 2 ** -14, 2 ** -13)])[None]
+    ids_h, res_h = _run(rvq, dev, x, cb)
+    assert oracle.encode(x, cb)["ids"][0, 0] == 2
+    assert ids_h[0, 0] == 2
+    parity.check_teacher_forced(x, "f32", ids_h, cb)
+
+
+# Rows where bf16 screening ranks the nearest codeword third (found by
+# random sweeps of an encoder that rescored only the two best keys):
+# (seed, n, d, L, K, dtype, row, level, gap / ||r||^2 at least)
+SWEEP_ROWS = [
+    (1017, 23296, 50, 10, 3672, "f32", 16322, 3, 2.3e-4),
+    (1027, 2350, 206, 11, 3721, "bf16", 561, 2, 1.3e-4),
+    (1042, 1080, 450, 7, 1663, "bf16", 79, 0, 1.5e-4),
+    (1004, 436, 149, 5, 4310, "f32", 100, 2, 1.5e-4),
+    (1011, 21998, 1057, 5, 1712, "f32", 19741, 0, 1.1e-4),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP_ROWS, ids=lambda c: f"s{c[0]}_d{c[2]}_row{c[6]}")
+def test_sweep_rows_return_the_nearest(rvq, dev, case):
+    seed, n, d, L, K, dt, row, level, rel = case
+    w = workloads.random_problem(seed, n, d, L, K, x_dtype=dt)
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    ids, res = rvq.rvq_encode(x, cb, rvq.rvq_prepare_codebooks(cb), residual=True)
+    torch.cuda.synchronize()
+    sel = np.array([0, row, n - 1])
+    sub = w.rows(sel)
+    ids_h = ids.cpu().numpy()[sel]
+    ref = oracle.encode(sub.x, sub.codebooks, x_dtype=dt)
+    # the listed level is a strict decision (the gap exceeds 1e-4 ||r||^2)
+    assert ref["gap"][1, level] > rel * 0.99 * ref["rn2"][1, level]
+    stats = parity.check_ids(ids_h, sub.x, dt, w.codebooks, ref=ref)
+    assert ids_h[1, level] == ref["ids"][1, level]
+    res_h = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
+    parity.check_residual(res_h, sub.x, dt, ids_h, w.codebooks)
+    print(f"[sweep row s{seed}] gpu {ids_h[1]} oracle {ref['ids'][1]} {stats}")
+
+
+def _crowd(d, K, L, members, spacing, seed):
+    """A codebook whose level 0 holds `members` codewords near the row x,
+    at squared distances spacing * (1, 2, 3, ...) * ||x||^2 in a shuffled
+    order of their indices, the other codewords far away."""
+    g = np.random.default_rng(seed)
+    x = (1.0 + 0.25 * g.standard_normal(d)).astype(np.float32)
+    cb = (3.0 * g.standard_normal((L, K, d))).astype(np.float32)
+    nx2 = float((x.astype(np.float64) ** 2).sum())
+    for j, k in enumerate(members):
+        u = g.standard_normal(d)
+        u /= np.linalg.norm(u)
+        cb[0, k] = (x + np.sqrt(spacing * (j + 1) * nx2) * u).astype(np.float32)
+    return x[None], cb
+
+
+@pytest.mark.parametrize("n", [1, 20000], ids=["split", "fused"])
+@pytest.mark.parametrize("kind", ["one_block", "two_blocks", "many_blocks", "duplicates"])
+def test_crowded_bands(rvq, dev, kind, n):
+    # one_block: five close codewords in one 64-codeword block (the sweep
+    # keeps two keys per block, so the block is rescored whole); two_blocks:
+    # three in each of two blocks; many_blocks: nine in nine blocks (more
+    # than the rescoring takes); duplicates: nine copies of the nearest
+    # codeword.  The last three leave the level to the exact scan.
+    d, K, L = 64, 1000, 3
+    if kind == "one_block":
+        members = [133, 130, 157, 128, 190]
+    elif kind == "two_blocks":
+        members = [70, 100, 81, 640, 700, 655]
+    else:
+        members = [40, 140, 240, 340, 440, 540, 640, 740, 840]
+    x, cb = _crowd(d, K, L, members, 3e-4, seed=len(kind))
+    if kind == "duplicates":
+        for k in members[1:]:
+            cb[0, k] = cb[0, members[0]]
+    x = np.repeat(x, n, axis=0)
+    ref = oracle.encode(x[:1], cb)
+    want = members[0]
+    assert ref["ids"][0, 0] == want
+    ids_h, res_h = _run(rvq, dev, x, cb)
+    print(f"[crowd {kind} n={n}] gpu {ids_h[0]} oracle {ref['ids'][0]}")
+    assert (ids_h[:, 0] == want).all()
+    assert (ids_h == ids_h[0]).all()
+    parity.check_ids(ids_h[:1], x[:1], "f32", cb, ref=ref)
+    parity.check_residual(res_h[:1], x[:1], "f32", ids_h[:1], cb)

@@ -39,7 +39,6 @@ def _full_parity(rvq, w, dev, tag):
     stats = parity.check_strict_prefix(ids_h, ref)
     parity.check_teacher_forced(w.x, w.x_dtype, ids_h, w.codebooks)
     parity.check_residual(res.cpu().numpy(), w.x, w.x_dtype, ids_h, w.codebooks)
-    scr = parity.check_screened(w.x, w.x_dtype, ids_h, res.cpu().numpy(), w.codebooks)
     out32 = rvq.rvq_decode(ids, cb, torch.float32)
     out16 = rvq.rvq_decode(ids, cb, torch.bfloat16)
     hist, msr = rvq.rvq_level_stats(ids, w.K, x, cb)
@@ -48,7 +47,7 @@ def _full_parity(rvq, w, dev, tag):
     parity.check_decode_bf16(parity.bf16_tensor_bits(out16), ids_h, w.codebooks)
     np.testing.assert_array_equal(hist.cpu().numpy(), oracle.hist(ids_h, w.K))
     parity.check_msr(msr.cpu().numpy(), w.x, w.x_dtype, ids_h, w.codebooks)
-    print(f"[{tag}] {stats} screened {scr}")
+    print(f"[{tag}] {stats}")
     return ids_h, ref
 
 
@@ -88,46 +87,43 @@ def test_random_shapes_full(rvq, dev, case):
 
 
 def test_single_image(rvq, dev):
+    # every row against the fp64 oracle
     w = workloads.single_image()
     ids, res, x, cb, _ = _encode(rvq, w, dev)
     ids_h = ids.cpu().numpy()
-    sel = np.random.default_rng(0).choice(w.N, 96, replace=False)
-    sel.sort()
-    sub = w.rows(sel)
-    ref = oracle.encode(sub.x, sub.codebooks)
-    print("[single_image]", parity.check_strict_prefix(ids_h[sel], ref))
-    parity.check_teacher_forced(sub.x, "f32", ids_h[sel], w.codebooks)
+    print("[single_image]", parity.check_ids(ids_h, w.x, "f32", w.codebooks))
     parity.check_residual(res.cpu().numpy(), w.x, "f32", ids_h, w.codebooks)
-    print("[single_image] screened",
-          parity.check_screened(sub.x, "f32", ids_h[sel], res.cpu().numpy()[sel], w.codebooks))
     out = rvq.rvq_decode(ids, cb, torch.float32)
     torch.cuda.synchronize()
     parity.check_decode_f32(out.cpu().numpy(), ids_h, w.codebooks)
 
 
 def test_native_batch(rvq, dev):
+    # The benchmark workload in the configuration the benchmark times: 2,048
+    # sampled rows (every image's first, middle and last row among them)
+    # against the fp64 oracle, the decode, counts and msr of the step's
+    # one-pass kernel against the oracle on every row, and batch invariance.
     w = workloads.native_batch()
     ids, res, x, cb, prepared = _encode(rvq, w, dev)
     ids_h = ids.cpu().numpy()
-    # oracle on sampled rows: 3 per image (first, middle, last) incl. the batch tail
     off = w.offsets
-    sel = np.unique(np.concatenate([[off[i], (off[i] + off[i + 1]) // 2, off[i + 1] - 1]
-                                    for i in range(16)]))
+    ends = np.concatenate([[off[i], (off[i] + off[i + 1]) // 2, off[i + 1] - 1] for i in range(16)])
+    rest = np.random.default_rng(7).choice(w.N, 2048 - len(np.unique(ends)), replace=False)
+    sel = np.unique(np.concatenate([ends, rest]))
+    while len(sel) < 2048:
+        sel = np.unique(np.concatenate([sel, np.random.default_rng(len(sel)).choice(w.N, 2048 - len(sel))]))
     sub = w.rows(sel)
-    ref = oracle.encode(sub.x, sub.codebooks, x_dtype="bf16")
-    print("[native_batch]", parity.check_strict_prefix(ids_h[sel], ref))
-    parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
+    print("[native_batch]", len(sel), "rows", parity.check_ids(ids_h[sel], sub.x, "bf16", w.codebooks))
     res_sel = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
     parity.check_residual(res_sel, sub.x, "bf16", ids_h[sel], w.codebooks)
-    print("[native_batch] screened",
-          parity.check_screened(sub.x, "bf16", ids_h[sel], res_sel, w.codebooks))
-    out16 = rvq.rvq_decode(ids, cb, torch.bfloat16)
+    # the step's decode + statistics pass, against the oracle
+    out16, hist, msr = rvq.rvq_decode_level_stats(ids, x, cb, torch.bfloat16)
     out32 = rvq.rvq_decode(ids, cb, torch.float32)
-    hist, _ = rvq.rvq_level_stats(ids, w.K)
     torch.cuda.synchronize()
     parity.check_decode_bf16(parity.bf16_tensor_bits(out16), ids_h, w.codebooks)
     parity.check_decode_f32(out32.cpu().numpy(), ids_h, w.codebooks)
     np.testing.assert_array_equal(hist.cpu().numpy(), oracle.hist(ids_h, w.K))
+    parity.check_msr(msr.cpu().numpy(), w.x, "bf16", ids_h, w.codebooks)
     # batch invariance: one image encoded alone gives the same bits
     a, b = int(off[5]), int(off[6])
     ids5, res5 = rvq.rvq_encode(x[a:b].contiguous(), cb, prepared, residual=True)
@@ -137,6 +133,8 @@ def test_native_batch(rvq, dev):
 
 
 def test_bulk_tokenisation_sampled(rvq, dev):
+    # full size (1,048,576 x 1280 bf16, L = 16, K = 16384); 256 sampled rows
+    # (the first and last among them) against the fp64 oracle
     w = workloads.bulk_tokenisation()
     x = parity.x_to_device(w, dev)
     cb = torch.from_numpy(w.codebooks).to(dev)
@@ -145,14 +143,11 @@ def test_bulk_tokenisation_sampled(rvq, dev):
     torch.cuda.synchronize()
     ids_h = ids.cpu().numpy()
     assert ids_h.min() >= 0 and ids_h.max() < w.K
-    sel = np.concatenate([[0, w.N - 1], np.random.default_rng(1).choice(w.N, 6, replace=False)])
-    sel.sort()
+    sel = np.unique(np.concatenate([[0, w.N - 1],
+                                    np.random.default_rng(1).choice(w.N, 254, replace=False)]))
     sub = w.rows(sel)
-    ref = oracle.encode(sub.x, sub.codebooks, x_dtype="bf16")
-    print("[bulk_tokenisation]", parity.check_strict_prefix(ids_h[sel], ref))
-    parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
-    print("[bulk_tokenisation] screened",
-          parity.check_screened(sub.x, "bf16", ids_h[sel], None, w.codebooks))
+    print("[bulk_tokenisation]", len(sel), "rows",
+          parity.check_ids(ids_h[sel], sub.x, "bf16", w.codebooks))
 
 
 def test_decode_heavy(rvq, dev):
@@ -178,12 +173,10 @@ def test_decode_heavy(rvq, dev):
     sids_h = sids.cpu().numpy()
     np.testing.assert_array_equal(h2.cpu().numpy(), oracle.hist(sids_h, w.K))
     parity.check_msr(msr.cpu().numpy(), w.x, "f32", sids_h, w.codebooks)
-    sel2 = np.random.default_rng(3).choice(w.N, 48, replace=False)
+    sel2 = np.random.default_rng(3).choice(w.N, 512, replace=False)
     sel2.sort()
     sub = w.rows(sel2)
-    ref = oracle.encode(sub.x, sub.codebooks)
-    print("[decode_heavy msr subset]", parity.check_strict_prefix(sids_h[sel2], ref))
-    parity.check_teacher_forced(sub.x, "f32", sids_h[sel2], w.codebooks)
+    print("[decode_heavy msr subset]", parity.check_ids(sids_h[sel2], sub.x, "f32", w.codebooks))
 
 
 def test_empty_batch(rvq, dev):
@@ -199,10 +192,10 @@ def test_empty_batch(rvq, dev):
     assert torch.all(msr == 0)
 
 
-def test_duplicate_codewords_pick_a_nearest(rvq, dev):
-    # Exact ties: several IDs are equally correct.  The oracle takes the
-    # lowest index; the GPU must take one of the tied codewords, with the
-    # same (minimal) distance, and the same one every time.
+def test_duplicate_codewords_pick_the_lowest_index(rvq, dev):
+    # Exact ties: the oracle takes the lowest index, and so does the GPU:
+    # every tied codeword is inside the candidate band, their fp32 distances
+    # are equal, and the lower index wins a tie.
     rng = np.random.default_rng(41)
     L, K, d = 2, 600, 64
     cb = rng.standard_normal((L, K, d)).astype(np.float32)
@@ -216,7 +209,7 @@ def test_duplicate_codewords_pick_a_nearest(rvq, dev):
     ids_h = ids.cpu().numpy()
     ref = oracle.encode(x, cb)
     assert np.all(ref["ids"][:, 0] == 10)
-    assert np.all(np.isin(ids_h[:, 0], [10, 300, 599]))
+    np.testing.assert_array_equal(ids_h[:, 0], 10)
     tf = oracle.teacher_forced(x, ids_h, cb)
     assert np.all(tf["excess"][:, 0] == 0.0)
     parity.check_teacher_forced(x, "f32", ids_h, cb)
@@ -293,11 +286,19 @@ def test_prepared_stream_layout(rvq, dev, d):
             np.testing.assert_array_equal(nb[:, :32, 1], lo)
     real = np.arange(Kp) < K
     exact = (cb.astype(np.float64) ** 2).sum(axis=2)
-    np.testing.assert_allclose(norms[:, real], exact, rtol=2e-6)
+    # an fp32 sum of d squares: within (d + 1) 2^-24 of the exact norm
+    np.testing.assert_array_less(np.abs(norms[:, real] - exact), (d + 1) * 2.0 ** -24 * exact + 1e-30)
     np.testing.assert_array_equal(norms[:, ~real], np.float32(3.0e38))
-    # bit for bit the fp32 chain the screening oracle states
-    chain = oracle.screen_sq_chain(cb.reshape(L * K, d)).reshape(L, K)
-    np.testing.assert_array_equal(norms[:, real].view(np.uint32), chain.view(np.uint32))
+    # the band bound's codebook terms per level: max ||c||^2 (the fp32
+    # norms above) and max ||c - bf16(c)||^2 within the fp32 sum bound
+    toff = al(soff + L * T * tb)
+    loff = toff + al(L * T * 2 * 4)
+    lstat = prep[loff:loff + L * 16].view(np.float32).reshape(L, 4)
+    np.testing.assert_array_equal(lstat[:, 0], norms[:, real].max(axis=1))
+    rnd = cb.astype(np.float64) - workloads.f32_from_bf16_bits(workloads.bf16_bits_from_f32(cb))
+    dmax = (rnd ** 2).sum(axis=2).max(axis=1)
+    np.testing.assert_array_less(np.abs(lstat[:, 1] - dmax), (d + 1) * 2.0 ** -24 * dmax + 1e-38)
+    np.testing.assert_array_equal(lstat[:, 2:], 0)
 
 
 EMBED = [
@@ -555,7 +556,6 @@ def test_batch_invariance_across_encoder_modes(rvq, dev):
     parity.check_teacher_forced(sub.x, "bf16", ids_h[sel], w.codebooks)
     res_sel = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
     parity.check_residual(res_sel, sub.x, "bf16", ids_h[sel], w.codebooks)
-    parity.check_screened(sub.x, "bf16", ids_h[sel], res_sel, w.codebooks)
 
 
 # Shapes for the all-levels-in-one-launch encoder (n >= 19,712 rows fills the
@@ -599,8 +599,6 @@ def test_fused_mode_shapes(rvq, dev, case):
     parity.check_teacher_forced(sub.x, dt, ids_h[sel], w.codebooks)
     res_sel = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
     parity.check_residual(res_sel, sub.x, dt, ids_h[sel], w.codebooks)
-    print(f"[fused {w.name}] screened",
-          parity.check_screened(sub.x, dt, ids_h[sel], res_sel, w.codebooks))
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
