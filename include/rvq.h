@@ -367,6 +367,42 @@ rvq_status rvq_stream_encode_to_cache(const char *path, const void *x_host, rvq_
                                       void *workspace, size_t workspace_bytes, hipStream_t stream,
                                       int64_t *chunks_done);
 
+/* ------------------------------------------------------------------------
+ * Token-count-aware packing across data-parallel ranks (host code).
+ *
+ * With the visual tokenizer out of the training graph, every sample's
+ * image-token count is known when batches are packed, so the share of
+ * visual tokens on each data-parallel rank can be kept close to the
+ * batch's ("LongCat-2.5 Released", section 4 "Infrastructure: Under 80 GB
+ * Per Card", "Supernode-aware parallelism", last paragraph; "LongCat-2.5
+ * 发布：面向智能体任务的原生多模态大模型", "Supernode-Aware Parallelism",
+ * last paragraph).  The pages state the goal only; the objective is this
+ * library's reading of it.  Sample i has t_i text and v_i image tokens,
+ * n_i = t_i + v_i; the batch has N = sum n_i tokens, V = sum v_i of them
+ * visual, p = V / N.  Rank r receives N_r tokens, V_r of them visual, and
+ * at most `capacity` tokens.  The planner minimises
+ *     max_r |V_r - p N_r|      (the rank's tokens beyond the batch's
+ *                               modality proportion),
+ * then max_r N_r, computing the excesses exactly in integers
+ * (N (V_r - p N_r) = sum over the rank of v_i N - V n_i).
+ *
+ * text_tokens, image_tokens: host arrays [samples], each >= 0, at most
+ * 2^30 tokens in all.  ranks >= 1.  Inputs of at most exact_max samples
+ * are solved exactly (exhaustive search with a bound; keep exact_max small,
+ * about 12: the search is exponential); larger ones by a greedy
+ * assignment (samples by decreasing modality excess, each to the rank
+ * that keeps its excess smallest) followed by moves and swaps that lower
+ * the largest excess.  rank_of (host, [samples]) receives each sample's
+ * rank.  summary (host, [3], or NULL): max_r |sum of v_i N - V n_i| (the
+ * objective times N), N, and max_r N_r.  Returns RVQ_ERR_INVALID_ARGUMENT
+ * for bad arguments and RVQ_ERR_UNSUPPORTED when a sample exceeds the
+ * capacity, the samples do not fit, or the counts are too large.  No HIP
+ * call; thread-safe.
+ * ---------------------------------------------------------------------- */
+rvq_status rvq_pack_ranks(const int64_t *text_tokens, const int64_t *image_tokens,
+                          int64_t samples, int32_t ranks, int64_t capacity, int32_t exact_max,
+                          int32_t *rank_of, int64_t *summary);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ __all__ = [
     "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_decode_level_stats",
     "rvq_embed_tokens", "rvq_idcache_resume", "rvq_idcache_append", "rvq_idcache_read",
     "rvq_stream_workspace_size", "rvq_stream_encode", "rvq_stream_encode_to_cache",
-    "rvq_status_string",
+    "rvq_pack_ranks", "rvq_status_string",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,7 @@ _lib.rvq_idcache_append.argtypes = [ctypes.c_char_p, _i64, _i32, _i32, _i64, _i6
 _lib.rvq_idcache_read.argtypes = [ctypes.c_char_p, _i64, _i32, _i32, _i64, _p, _pi64]
 _CHUNK_CB = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                              ctypes.c_int64, ctypes.c_void_p)
+_lib.rvq_pack_ranks.argtypes = [_p, _p, _i64, _i32, _i64, _i32, _p, _p]
 _lib.rvq_stream_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _psz]
 _lib.rvq_stream_encode.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _i64,
                                    _i64, _i64, _p, _p, _p, _sz, _p, _pi64]
@@ -90,7 +91,7 @@ for _f in ("rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_s
            "rvq_encode", "rvq_encode_profiled", "rvq_decode", "rvq_level_stats_workspace_size",
            "rvq_level_stats", "rvq_decode_level_stats", "rvq_embed_tokens", "rvq_idcache_resume",
            "rvq_idcache_append", "rvq_idcache_read", "rvq_stream_workspace_size",
-           "rvq_stream_encode", "rvq_stream_encode_to_cache"):
+           "rvq_stream_encode", "rvq_stream_encode_to_cache", "rvq_pack_ranks"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -131,11 +132,36 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
 
 
-def _need_cuda(name: str, t: torch.Tensor) -> None:
+def _need_cuda(name: str, t: torch.Tensor, device: Optional[torch.device] = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_codebooks(codebooks: torch.Tensor, device: Optional[torch.device] = None):
+    """Codebooks are a float32 [L, K, d] device tensor; returns (L, K, d)."""
+    _need_cuda("codebooks", codebooks, device)
+    if codebooks.dtype != torch.float32 or codebooks.dim() != 3:
+        raise ValueError("codebooks must be float32 [L, K, d]")
+    return tuple(int(v) for v in codebooks.shape)
+
+
+def _need_shape(name: str, t: torch.Tensor, shape: tuple, dtype: torch.dtype,
+                device: torch.device) -> None:
+    _need_cuda(name, t, device)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} {list(shape)} (got {t.dtype} {list(t.shape)})")
+
+
+def _need_bytes(name: str, t: torch.Tensor, nbytes: int, device: torch.device) -> None:
+    _need_cuda(name, t, device)
+    if t.dtype != torch.uint8 or t.dim() != 1 or t.numel() < nbytes:
+        raise ValueError(f"{name} must be a uint8 buffer of at least {nbytes} bytes")
 
 
 def rvq_prepared_size(L: int, K: int, d: int) -> int:
@@ -146,9 +172,10 @@ def rvq_prepared_size(L: int, K: int, d: int) -> int:
 
 def rvq_prepare_codebooks(codebooks: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Norms and bf16 copy of a fixed [L, K, d] fp32 codebook set."""
-    _need_cuda("codebooks", codebooks)
-    L, K, d = codebooks.shape
+    L, K, d = _need_codebooks(codebooks)
     nbytes = rvq_prepared_size(L, K, d)
+    if out is not None:
+        _need_bytes("out", out, nbytes, codebooks.device)
     prepared = out if out is not None else torch.empty(nbytes, dtype=torch.uint8,
                                                        device=codebooks.device)
     _check(_lib.rvq_prepare_codebooks(_ptr(codebooks), L, K, d, _ptr(prepared), prepared.numel(),
@@ -171,17 +198,24 @@ def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, prepared: Optional[torc
     distance launch; ``launches``: optional ctypes.c_int32 receiving the
     number of launches recorded (rvq_encode_profiled)."""
     _need_cuda("x", x)
-    _need_cuda("codebooks", codebooks)
-    L, K, d = codebooks.shape
-    n = x.shape[0]
+    dev = x.device
+    L, K, d = _need_codebooks(codebooks, dev)
     if x.dim() != 2 or x.shape[1] != d:
         raise ValueError("x must be [n, d] with the codebooks' d")
+    _dtype_code(x.dtype)
+    n = x.shape[0]
     if prepared is None:
         prepared = rvq_prepare_codebooks(codebooks)
-    dev = x.device
+    _need_bytes("prepared", prepared, rvq_prepared_size(L, K, d), dev)
+    if ids_out is not None:
+        _need_shape("ids_out", ids_out, (n, L), torch.int32, dev)
     ids = ids_out if ids_out is not None else torch.empty((n, L), dtype=torch.int32, device=dev)
     res = torch.empty((n, d), dtype=torch.float32, device=dev) if residual else None
     wbytes = rvq_encode_workspace_size(n, d, L, K)
+    if workspace is not None:
+        _need_cuda("workspace", workspace, dev)
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a uint8 [bytes] tensor")
     if workspace is None or workspace.numel() < wbytes:
         workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
     _check(_lib.rvq_encode_profiled(_ptr(x), _dtype_code(x.dtype), n, d, _ptr(codebooks),
@@ -196,14 +230,18 @@ def rvq_decode(ids: torch.Tensor, codebooks: torch.Tensor, out_dtype: torch.dtyp
                out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Sum of the chosen codewords of the first ``levels`` levels (default all)."""
     _need_cuda("ids", ids)
-    _need_cuda("codebooks", codebooks)
-    L, K, d = codebooks.shape
+    dev = ids.device
+    L, K, d = _need_codebooks(codebooks, dev)
     n = ids.shape[0]
     if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[1] != L:
         raise ValueError("ids must be int32 [n, L]")
     levels = L if levels is None else int(levels)
+    _dtype_code(out_dtype)
+    if bad_ids is not None:
+        _need_shape("bad_ids", bad_ids, (1,), torch.int32, dev)
     if out is None:
-        out = torch.empty((n, d), dtype=out_dtype, device=ids.device)
+        out = torch.empty((n, d), dtype=out_dtype, device=dev)
+    _need_shape("out", out, (n, d), out_dtype, dev)
     _check(_lib.rvq_decode(_ptr(ids), n, _ptr(codebooks), L, K, d, levels, _ptr(out),
                            _dtype_code(out.dtype), _ptr(bad_ids), _stream(ids.device)))
     return out
@@ -219,26 +257,33 @@ def rvq_embed_tokens(ids: torch.Tensor, level_tables: torch.Tensor,
     rows of the per-level tables [L, K, D], a text token (is_visual == 0) is
     row ids[t, 0] of text_table [V, D].  Tables are float32 or bfloat16."""
     _need_cuda("ids", ids)
-    _need_cuda("level_tables", level_tables)
+    dev = ids.device
+    _need_cuda("level_tables", level_tables, dev)
+    if level_tables.dim() != 3:
+        raise ValueError("level_tables must be [L, K, D]")
     L, K, D = level_tables.shape
     if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[1] != L:
         raise ValueError("ids must be int32 [T, L]")
     T = ids.shape[0]
+    _dtype_code(out_dtype)
+    if bad_ids is not None:
+        _need_shape("bad_ids", bad_ids, (1,), torch.int32, dev)
     tdt = _dtype_code(level_tables.dtype)
     V = 0
     if text_table is not None:
-        _need_cuda("text_table", text_table)
+        _need_cuda("text_table", text_table, dev)
         if text_table.dtype != level_tables.dtype or text_table.dim() != 2 or text_table.shape[1] != D:
             raise ValueError("text_table must be [V, D] in the level tables' dtype")
         V = text_table.shape[0]
     if is_visual is not None:
-        _need_cuda("is_visual", is_visual)
+        _need_cuda("is_visual", is_visual, dev)
         if is_visual.dtype == torch.bool:
             is_visual = is_visual.view(torch.uint8)
         if is_visual.dtype != torch.uint8 or is_visual.shape != (T,):
             raise ValueError("is_visual must be uint8 or bool [T]")
     if out is None:
-        out = torch.empty((T, D), dtype=out_dtype, device=ids.device)
+        out = torch.empty((T, D), dtype=out_dtype, device=dev)
+    _need_shape("out", out, (T, D), out_dtype, dev)
     _check(_lib.rvq_embed_tokens(_ptr(ids), _ptr(is_visual), T, L, _ptr(text_table), V,
                                  _ptr(level_tables), K, D, tdt, _ptr(out), _dtype_code(out.dtype),
                                  _ptr(bad_ids), _stream(ids.device)))
@@ -274,6 +319,26 @@ def rvq_idcache_read(path: str, n: int, L: int, K: int, chunk_rows: int):
     return ids, done.value
 
 
+def rvq_pack_ranks(text_tokens, image_tokens, ranks: int, capacity: int, exact_max: int = 12):
+    """Assign samples (text and image token counts, host sequences) to
+    `ranks` data-parallel ranks of at most `capacity` tokens each, keeping
+    every rank's visual share close to the batch's.  Returns (rank of each
+    sample as an int32 numpy array, summary): summary holds "dev" (max over
+    ranks of |V_r - p N_r| times N, an integer), "N" and "max_load"."""
+    import numpy as np
+    t = np.ascontiguousarray(text_tokens, dtype=np.int64)
+    v = np.ascontiguousarray(image_tokens, dtype=np.int64)
+    if t.ndim != 1 or t.shape != v.shape:
+        raise ValueError("text_tokens and image_tokens must be 1-D and of one length")
+    out = np.empty(t.shape[0], dtype=np.int32)
+    summ = np.zeros(3, dtype=np.int64)
+    _check(_lib.rvq_pack_ranks(t.ctypes.data_as(ctypes.c_void_p), v.ctypes.data_as(ctypes.c_void_p),
+                               t.shape[0], int(ranks), int(capacity), int(exact_max),
+                               out.ctypes.data_as(ctypes.c_void_p),
+                               summ.ctypes.data_as(ctypes.c_void_p)))
+    return out, {"dev": int(summ[0]), "N": int(summ[1]), "max_load": int(summ[2])}
+
+
 def rvq_stream_workspace_size(chunk_rows: int, d: int, L: int, K: int) -> int:
     out = ctypes.c_size_t()
     _check(_lib.rvq_stream_workspace_size(chunk_rows, d, L, K, ctypes.byref(out)))
@@ -285,19 +350,20 @@ def _stream_args(x_host: torch.Tensor, codebooks: torch.Tensor, prepared: torch.
                  workspace: Optional[torch.Tensor]):
     if x_host.is_cuda or not x_host.is_contiguous() or x_host.dim() != 2:
         raise ValueError("x_host must be a contiguous [n, d] host tensor")
-    _need_cuda("codebooks", codebooks)
-    _need_cuda("prepared", prepared)
-    L, K, d = codebooks.shape
+    L, K, d = _need_codebooks(codebooks)
     n = x_host.shape[0]
     if x_host.shape[1] != d:
         raise ValueError("x_host width differs from the codebooks'")
+    _dtype_code(x_host.dtype)
+    _need_bytes("prepared", prepared, rvq_prepared_size(L, K, d), codebooks.device)
     if ids_out is None:
         ids_out = torch.empty((n, L), dtype=torch.int32, pin_memory=x_host.is_pinned())
     if ids_out.is_cuda or ids_out.dtype != torch.int32 or ids_out.shape != (n, L):
         raise ValueError("ids_out must be a host int32 [n, L] tensor")
+    wbytes = rvq_stream_workspace_size(chunk_rows, d, L, K)
     if workspace is None:
-        workspace = torch.empty(rvq_stream_workspace_size(chunk_rows, d, L, K),
-                                dtype=torch.uint8, device=codebooks.device)
+        workspace = torch.empty(wbytes, dtype=torch.uint8, device=codebooks.device)
+    _need_bytes("workspace", workspace, wbytes, codebooks.device)
     return n, d, L, K, ids_out, workspace
 
 
@@ -361,21 +427,32 @@ def rvq_level_stats(ids: torch.Tensor, K: int, x: Optional[torch.Tensor] = None,
     """Per-level usage counts [L, K] int64 and, when x is given, the per-level
     mean squared residual [L] fp64."""
     _need_cuda("ids", ids)
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise ValueError("ids must be int32 [n, L]")
     n, L = ids.shape
     dev = ids.device
+    if bad_ids is not None:
+        _need_shape("bad_ids", bad_ids, (1,), torch.int32, dev)
     hist = torch.empty((L, K), dtype=torch.int64, device=dev)
     msr = None
     d = 1
     xdt = RVQ_F32
     if x is not None:
-        _need_cuda("x", x)
+        _need_cuda("x", x, dev)
         if codebooks is None:
             raise ValueError("codebooks are required with x")
-        _need_cuda("codebooks", codebooks)
+        if x.dim() != 2 or x.shape[0] != n:
+            raise ValueError("x must be [n, d] with the IDs' n")
         d = x.shape[1]
+        if _need_codebooks(codebooks, dev) != (L, K, d):
+            raise ValueError(f"codebooks must be float32 [{L}, {K}, {d}] (the IDs' L, K and x's d)")
         xdt = _dtype_code(x.dtype)
         msr = torch.empty((L,), dtype=torch.float64, device=dev)
     wbytes = rvq_level_stats_workspace_size(n, L, K, d, x is not None)
+    if workspace is not None:
+        _need_cuda("workspace", workspace, dev)
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a uint8 [bytes] tensor")
     if workspace is None or workspace.numel() < wbytes:
         workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
     _check(_lib.rvq_level_stats(_ptr(ids), n, L, K, _ptr(hist), _ptr(x), xdt, d, _ptr(codebooks),
@@ -394,20 +471,28 @@ def rvq_decode_level_stats(ids: torch.Tensor, x: torch.Tensor, codebooks: torch.
     [L] fp64 of the same IDs in one gather pass (the same bits as rvq_decode
     followed by rvq_level_stats)."""
     _need_cuda("ids", ids)
-    _need_cuda("x", x)
-    _need_cuda("codebooks", codebooks)
-    L, K, d = codebooks.shape
+    dev = ids.device
+    _need_cuda("x", x, dev)
+    L, K, d = _need_codebooks(codebooks, dev)
     n = ids.shape[0]
     if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[1] != L:
         raise ValueError("ids must be int32 [n, L]")
     if x.dim() != 2 or x.shape[0] != n or x.shape[1] != d:
         raise ValueError("x must be [n, d] with the codebooks' d")
-    dev = ids.device
+    _dtype_code(x.dtype)
+    _dtype_code(out_dtype)
+    if bad_ids is not None:
+        _need_shape("bad_ids", bad_ids, (1,), torch.int32, dev)
     if out is None:
         out = torch.empty((n, d), dtype=out_dtype, device=dev)
+    _need_shape("out", out, (n, d), out_dtype, dev)
     hist = torch.empty((L, K), dtype=torch.int64, device=dev)
     msr = torch.empty((L,), dtype=torch.float64, device=dev)
     wbytes = rvq_level_stats_workspace_size(n, L, K, d, True)
+    if workspace is not None:
+        _need_cuda("workspace", workspace, dev)
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a uint8 [bytes] tensor")
     if workspace is None or workspace.numel() < wbytes:
         workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
     _check(_lib.rvq_decode_level_stats(_ptr(ids), n, _ptr(codebooks), L, K, d, _ptr(out),

@@ -41,7 +41,7 @@ def test_random_shapes_against_the_oracle():
         cb = torch.from_numpy(w.codebooks).to(dev)
         ids, res = rvq.rvq_encode(x, cb, rvq.rvq_prepare_codebooks(cb), residual=True)
         torch.cuda.synchronize()
-        rows = int(max(16, min(256, n, 4e9 / (3.0 * L * K * d))))
+        rows = min(n, int(max(16, min(256, 4e9 / (3.0 * L * K * d)))))
         sel = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(seed).choice(n, rows, replace=False)]))
         sub = w.rows(sel)
         ids_h = ids.cpu().numpy()[sel]
@@ -55,4 +55,5 @@ def test_random_shapes_against_the_oracle():
             raise AssertionError(f"{tag}: {e}") from None
         decisions += st["decisions"]
         strict += st["strict_decisions"]
+        print(f"[sweep] {tag}: {st['decisions']} decisions ok", flush=True)
     print(f"[sweep] {count} shapes, {decisions} sampled decisions, {strict} strict; none broke a rule")
