@@ -368,6 +368,25 @@ rvq_status rvq_stream_encode_to_cache(const char *path, const void *x_host, rvq_
                                       int64_t *chunks_done);
 
 /* ------------------------------------------------------------------------
+ * rvq_encode with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is the library's own
+ * file-scope device array of 256 MiB (268,435,456 bytes; one on every
+ * device the library runs on, held until the process ends): enough for one
+ * image of up to 84 x 84 patches (7,056 rows) at d = 1152, L = 8,
+ * K = 8192.  Arguments, layouts, results and errors are rvq_encode's; a call
+ * whose workspace (rvq_encode_workspace_size) exceeds the array returns
+ * RVQ_ERR_UNSUPPORTED before any HIP call.  No hipMalloc or hipFree.  The
+ * device address of the array is looked up on a device's first call (with
+ * that device current).  Every call on one device shares the array: calls
+ * that overlap on one GPU (several streams or threads) race, and must not
+ * be made.
+ * ---------------------------------------------------------------------- */
+rvq_status rvq_encode_noalloc(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
+                              const float *codebooks, const void *prepared, int32_t L, int32_t K,
+                              int32_t *ids, float *residual_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Token-count-aware packing across data-parallel ranks (host code).
  *
  * With the visual tokenizer out of the training graph, every sample's

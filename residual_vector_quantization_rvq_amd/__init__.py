@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "RVQError", "library_path", "exported_symbols", "RVQ_F32", "RVQ_BF16",
     "rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size", "rvq_encode",
-    "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_decode_level_stats",
+    "rvq_encode_noalloc", "rvq_decode", "rvq_level_stats_workspace_size", "rvq_level_stats",
+    "rvq_decode_level_stats",
     "rvq_embed_tokens", "rvq_idcache_resume", "rvq_idcache_append", "rvq_idcache_read",
     "rvq_stream_workspace_size", "rvq_stream_encode", "rvq_stream_encode_to_cache",
     "rvq_pack_ranks", "rvq_status_string",
@@ -67,6 +68,7 @@ _lib.rvq_encode_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _psz]
 _lib.rvq_encode.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _sz, _p]
 _lib.rvq_encode_profiled.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p,
                                      _sz, _p, _p, ctypes.POINTER(ctypes.c_int32)]
+_lib.rvq_encode_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p]
 _lib.rvq_decode.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _i32, _p, ctypes.c_int, _p, _p]
 _lib.rvq_level_stats_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _psz]
 _lib.rvq_level_stats.argtypes = [_p, _i64, _i32, _i32, _p, _p, ctypes.c_int, _i32, _p, _p, _p,
@@ -88,8 +90,8 @@ _lib.rvq_stream_encode.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _
 _lib.rvq_stream_encode_to_cache.argtypes = [ctypes.c_char_p, _p, ctypes.c_int, _i64, _i32, _p,
                                             _p, _i32, _i32, _p, _i64, _i64, _p, _sz, _p, _pi64]
 for _f in ("rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size",
-           "rvq_encode", "rvq_encode_profiled", "rvq_decode", "rvq_level_stats_workspace_size",
-           "rvq_level_stats", "rvq_decode_level_stats", "rvq_embed_tokens", "rvq_idcache_resume",
+           "rvq_encode", "rvq_encode_noalloc", "rvq_encode_profiled", "rvq_decode",
+           "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_decode_level_stats", "rvq_embed_tokens", "rvq_idcache_resume",
            "rvq_idcache_append", "rvq_idcache_read", "rvq_stream_workspace_size",
            "rvq_stream_encode", "rvq_stream_encode_to_cache", "rvq_pack_ranks"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -223,6 +225,25 @@ def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, prepared: Optional[torc
                                     workspace.numel(), _stream(dev), events,
                                     None if launches is None else ctypes.byref(launches)))
     return (ids, res) if residual else ids
+
+
+def rvq_encode_noalloc(x: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
+                       ids_out: torch.Tensor, residual_out: Optional[torch.Tensor] = None) -> None:
+    """rvq_encode into caller-given outputs with the library's own device
+    scratch as workspace (no device allocation in the call)."""
+    _need_cuda("x", x)
+    dev = x.device
+    L, K, d = _need_codebooks(codebooks, dev)
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError("x must be [n, d] with the codebooks' d")
+    n = x.shape[0]
+    _need_bytes("prepared", prepared, rvq_prepared_size(L, K, d), dev)
+    _need_shape("ids_out", ids_out, (n, L), torch.int32, dev)
+    if residual_out is not None:
+        _need_shape("residual_out", residual_out, (n, d), torch.float32, dev)
+    _check(_lib.rvq_encode_noalloc(_ptr(x), _dtype_code(x.dtype), n, d, _ptr(codebooks),
+                                   _ptr(prepared), L, K, _ptr(ids_out), _ptr(residual_out),
+                                   _stream(dev)))
 
 
 def rvq_decode(ids: torch.Tensor, codebooks: torch.Tensor, out_dtype: torch.dtype = torch.float32,
