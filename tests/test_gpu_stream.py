@@ -1,13 +1,14 @@
 """The streaming encoder and the resumable ID cache on the GPU: chunked
-encoding of host rows gives bit for bit the IDs of one rvq_encode call (the
-encoder is batch-invariant, which test_gpu_parity checks against the oracle),
-and interrupted runs resume to the same result."""
+encoding of host rows gives bit for bit the IDs of one rvq_encode call, and
+sampled rows of every chunk (its first and last rows among them) meet the
+fp64 oracle's ID rules; interrupted runs resume to the same result."""
 import os
 
 import numpy as np
 import pytest
 import torch
 
+import parity
 import workloads
 
 pytestmark = pytest.mark.gpu
@@ -33,6 +34,19 @@ def problem(rvq):
     return w, x_host, cb, prepared, ref
 
 
+def _check_chunks_against_oracle(w, ids, chunk, per_chunk=24, seed=0):
+    """Sampled rows of every chunk, the chunk's first and last rows among
+    them, against the fp64 oracle."""
+    g = np.random.default_rng(seed)
+    sel = []
+    for r0 in range(0, w.N, chunk):
+        r1 = min(w.N, r0 + chunk)
+        sel += [r0, r1 - 1] + list(g.integers(r0, r1, per_chunk))
+    sel = np.unique(np.array(sel))
+    sub = w.rows(sel)
+    return parity.check_ids(np.asarray(ids)[sel], sub.x, "bf16", w.codebooks)
+
+
 @pytest.mark.parametrize("pinned,chunk", [(True, 5000), (False, 12000), (True, 40000)])
 def test_stream_encode_matches_one_call(rvq, problem, pinned, chunk):
     w, x_host, cb, prepared, ref = problem
@@ -45,6 +59,7 @@ def test_stream_encode_matches_one_call(rvq, problem, pinned, chunk):
     assert done == nchunks
     assert seen == [(c, c * chunk, min(chunk, w.N - c * chunk)) for c in range(nchunks)]
     assert torch.equal(ids, ref)
+    print(f"[stream] oracle on sampled rows: {_check_chunks_against_oracle(w, ids.numpy(), chunk)}")
 
 
 def test_stream_encode_stop_and_resume(rvq, problem):
@@ -78,6 +93,7 @@ def test_stream_encode_to_cache_resumes(rvq, problem, tmp_path):
     got, done = rvq.rvq_idcache_read(path, w.N, L, K, chunk)
     assert done == 11
     np.testing.assert_array_equal(got, ref.numpy())
+    print(f"[cache] oracle on sampled rows: {_check_chunks_against_oracle(w, got, chunk, 16, 1)}")
     # nothing left to do
     _, done = rvq.rvq_stream_encode_to_cache(path, x, cb, prepared, chunk)
     assert done == 11
