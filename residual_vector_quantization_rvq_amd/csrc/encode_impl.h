@@ -63,6 +63,9 @@ __device__ __forceinline__ int block_index(float key, int b) {
 // where the epilogue reads them without copies.  A fragment is one 128-bit
 // value (8 bf16 packed in 4 words).
 constexpr int kFragsInAgpr = 64;
+// Sub-tiles of a tile whose keys are formed during the next tile's first
+// stage blocks (2 or 4; the rest right after the tile).
+constexpr int kCarry = 1;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -98,105 +101,191 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // M0 + offset + 16*i: the instruction offset moves the global and the LDS
 // address alike, so M0 is set once.  The scalar-base form keeps the
 // per-lane address at 32 bits, which costs the issuing wave measurably
-// fewer cycles than a 64-bit per-lane address.
-#define RVQ_D0 "s_mov_b32 m0, %[lds]\n\tglobal_load_lds_dwordx4 %[voff], %[gsb]\n\t"
-#define RVQ_D1 "global_load_lds_dwordx4 %[voff], %[gsb] offset:1024\n\t"
-#define RVQ_D2 "global_load_lds_dwordx4 %[voff], %[gsb] offset:2048\n\t"
-#define RVQ_D3 "global_load_lds_dwordx4 %[voff], %[gsb] offset:3072\n\t"
+// fewer cycles than a 64-bit per-lane address.  (Prefix RVQ_DY: with
+// refill loads, RVQ_DN: without.)
+#define RVQ_DY_0 "s_mov_b32 m0, %[lds]\n\tglobal_load_lds_dwordx4 %[voff], %[gsb]\n\t"
+#define RVQ_DY_1 "global_load_lds_dwordx4 %[voff], %[gsb] offset:1024\n\t"
+#define RVQ_DY_2 "global_load_lds_dwordx4 %[voff], %[gsb] offset:2048\n\t"
+#define RVQ_DY_3 "global_load_lds_dwordx4 %[voff], %[gsb] offset:3072\n\t"
+#define RVQ_DN_0 ""
+#define RVQ_DN_1 ""
+#define RVQ_DN_2 ""
+#define RVQ_DN_3 ""
+
+// Epilogue keys.  Accumulator element i of a sub-tile becomes a key: the
+// score with the 5-bit tag t in its low bits (v_and_or), then the block's two
+// smallest keys k2 = med3(k1, k2, key) and k1 = min(k1, key): three VALU ops
+// per score.  Written out: compiled, each min would first canonicalise both
+// operands.
+#define RVQ_KEY(i, t)                                     \
+  "v_and_or_b32 %[key], %[a" #i "], %[keep], " #t "\n\t" \
+  "v_med3_f32 %[k2], %[k1], %[k2], %[key]\n\t"           \
+  "v_min_f32 %[k1], %[k1], %[key]\n\t"
+// A block can carry the keys of the previous tile's sub-tile, one score
+// after each of its sixteen k-step MFMAs, so they issue while the matrix
+// core works.  Prefix RVQ_EL: tags 0..15 (an even sub-tile), RVQ_EH: tags
+// 16..31 (an odd one), RVQ_EN: none.
+#define RVQ_EN_0 ""
+#define RVQ_EN_1 ""
+#define RVQ_EN_2 ""
+#define RVQ_EN_3 ""
+#define RVQ_EN_4 ""
+#define RVQ_EN_5 ""
+#define RVQ_EN_6 ""
+#define RVQ_EN_7 ""
+#define RVQ_EN_8 ""
+#define RVQ_EN_9 ""
+#define RVQ_EN_10 ""
+#define RVQ_EN_11 ""
+#define RVQ_EN_12 ""
+#define RVQ_EN_13 ""
+#define RVQ_EN_14 ""
+#define RVQ_EN_15 ""
+#define RVQ_EL_0 RVQ_KEY(0, 0)
+#define RVQ_EL_1 RVQ_KEY(1, 1)
+#define RVQ_EL_2 RVQ_KEY(2, 2)
+#define RVQ_EL_3 RVQ_KEY(3, 3)
+#define RVQ_EL_4 RVQ_KEY(4, 4)
+#define RVQ_EL_5 RVQ_KEY(5, 5)
+#define RVQ_EL_6 RVQ_KEY(6, 6)
+#define RVQ_EL_7 RVQ_KEY(7, 7)
+#define RVQ_EL_8 RVQ_KEY(8, 8)
+#define RVQ_EL_9 RVQ_KEY(9, 9)
+#define RVQ_EL_10 RVQ_KEY(10, 10)
+#define RVQ_EL_11 RVQ_KEY(11, 11)
+#define RVQ_EL_12 RVQ_KEY(12, 12)
+#define RVQ_EL_13 RVQ_KEY(13, 13)
+#define RVQ_EL_14 RVQ_KEY(14, 14)
+#define RVQ_EL_15 RVQ_KEY(15, 15)
+#define RVQ_EH_0 RVQ_KEY(0, 16)
+#define RVQ_EH_1 RVQ_KEY(1, 17)
+#define RVQ_EH_2 RVQ_KEY(2, 18)
+#define RVQ_EH_3 RVQ_KEY(3, 19)
+#define RVQ_EH_4 RVQ_KEY(4, 20)
+#define RVQ_EH_5 RVQ_KEY(5, 21)
+#define RVQ_EH_6 RVQ_KEY(6, 22)
+#define RVQ_EH_7 RVQ_KEY(7, 23)
+#define RVQ_EH_8 RVQ_KEY(8, 24)
+#define RVQ_EH_9 RVQ_KEY(9, 25)
+#define RVQ_EH_10 RVQ_KEY(10, 26)
+#define RVQ_EH_11 RVQ_KEY(11, 27)
+#define RVQ_EH_12 RVQ_KEY(12, 28)
+#define RVQ_EH_13 RVQ_KEY(13, 29)
+#define RVQ_EH_14 RVQ_KEY(14, 30)
+#define RVQ_EH_15 RVQ_KEY(15, 31)
 
 // A stage inside a tile: p holds its k-step 0 on entry.  Reads are spread
 // one per MFMA, each five MFMAs ahead of its use, and a refill load follows
 // the first MFMA of each k-step: evenly spaced requests keep the LDS queue
 // short.  (Probes of this block measured 682 cycles with reads in bursts of
 // four one k-step ahead, 657 spread four ahead, 635 as here.)
-#define RVQ_STAGE_BODY(NX, D0, D1, D2, D3)                                               \
-  RVQ_WAIT(0) RVQ_RD(t0, addr, 5120) RVQ_RD(t1, addr, 9216) RVQ_MF(c0, p0, b0) D0        \
-  RVQ_RD(t2, addr, 13312) RVQ_MF(c1, p1, b0) RVQ_RD(t3, addr, 17408) RVQ_MF(c2, p2, b0)  \
-  RVQ_RD(t4, addr, 6144) RVQ_MF(c3, p3, b0) RVQ_RD(t5, addr, 10240) RVQ_WAIT(5)          \
-  RVQ_MF(c0, t0, b1) D1 RVQ_RD(t6, addr, 14336) RVQ_WAIT(5) RVQ_MF(c1, t1, b1)           \
-  RVQ_RD(t7, addr, 18432) RVQ_WAIT(5) RVQ_MF(c2, t2, b1) RVQ_RD(t0, addr, 7168)          \
-  RVQ_WAIT(5) RVQ_MF(c3, t3, b1) RVQ_RD(t1, addr, 11264) RVQ_WAIT(5) RVQ_MF(c0, t4, b2)  \
-  D2 RVQ_RD(t2, addr, 15360) RVQ_WAIT(5) RVQ_MF(c1, t5, b2) RVQ_RD(t3, addr, 19456)      \
-  RVQ_WAIT(5) RVQ_MF(c2, t6, b2) NX##_0 RVQ_WAIT(5) RVQ_MF(c3, t7, b2) NX##_1            \
-  RVQ_WAIT(5) RVQ_MF(c0, t0, b3) D3 NX##_2 RVQ_WAIT(5) RVQ_MF(c1, t1, b3) NX##_3         \
-  RVQ_WAIT(5) RVQ_MF(c2, t2, b3) RVQ_WAIT(4) RVQ_MF(c3, t3, b3) RVQ_WAIT(0)             
+#define RVQ_STAGE_BODY(NX, D, E)                                                                 \
+  RVQ_WAIT(0) RVQ_RD(t0, addr, 5120) RVQ_RD(t1, addr, 9216) RVQ_MF(c0, p0, b0) D##_0 E##_0       \
+  RVQ_RD(t2, addr, 13312) RVQ_MF(c1, p1, b0) E##_1 RVQ_RD(t3, addr, 17408) RVQ_MF(c2, p2, b0)    \
+  E##_2 RVQ_RD(t4, addr, 6144) RVQ_MF(c3, p3, b0) E##_3 RVQ_RD(t5, addr, 10240) RVQ_WAIT(5)      \
+  RVQ_MF(c0, t0, b1) D##_1 E##_4 RVQ_RD(t6, addr, 14336) RVQ_WAIT(5) RVQ_MF(c1, t1, b1) E##_5    \
+  RVQ_RD(t7, addr, 18432) RVQ_WAIT(5) RVQ_MF(c2, t2, b1) E##_6 RVQ_RD(t0, addr, 7168)            \
+  RVQ_WAIT(5) RVQ_MF(c3, t3, b1) E##_7 RVQ_RD(t1, addr, 11264) RVQ_WAIT(5) RVQ_MF(c0, t4, b2)    \
+  D##_2 E##_8 RVQ_RD(t2, addr, 15360) RVQ_WAIT(5) RVQ_MF(c1, t5, b2) E##_9                       \
+  RVQ_RD(t3, addr, 19456) RVQ_WAIT(5) RVQ_MF(c2, t6, b2) E##_10 NX##_0 RVQ_WAIT(5)               \
+  RVQ_MF(c3, t7, b2) E##_11 NX##_1 RVQ_WAIT(5) RVQ_MF(c0, t0, b3) D##_3 E##_12 NX##_2            \
+  RVQ_WAIT(5) RVQ_MF(c1, t1, b3) E##_13 NX##_3 RVQ_WAIT(5) RVQ_MF(c2, t2, b3) E##_14 RVQ_WAIT(4) \
+  RVQ_MF(c3, t3, b3) E##_15 RVQ_WAIT(0)
 
 // The stage opening a tile: p holds the norm k-step on entry, and the
-// accumulators start from ||c||^2 (B = ones at k = 0, 1).
+// accumulators start from ||c||^2 (B = ones at k = 0, 1).  Its keys start
+// after five MFMAs, long after the previous tile's last accumulator write
+// has landed.
 #define RVQ_MFN(c, a) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #a "], %[bn], 0\n\t"
-#define RVQ_STAGE0_BODY(NX, D0, D1, D2, D3)                                              \
-  RVQ_WAIT(0) RVQ_RD(t0, addr, 4096) RVQ_RD(t1, addr, 8192) RVQ_MFN(c0, p0)              \
-  RVQ_RD(t2, addr, 12288) RVQ_MFN(c1, p1) RVQ_RD(t3, addr, 16384) RVQ_MFN(c2, p2)        \
-  RVQ_RD(t4, addr, 5120) RVQ_MFN(c3, p3) RVQ_RD(t5, addr, 9216) RVQ_WAIT(5)              \
-  RVQ_MF(c0, t0, b0) D0 RVQ_RD(t6, addr, 13312) RVQ_WAIT(5) RVQ_MF(c1, t1, b0)           \
-  RVQ_RD(t7, addr, 17408) RVQ_WAIT(5) RVQ_MF(c2, t2, b0) RVQ_RD(t0, addr, 6144)          \
-  RVQ_WAIT(5) RVQ_MF(c3, t3, b0) RVQ_RD(t1, addr, 10240) RVQ_WAIT(5) RVQ_MF(c0, t4, b1)  \
-  D1 RVQ_RD(t2, addr, 14336) RVQ_WAIT(5) RVQ_MF(c1, t5, b1) RVQ_RD(t3, addr, 18432)      \
-  RVQ_WAIT(5) RVQ_MF(c2, t6, b1) RVQ_RD(t4, addr, 7168) RVQ_WAIT(5) RVQ_MF(c3, t7, b1)   \
-  RVQ_RD(t5, addr, 11264) RVQ_WAIT(5) RVQ_MF(c0, t0, b2) D2 RVQ_RD(t6, addr, 15360)      \
-  RVQ_WAIT(5) RVQ_MF(c1, t1, b2) RVQ_RD(t7, addr, 19456) RVQ_WAIT(5) RVQ_MF(c2, t2, b2)  \
-  NX##_0 RVQ_WAIT(5) RVQ_MF(c3, t3, b2) NX##_1 RVQ_WAIT(5) RVQ_MF(c0, t4, b3) D3 NX##_2  \
-  RVQ_WAIT(5) RVQ_MF(c1, t5, b3) NX##_3 RVQ_WAIT(5) RVQ_MF(c2, t6, b3) RVQ_WAIT(4)       \
-  RVQ_MF(c3, t7, b3) RVQ_WAIT(0)
+#define RVQ_STAGE0_BODY(NX, D, E)                                                                \
+  RVQ_WAIT(0) RVQ_RD(t0, addr, 4096) RVQ_RD(t1, addr, 8192) RVQ_MFN(c0, p0)                      \
+  RVQ_RD(t2, addr, 12288) RVQ_MFN(c1, p1) RVQ_RD(t3, addr, 16384) RVQ_MFN(c2, p2)                \
+  RVQ_RD(t4, addr, 5120) RVQ_MFN(c3, p3) RVQ_RD(t5, addr, 9216) RVQ_WAIT(5)                      \
+  RVQ_MF(c0, t0, b0) D##_0 E##_0 RVQ_RD(t6, addr, 13312) RVQ_WAIT(5) RVQ_MF(c1, t1, b0) E##_1    \
+  RVQ_RD(t7, addr, 17408) RVQ_WAIT(5) RVQ_MF(c2, t2, b0) E##_2 RVQ_RD(t0, addr, 6144)            \
+  RVQ_WAIT(5) RVQ_MF(c3, t3, b0) E##_3 RVQ_RD(t1, addr, 10240) RVQ_WAIT(5) RVQ_MF(c0, t4, b1)    \
+  D##_1 E##_4 RVQ_RD(t2, addr, 14336) RVQ_WAIT(5) RVQ_MF(c1, t5, b1) E##_5                       \
+  RVQ_RD(t3, addr, 18432) RVQ_WAIT(5) RVQ_MF(c2, t6, b1) E##_6 RVQ_RD(t4, addr, 7168)            \
+  RVQ_WAIT(5) RVQ_MF(c3, t7, b1) E##_7 RVQ_RD(t5, addr, 11264) RVQ_WAIT(5) RVQ_MF(c0, t0, b2)    \
+  D##_2 E##_8 RVQ_RD(t6, addr, 15360) RVQ_WAIT(5) RVQ_MF(c1, t1, b2) E##_9                       \
+  RVQ_RD(t7, addr, 19456) RVQ_WAIT(5) RVQ_MF(c2, t2, b2) E##_10 NX##_0 RVQ_WAIT(5)               \
+  RVQ_MF(c3, t3, b2) E##_11 NX##_1 RVQ_WAIT(5) RVQ_MF(c0, t4, b3) D##_3 E##_12 NX##_2            \
+  RVQ_WAIT(5) RVQ_MF(c1, t5, b3) E##_13 NX##_3 RVQ_WAIT(5) RVQ_MF(c2, t6, b3) E##_14 RVQ_WAIT(4) \
+  RVQ_MF(c3, t7, b3) E##_15 RVQ_WAIT(0)
 
-#define RVQ_TEMPS                                                                          \
-  [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [t4] "=&v"(t[4]), \
-      [t5] "=&v"(t[5]), [t6] "=&v"(t[6]), [t7] "=&v"(t[7])
-#define RVQ_PREF [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3])
+// Operand lists, as function-like macros so that they expand only where
+// the asm statement is formed.
+#define RVQ_OA_W() [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3])
+#define RVQ_OA_RW() [c0] "+v"(c[0]), [c1] "+v"(c[1]), [c2] "+v"(c[2]), [c3] "+v"(c[3])
+#define RVQ_OUT_COMMON                                                                         \
+  [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3]), [t0] "=&v"(t[0]),      \
+      [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [t4] "=&v"(t[4]), [t5] "=&v"(t[5]), \
+      [t6] "=&v"(t[6]), [t7] "=&v"(t[7]), [m0o] "=&{m0}"(m0_out)
+#define RVQ_IN_COMMON(cls)                                                                       \
+  [addr] "v"(addr), [naddr] "v"(naddr), [b0] #cls(b0), [b1] #cls(b1), [b2] #cls(b2),          \
+      [b3] #cls(b3), [gsb] "s"(gsb), [voff] "v"(voff), [lds] "s"(lds)
+#define RVQ_NONE()
+#define RVQ_IN_BN() , [bn] "v"(bn)
+#define RVQ_OUT_KEYS() , [k1] "+v"(k1), [k2] "+v"(k2), [key] "=&v"(key)
+#define RVQ_IN_KEYS_LIST                                                                      \
+  [a0] "v"(e[0]), [a1] "v"(e[1]), [a2] "v"(e[2]), [a3] "v"(e[3]), [a4] "v"(e[4]),               \
+      [a5] "v"(e[5]), [a6] "v"(e[6]), [a7] "v"(e[7]), [a8] "v"(e[8]), [a9] "v"(e[9]),           \
+      [a10] "v"(e[10]), [a11] "v"(e[11]), [a12] "v"(e[12]), [a13] "v"(e[13]), [a14] "v"(e[14]), \
+      [a15] "v"(e[15]), [keep] "s"(keep)
+#define RVQ_IN_KEYS() , RVQ_IN_KEYS_LIST
 
 // FIRST: the stage opens a tile.  NEXT_TILE: the next stage opens a tile.
 // B_IN_AGPR: the stage's row fragments live in AGPRs.  DMA: the block also
-// issues this wave's refill loads (gsb + voff, lds).
-template <bool FIRST, bool NEXT_TILE, bool B_IN_AGPR, bool DMA>
+// issues this wave's refill loads (gsb + voff, lds).  EPI: -1 no keys, 0 / 1
+// the keys of sub-tile accumulator e with tags 0..15 / 16..31 folded into
+// the block's running pair (k1, k2).
+template <bool FIRST, bool NEXT_TILE, bool B_IN_AGPR, bool DMA, int EPI>
 __device__ __forceinline__ void stage_block(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
                                             uint32_t naddr, const u32x4 &bn, const u32x4 &b0,
                                             const u32x4 &b1, const u32x4 &b2, const u32x4 &b3,
-                                            const uint4 *gsb, uint32_t voff, uint32_t lds) {
+                                            const uint4 *gsb, uint32_t voff, uint32_t lds,
+                                            const f32x16 &e, float &k1, float &k2) {
   u32x4 t[8];
   uint32_t m0_out;
-#define RVQ_IN(cls)                                                                        \
-  [addr] "v"(addr), [naddr] "v"(naddr), [b0] cls(b0), [b1] cls(b1), [b2] cls(b2), [b3] cls(b3), \
-      [gsb] "s"(gsb), [voff] "v"(voff), [lds] "s"(lds)
-#define RVQ_OUTSEL_0 \
-  [c0] "=&v"(c[0]), [c1] "=&v"(c[1]), [c2] "=&v"(c[2]), [c3] "=&v"(c[3]), RVQ_PREF, RVQ_TEMPS, [m0o] "=&{m0}"(m0_out)
-#define RVQ_OUTSEL_1 \
-  [c0] "+v"(c[0]), [c1] "+v"(c[1]), [c2] "+v"(c[2]), [c3] "+v"(c[3]), RVQ_PREF, RVQ_TEMPS, [m0o] "=&{m0}"(m0_out)
-#define RVQ_EMIT(BODY, OSEL, CLS, ...)                                                     \
-  asm volatile(BODY : RVQ_OUTSEL_##OSEL : RVQ_IN(CLS) __VA_ARGS__ : "memory")
-#define RVQ_NEXT_SEL(B0DY, NX) \
-  B0DY(NX, RVQ_D0, RVQ_D1, RVQ_D2, RVQ_D3)
-#define RVQ_NEXT_NODMA(B0DY, NX) B0DY(NX, "", "", "", "")
-#define RVQ_CASES(B0DY, OSEL, ...)                                                          \
-  if constexpr (NEXT_TILE) {                                                                \
-    if constexpr (DMA) {                                                                    \
-      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_TILE), OSEL, "a", __VA_ARGS__); \
-      else RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_TILE), OSEL, "v", __VA_ARGS__);              \
-    } else {                                                                                \
-      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_TILE), OSEL, "a", __VA_ARGS__); \
-      else RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_TILE), OSEL, "v", __VA_ARGS__);            \
-    }                                                                                       \
-  } else {                                                                                  \
-    if constexpr (DMA) {                                                                    \
-      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_STAGE), OSEL, "a", __VA_ARGS__); \
-      else RVQ_EMIT(RVQ_NEXT_SEL(B0DY, RVQ_NEXT_STAGE), OSEL, "v", __VA_ARGS__);             \
-    } else {                                                                                \
-      if constexpr (B_IN_AGPR) RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_STAGE), OSEL, "a", __VA_ARGS__); \
-      else RVQ_EMIT(RVQ_NEXT_NODMA(B0DY, RVQ_NEXT_STAGE), OSEL, "v", __VA_ARGS__);           \
-    }                                                                                       \
+  float key;
+  const uint32_t keep = ~31u;
+#define RVQ_SEL4(B, NX, D, E, OA, OK, IB, IK)                                                 \
+  if constexpr (B_IN_AGPR)                                                                    \
+    asm volatile(B(NX, D, E) : OA(), RVQ_OUT_COMMON OK() : RVQ_IN_COMMON(a) IB() IK() : "memory"); \
+  else                                                                                        \
+    asm volatile(B(NX, D, E) : OA(), RVQ_OUT_COMMON OK() : RVQ_IN_COMMON(v) IB() IK() : "memory");
+#define RVQ_SEL3(B, NX, E, OA, OK, IB, IK)                  \
+  if constexpr (DMA) {                                      \
+    RVQ_SEL4(B, NX, RVQ_DY, E, OA, OK, IB, IK)              \
+  } else {                                                  \
+    RVQ_SEL4(B, NX, RVQ_DN, E, OA, OK, IB, IK)              \
   }
-  if constexpr (FIRST) {
-    RVQ_CASES(RVQ_STAGE0_BODY, 0, , [bn] "v"(bn))
+#define RVQ_SEL2(B, E, OA, OK, IB, IK)                      \
+  if constexpr (NEXT_TILE) {                                \
+    RVQ_SEL3(B, RVQ_NEXT_TILE, E, OA, OK, IB, IK)           \
+  } else {                                                  \
+    RVQ_SEL3(B, RVQ_NEXT_STAGE, E, OA, OK, IB, IK)          \
+  }
+#define RVQ_SEL1(E, OK, IK)                                           \
+  if constexpr (FIRST) {                                              \
+    RVQ_SEL2(RVQ_STAGE0_BODY, E, RVQ_OA_W, OK, RVQ_IN_BN, IK)         \
+  } else {                                                            \
+    RVQ_SEL2(RVQ_STAGE_BODY, E, RVQ_OA_RW, OK, RVQ_NONE, IK)          \
+  }
+  if constexpr (EPI < 0) {
+    RVQ_SEL1(RVQ_EN, RVQ_NONE, RVQ_NONE)
+  } else if constexpr (EPI == 0) {
+    RVQ_SEL1(RVQ_EL, RVQ_OUT_KEYS, RVQ_IN_KEYS)
   } else {
-    RVQ_CASES(RVQ_STAGE_BODY, 1, )
+    RVQ_SEL1(RVQ_EH, RVQ_OUT_KEYS, RVQ_IN_KEYS)
   }
-#undef RVQ_CASES
-#undef RVQ_NEXT_NODMA
-#undef RVQ_NEXT_SEL
-#undef RVQ_EMIT
-#undef RVQ_OUTSEL_1
-#undef RVQ_OUTSEL_0
-#undef RVQ_IN
+#undef RVQ_SEL1
+#undef RVQ_SEL2
+#undef RVQ_SEL3
+#undef RVQ_SEL4
   (void)m0_out;
+  (void)key;
+  (void)keep;
 }
 
 // The norm fragments of the tile opening a level (slot base + 16*lane).
@@ -240,14 +329,15 @@ struct RowFrags {
     if constexpr (k < NA) return fa[k];
     else return fv[k - NA];
   }
-  template <int s, int S, bool DMA>
+  template <int s, int S, bool DMA, int EPI = -1>
   __device__ __forceinline__ void stage(f32x16 (&c)[4], u32x4 (&p)[4], uint32_t addr,
                                         uint32_t naddr, const u32x4 &bn, const uint4 *gsb,
-                                        uint32_t voff, uint32_t lds) const {
+                                        uint32_t voff, uint32_t lds, const f32x16 &e, float &k1,
+                                        float &k2) const {
     static_assert(NA % 4 == 0, "a stage's k-steps must share a register file");
-    stage_block<s == 0, s == S - 1, (s * 4 < NA), DMA>(c, p, addr, naddr, bn, get<s * 4>(),
-                                                        get<s * 4 + 1>(), get<s * 4 + 2>(),
-                                                        get<s * 4 + 3>(), gsb, voff, lds);
+    stage_block<s == 0, s == S - 1, (s * 4 < NA), DMA, EPI>(
+        c, p, addr, naddr, bn, get<s * 4>(), get<s * 4 + 1>(), get<s * 4 + 2>(), get<s * 4 + 3>(),
+        gsb, voff, lds, e, k1, k2);
   }};
 
 // Compile-time loop: f(integral_constant<int, i>) for i in [0, N).
@@ -442,7 +532,7 @@ __device__ __forceinline__ void dma16(const uint4 *base, uint32_t voff, uint32_t
 // one statement; the instruction offset moves both addresses.
 __device__ __forceinline__ void dma_stage(const uint4 *gsb, uint32_t voff, uint32_t lds) {
   uint32_t m0_out;
-  asm volatile(RVQ_D0 RVQ_D1 RVQ_D2 RVQ_D3
+  asm volatile(RVQ_DY_0 RVQ_DY_1 RVQ_DY_2 RVQ_DY_3
                : [m0o] "=&{m0}"(m0_out)
                : [gsb] "s"(gsb), [voff] "v"(voff), [lds] "s"(lds)
                : "memory");
@@ -1169,15 +1259,76 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // byte offsets of this wave's lanes in a stage and in a norm block
     const uint32_t soff = (uint32_t)(wave * 256 + lane) * 16u;
     const uint32_t noff = (uint32_t)(wave * 64 + lane) * 16u;
-    // One tile: FIRST / LAST say whether it is the level's first / last tile
-    // (0 no, 1 yes, 2 only known at run time), so the middle tiles carry no
-    // run-time tests of the level's boundaries.
-    auto tile = [&](int tt, auto FIRST_, auto LAST_) {
+    // Epilogue of a tile whose scores are in acc, on its own, for sub-tiles
+    // 0 .. nsub-1: the level's last tile (all four), every tile when a tile
+    // has too few stages to carry keys into the next one, else the
+    // sub-tiles not carried.  Accumulator element i of sub-tile j is
+    // codeword j*32 + (i/4)*8 + h*4 + i%4 of the tile for this lane's row.
+    // Per 64-codeword block p (sub-tiles 2p, 2p+1) the tag jj*16 + i is
+    // unique.  A block left half done (odd nsub) keeps its pair in (ck1, ck2)
+    // for the next tile's first carried stage.
+    float ck1 = __builtin_inff(), ck2 = __builtin_inff();
+    auto epilogue = [&](f32x16(&acc)[4], int tt, auto NSUB_) {
+      constexpr int nsub = decltype(NSUB_)::value;
+      if constexpr (nsub > 0) {
+        mfma_drain(acc);
+        const uint32_t keep = ~31u;
+        static_for<0, nsub>([&](auto J_) {
+          constexpr int j = decltype(J_)::value;
+          if constexpr ((j & 1) == 0) {
+            ck1 = __builtin_inff();
+            ck2 = __builtin_inff();
+          }
+          const f32x16 &e = acc[j];
+          float key;
+          if constexpr ((j & 1) == 0)
+            asm(RVQ_EL_0 RVQ_EL_1 RVQ_EL_2 RVQ_EL_3 RVQ_EL_4 RVQ_EL_5 RVQ_EL_6 RVQ_EL_7 RVQ_EL_8
+                    RVQ_EL_9 RVQ_EL_10 RVQ_EL_11 RVQ_EL_12 RVQ_EL_13 RVQ_EL_14 RVQ_EL_15
+                : [k1] "+v"(ck1), [k2] "+v"(ck2), [key] "=&v"(key)
+                : RVQ_IN_KEYS_LIST);
+          else
+            asm(RVQ_EH_0 RVQ_EH_1 RVQ_EH_2 RVQ_EH_3 RVQ_EH_4 RVQ_EH_5 RVQ_EH_6 RVQ_EH_7 RVQ_EH_8
+                    RVQ_EH_9 RVQ_EH_10 RVQ_EH_11 RVQ_EH_12 RVQ_EH_13 RVQ_EH_14 RVQ_EH_15
+                : [k1] "+v"(ck1), [k2] "+v"(ck2), [key] "=&v"(key)
+                : RVQ_IN_KEYS_LIST);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr ((j & 1) == 1) {
+            const int base = (t0 + tt) * kTileCw + (j >> 1) * 64 + h * 4;
+            // both keys are formed here, key by key (the compiler would
+            // otherwise sink k2's chain into the rare append and keep all
+            // of the block's keys alive)
+            asm volatile("" : "+v"(ck1), "+v"(ck2));
+            band_block(bs, ck1, ck2, base, band, r_other, mylist);
+          }
+        });
+        // the other half's running minimum, for the next tile's blocks (the
+        // exchange completes under that tile's matrix work)
+        if constexpr (nsub == 4) r_other = __shfl_xor(bs.R1, 32, 64);
+      }
+    };
+    // One tile into acc: FIRST / LAST say whether it is the level's first /
+    // last tile (0 no, 1 yes, 2 only known at run time), so the middle tiles
+    // carry no run-time tests of the level's boundaries.  With PREV, the
+    // previous tile's scores are in prev, and this tile's first four stage
+    // blocks form their keys, sub-tile s in block s, between their MFMAs;
+    // the block pair of sub-tiles 0, 1 goes to the band after stage 1, that
+    // of 2, 3 after stage 3.
+    auto tile = [&](int tt, auto FIRST_, auto LAST_, f32x16(&acc)[4], f32x16(&prev)[4],
+                    auto PREV_) {
       constexpr int FIRST = decltype(FIRST_)::value, LAST = decltype(LAST_)::value;
-      f32x16 acc[4];
+      constexpr bool PREV = decltype(PREV_)::value;
+      static_assert(!PREV || S >= 4, "the previous tile's keys need four stages");
       const uint4 *tsb = ls + (int64_t)tt * tile_u4;  // the tile in the stream
       static_for<0, S>([&](auto S_) {
         constexpr int s = decltype(S_)::value;
+        // stage s < kCarry carries sub-tile j of the previous tile
+        constexpr int j = 4 - kCarry + s;
+        constexpr int EPI = (PREV && s < kCarry) ? (j & 1) : -1;
+        const f32x16 &pe = prev[s < kCarry ? j : 0];
+        if constexpr (EPI == 0) {
+          ck1 = __builtin_inff();
+          ck2 = __builtin_inff();
+        }
         const int g = tt * S + s;
         // Stage g+1 must be in LDS for every wave before this stage's block
         // reads ahead into it: wait for this wave's loads of stage g+1 (at
@@ -1208,11 +1359,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // (uniform: read from lane 0 so that it is kept in an SGPR for M0)
         const uint32_t lds =
             __builtin_amdgcn_readfirstlane(ring_lds + prv + kNormBytes + (uint32_t)wave * 4096u);
-        auto with_refill = [&]() {
-          if constexpr (sr == 0)
-            dma16(tsb + dt * tile_u4, noff, ring_lds + prv + (uint32_t)wave * kBlockBytes);
-          bfr.template stage<s, S, true>(acc, pre, addr, naddr, bnorm, gsb, soff, lds);
-        };
         // (the last stage of a level reads ahead into a slot it never uses)
         if constexpr (LAST == 2) {
           // Whether this stage refills is known only at run time.  The block
@@ -1226,87 +1372,70 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
               dma16(tsb + dt * tile_u4, noff, ring_lds + prv + (uint32_t)wave * kBlockBytes);
             dma_stage(gsb, soff, lds);
           }
-          bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsb, soff, lds);
+          bfr.template stage<s, S, false, EPI>(acc, pre, addr, naddr, bnorm, gsb, soff, lds, pe,
+                                               ck1, ck2);
         } else if constexpr (LAST == 0 || s + kAhead < S) {
-          with_refill();
+          if constexpr (sr == 0)
+            dma16(tsb + dt * tile_u4, noff, ring_lds + prv + (uint32_t)wave * kBlockBytes);
+          bfr.template stage<s, S, true, EPI>(acc, pre, addr, naddr, bnorm, gsb, soff, lds, pe,
+                                              ck1, ck2);
         } else {
-          bfr.template stage<s, S, false>(acc, pre, addr, naddr, bnorm, gsb, soff, lds);
+          bfr.template stage<s, S, false, EPI>(acc, pre, addr, naddr, bnorm, gsb, soff, lds, pe,
+                                               ck1, ck2);
+        }
+        if constexpr (EPI == 1) {
+          // a 64-codeword block of the previous tile is complete
+          const int base = (t0 + tt - 1) * kTileCw + (j >> 1) * 64 + h * 4;
+          band_block(bs, ck1, ck2, base, band, r_other, mylist);
+          if constexpr (j == 3) r_other = __shfl_xor(bs.R1, 32, 64);
         }
         prv = cur;
         cur = nxt;
         nxt = nxt == (kSlots - 1) * kSlotBytes ? 0u : nxt + kSlotBytes;
       });
-      mfma_drain(acc);
-      // Epilogue: accumulator element i of sub-tile j is codeword
-      // j*32 + (i/4)*8 + h*4 + i%4 of the tile for this lane's row.  Per
-      // 64-codeword block p (sub-tiles 2p, 2p+1) the tag jj*16 + i is unique.
-      // Each key costs three VALU ops: pack, then the block's two smallest
-      // keys updated with med3 and min.
-      const uint32_t keep = ~31u;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float k1 = __builtin_inff(), k2 = __builtin_inff();
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          // key = score with tag jj*16 + i in its low 5 bits; k2 = the
-          // middle of (k1, k2, key); k1 = min(k1, key).  Written out, one
-          // statement per sub-tile: compiled, each min would first
-          // canonicalise both operands.
-          const f32x16 &c = acc[2 * p + jj];
-          float key;
-#define RVQ_KEY(i, t)                                                   \
-  "v_and_or_b32 %[key], %[a" #i "], %[keep], " #t "\n\t"             \
-  "v_med3_f32 %[k2], %[k1], %[k2], %[key]\n\t"                       \
-  "v_min_f32 %[k1], %[k1], %[key]\n\t"
-#define RVQ_KEY_IN                                                                         \
-  [a0] "v"(c[0]), [a1] "v"(c[1]), [a2] "v"(c[2]), [a3] "v"(c[3]), [a4] "v"(c[4]),         \
-      [a5] "v"(c[5]), [a6] "v"(c[6]), [a7] "v"(c[7]), [a8] "v"(c[8]), [a9] "v"(c[9]),      \
-      [a10] "v"(c[10]), [a11] "v"(c[11]), [a12] "v"(c[12]), [a13] "v"(c[13]),               \
-      [a14] "v"(c[14]), [a15] "v"(c[15]), [keep] "s"(keep)
-          if (jj == 0)
-            asm(RVQ_KEY(0, 0) RVQ_KEY(1, 1) RVQ_KEY(2, 2) RVQ_KEY(3, 3) RVQ_KEY(4, 4) RVQ_KEY(5, 5)
-                    RVQ_KEY(6, 6) RVQ_KEY(7, 7) RVQ_KEY(8, 8) RVQ_KEY(9, 9) RVQ_KEY(10, 10)
-                        RVQ_KEY(11, 11) RVQ_KEY(12, 12) RVQ_KEY(13, 13) RVQ_KEY(14, 14)
-                            RVQ_KEY(15, 15)
-                : [k1] "+v"(k1), [k2] "+v"(k2), [key] "=&v"(key)
-                : RVQ_KEY_IN);
-          else
-            asm(RVQ_KEY(0, 16) RVQ_KEY(1, 17) RVQ_KEY(2, 18) RVQ_KEY(3, 19) RVQ_KEY(4, 20)
-                    RVQ_KEY(5, 21) RVQ_KEY(6, 22) RVQ_KEY(7, 23) RVQ_KEY(8, 24) RVQ_KEY(9, 25)
-                        RVQ_KEY(10, 26) RVQ_KEY(11, 27) RVQ_KEY(12, 28) RVQ_KEY(13, 29)
-                            RVQ_KEY(14, 30) RVQ_KEY(15, 31)
-                : [k1] "+v"(k1), [k2] "+v"(k2), [key] "=&v"(key)
-                : RVQ_KEY_IN);
-#undef RVQ_KEY_IN
-#undef RVQ_KEY
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        const int base = (t0 + tt) * kTileCw + p * 64 + h * 4;
-        // both keys are formed here, key by key (the compiler would
-        // otherwise sink k2's chain into the rare append and keep all of
-        // the block's keys alive)
-        asm volatile("" : "+v"(k1), "+v"(k2));
-        band_block(bs, k1, k2, base, band, r_other, mylist);
-      }
-      // the other half's running minimum, for the next tile's blocks (the
-      // exchange completes under that tile's matrix work)
-      r_other = __shfl_xor(bs.R1, 32, 64);
     };
     using TNo = std::integral_constant<int, 0>;
     using TYes = std::integral_constant<int, 1>;
     using TRun = std::integral_constant<int, 2>;
+    using PNo = std::integral_constant<bool, false>;
+    using PYes = std::integral_constant<bool, true>;
+    // two accumulator sets: tile i writes set i % 2 while its first blocks
+    // read the other's last kCarry sub-tiles; the rest of a tile's epilogue
+    // runs right after it
+    f32x16 accA[4], accB[4];
+    using NAll = std::integral_constant<int, 4>;
+    using NOwn = std::integral_constant<int, 4 - kCarry>;
     if constexpr (S >= kAhead) {
       // with at least kAhead stages per tile only the first and the last
       // tile of a level see its boundaries
       if (ntiles == 1) {
-        tile(0, TYes{}, TYes{});
+        tile(0, TYes{}, TYes{}, accA, accB, PNo{});
+        epilogue(accA, 0, NAll{});
       } else {
-        tile(0, TYes{}, TNo{});
-        for (int tt = 1; tt + 1 < ntiles; ++tt) tile(tt, TNo{}, TNo{});
-        tile(ntiles - 1, TNo{}, TYes{});
+        tile(0, TYes{}, TNo{}, accA, accB, PNo{});
+        epilogue(accA, 0, NOwn{});
+        for (int tt = 1;; tt += 2) {
+          if (tt == ntiles - 1) {
+            tile(tt, TNo{}, TYes{}, accB, accA, PYes{});
+            epilogue(accB, tt, NAll{});
+            break;
+          }
+          tile(tt, TNo{}, TNo{}, accB, accA, PYes{});
+          epilogue(accB, tt, NOwn{});
+          if (tt + 1 == ntiles - 1) {
+            tile(tt + 1, TNo{}, TYes{}, accA, accB, PYes{});
+            epilogue(accA, tt + 1, NAll{});
+            break;
+          }
+          tile(tt + 1, TNo{}, TNo{}, accA, accB, PYes{});
+          epilogue(accA, tt + 1, NOwn{});
+        }
       }
     } else {
-      for (int tt = 0; tt < ntiles; ++tt) tile(tt, TRun{}, TRun{});
+      for (int tt = 0; tt < ntiles; ++tt) {
+        tile(tt, TRun{}, TRun{}, accA, accB, PNo{});
+        epilogue(accA, tt, NAll{});
+      }
     }
 
     if (FUSED) {
