@@ -66,30 +66,49 @@ __global__ __launch_bounds__(256) void fragment_rows_kernel(const float *__restr
 }
 
 // Band inputs of the level-0 rows for split mode (the fused encoder forms
-// them while building its fragments): two lanes per row, lane h summing
-// bf16(v)^2 and (v - bf16(v))^2 over features ks*16 + h*8 + e in order, then
-// half 0 + half 1, as every encoder kernel sums them.
+// them while building its fragments): sum bf16(v)^2 and sum (v - bf16(v))^2
+// of each half, over features ks*16 + h*8 + e in order with fmaf, then
+// half 0 + half 1, as every encoder kernel sums them.  One wave per row:
+// every lane rounds its features into LDS, then lane 2q + h runs the chain
+// of sum q of half h, so one instruction stream serves all four chains.
 __global__ __launch_bounds__(256) void row_stats_kernel(const float *__restrict__ src, int64_t n,
                                                         int dp, float2 *__restrict__ rstat) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t >> 1;
-  const int h = (int)(t & 1);
-  float srb = 0.f, sdr = 0.f;
-  if (row < n) {
-    for (int ks = 0; ks < (dp >> 4); ++ks) {
-      float v[8];
-      read8(src, row, dp, ks * 16 + h * 8, true, v);
+  __shared__ float4 area[4][2][kMaxStages * kStageCols / 4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= n) return;
+  const int dp4 = dp >> 2;
+  const float4 *rs = reinterpret_cast<const float4 *>(src + row * dp);
+  for (int i = lane; i < dp4; i += 64) {
+    const float4 t = rs[i];
+    const float4 b = make_float4(bf16_bits_to_f32(f32_to_bf16_bits(t.x)),
+                                 bf16_bits_to_f32(f32_to_bf16_bits(t.y)),
+                                 bf16_bits_to_f32(f32_to_bf16_bits(t.z)),
+                                 bf16_bits_to_f32(f32_to_bf16_bits(t.w)));
+    area[wave][0][i] = b;
+    area[wave][1][i] = make_float4(t.x - b.x, t.y - b.y, t.z - b.z, t.w - b.w);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float acc = 0.f;
+  if (lane < 4) {
+    const float4 *tl = &area[wave][lane >> 1][(lane & 1) * 2];
+    const int kend = dp >> 4;
+#pragma unroll 4
+    for (int ks = 0; ks < kend; ++ks) {
+      const float4 ta = tl[ks * 4], tb = tl[ks * 4 + 1];
+      const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float b = bf16_bits_to_f32(f32_to_bf16_bits(v[e]));
-        const float u = v[e] - b;
-        srb = fmaf(b, b, srb);
-        sdr = fmaf(u, u, sdr);
-      }
+      for (int e = 0; e < 8; ++e) acc = fmaf(tv[e], tv[e], acc);
     }
   }
-  const float orb = __shfl_xor(srb, 1, 64), odr = __shfl_xor(sdr, 1, 64);
-  if (row < n && h == 0) rstat[row] = make_float2(srb + orb, sdr + odr);
+  const float rb0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
+  const float rb1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 1));
+  const float dr0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 2));
+  const float dr1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 3));
+  if (lane == 0) rstat[row] = make_float2(rb0 + rb1, dr0 + dr1);
 }
 
 // Levels whose candidate band could not be shown complete (repair code
@@ -286,8 +305,7 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
     const int64_t pieces = ceil_div(a.n, kRowsPerWG) * 4 * (a.dp >> 4) * 64;
     fragment_rows_kernel<<<dim3((unsigned)ceil_div(pieces, 256)), dim3(256), 0, s>>>(
         a.src0, a.n, a.dp, a.xfrag, pieces);
-    row_stats_kernel<<<dim3((unsigned)ceil_div(2 * a.n, 256)), dim3(256), 0, s>>>(a.src0, a.n,
-                                                                                a.dp, a.rstat);
+    row_stats_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(a.src0, a.n, a.dp, a.rstat);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

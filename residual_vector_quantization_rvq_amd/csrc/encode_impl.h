@@ -455,26 +455,21 @@ __device__ __forceinline__ void read_src(const uint16_t *src, int64_t row, int d
 
 // The same fragments from the bf16 fragment copy of a block of 32 rows
 // (split mode): k-step ks of lane L is the 16 bytes at blk[ks * 64 + L], so
-// every load of a wave is 1 KB of consecutive bytes.  K-steps past the row
-// (ks >= ksp) are zero.
+// every load of a wave is 1 KB of consecutive bytes.  All KS loads issue
+// back to back, straight into the fragment registers, and nothing waits
+// for them here: each stage block's first use of its four fragments is
+// where the wait goes, so the loads complete under the sweep's first
+// stages.  K-steps past the row (ks >= ksp) load k-step ksp-1 again: their
+// codebook A-fragments are zero, so any finite fragment adds exactly zero.
 template <int KS>
 __device__ __forceinline__ void build_bfrags_frag(RowFrags<KS> &bfr, const uint4 *blk, int ksp,
                                                   int lane) {
-  static_for<0, (KS + 15) / 16>([&](auto G_) {
-    constexpr int g = decltype(G_)::value;
-    constexpr int n = KS - g * 16 < 16 ? KS - g * 16 : 16;
-    u32x4 f[16];
-    static_for<0, n>([&](auto U_) {
-      constexpr int ks = g * 16 + decltype(U_)::value;
-      const bool active = ks < ksp;
-      const uint4 q = blk[(active ? ks : 0) * 64 + lane];
-      f[decltype(U_)::value] = active ? u32x4{q.x, q.y, q.z, q.w} : u32x4{0u, 0u, 0u, 0u};
-    });
-    static_for<0, n>([&](auto U_) {
-      constexpr int ks = g * 16 + decltype(U_)::value;
-      bfr.template set<ks>(f[decltype(U_)::value]);
-    });
-    opaque(blk);
+  static_for<0, KS>([&](auto K_) {
+    constexpr int ks = decltype(K_)::value;
+    const uint4 q = blk[(ks < ksp ? ks : ksp - 1) * 64 + lane];
+    const u32x4 v = u32x4{q.x, q.y, q.z, q.w};
+    if constexpr (ks < RowFrags<KS>::NA) bfr.fa[ks] = v;
+    else bfr.fv[ks - RowFrags<KS>::NA] = v;
   });
 }
 
@@ -549,6 +544,21 @@ __host__ __device__ constexpr int dma_after_next(int s) {
   int c = 0;
   for (int k = 2; k < kAhead; ++k) c += dma_count((s + k) % S);
   return c;
+}
+
+// Split mode, first tile, stage s < kAhead - 1 (stage s+1 still one of the
+// prologue's): a lower bound on the loads this wave issued after stage
+// s+1's, namely the rest of the prologue (stages s+2 .. kAhead-1), the 4S
+// row-fragment loads that follow it, and the refills of stages 0 .. s-1
+// (all refills before the level's end when LAST; capped at the counter's
+// range).
+template <int S, bool LAST>
+__host__ __device__ constexpr int split_after_next(int s) {
+  int c = 4 * S;
+  for (int k = s + 2; k < kAhead; ++k) c += dma_count(k % S);
+  for (int k = 0; k < s; ++k)
+    if (!LAST || k + kAhead < S) c += dma_count((k + kAhead) % S);
+  return c < 63 ? c : 63;
 }
 
 template <int N>
@@ -1339,6 +1349,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         if constexpr (FIRST == 2 || LAST == 2) {
           if (g == 0 || g + kAhead - 1 >= nst) wait_vmcnt<0>();
           else wait_vmcnt<dma_after_next<S>(s)>();
+        } else if constexpr (!FUSED && FIRST == 1 && s + 1 < kAhead &&
+                             !(LAST == 1 && s + kAhead - 1 >= S)) {
+          // the row fragments, issued after the prologue, are still on
+          // their way: stage s+1's loads are older than all of them
+          wait_vmcnt<split_after_next<S, LAST == 1>(s)>();
         } else if constexpr ((FIRST == 1 && s == 0) || (LAST == 1 && s + kAhead - 1 >= S)) {
           wait_vmcnt<0>();
         } else {
@@ -1621,19 +1636,39 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   const int hh = lane & 1;
   float R1 = __builtin_inff();
   int I1 = kNoIndex, ovf = 0;
-  for (int sp2 = lane >> 1; sp2 < splits; sp2 += 32) {
-    const float4 *rec = a.part + ((row * splits + sp2) * 2 + hh) * kRecF4;
-    const int c = __float_as_int(rec[0].x);
+  // (a record is read whole, count and entries at once: its unused entries
+  // are allocated, only never looked at; the lane's first two records stay
+  // in registers for the second pass)
+  auto rec_at = [&](int sp2) { return a.part + ((row * splits + sp2) * 2 + hh) * kRecF4; };
+  float4 rc[2][kRecF4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int sp2 = (lane >> 1) + 32 * q;
+    const float4 *rec = rec_at(sp2 < splits ? sp2 : 0);
+#pragma unroll
+    for (int j = 0; j < kRecF4; ++j) rc[q][j] = rec[j];
+    if (sp2 >= splits) rc[q][0].x = __int_as_float(0);
+  }
+  auto first_pass = [&](const float4(&e)[kRecF4]) {
+    const int c = __float_as_int(e[0].x);
     ovf |= c > kList ? 1 : 0;
-    const int nl = c < kList ? c : kList;
-    for (int j = 0; j < nl; ++j) {
-      const float4 e = rec[1 + j];
-      const int i = block_index(e.x, __float_as_int(e.z));
-      if (lex_lt(e.x, i, R1, I1)) {
-        R1 = e.x;
+#pragma unroll
+    for (int j = 0; j < kList; ++j) {
+      const int i = block_index(e[1 + j].x, __float_as_int(e[1 + j].z));
+      if (j < c && lex_lt(e[1 + j].x, i, R1, I1)) {
+        R1 = e[1 + j].x;
         I1 = i;
       }
     }
+  };
+  first_pass(rc[0]);
+  first_pass(rc[1]);
+  for (int sp2 = (lane >> 1) + 64; sp2 < splits; sp2 += 32) {
+    const float4 *rec = rec_at(sp2);
+    float4 e[kRecF4];
+#pragma unroll
+    for (int j = 0; j < kRecF4; ++j) e[j] = rec[j];
+    first_pass(e);
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -1645,6 +1680,16 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
     }
   }
   const int Im = (I1 >= 0 && I1 < a.K) ? I1 : 0;  // finite inputs always give a valid codeword
+  // the nearest key's codeword, the winner unless another candidate turns
+  // up: its load overlaps the second pass
+  const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
+  const float4 *pim = reinterpret_cast<const float4 *>(cb_l + (int64_t)Im * a.dp);
+  float4 xim[NV];
+  static_for<0, NV>([&](auto V_) {
+    constexpr int v = decltype(V_)::value;
+    const int i = lane + 64 * v;
+    if (i < dp4) xim[v] = pim[i];
+  });
   const float2 st = a.rstat[row];
   const float band = screen_band(st.x, st.y, a.lstat[4 * level], a.lstat[4 * level + 1], a.d);
   const float thr = __fadd_rn(R1, band);
@@ -1653,12 +1698,11 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   // and the failing blocks of each half
   if (lane == 0) ncand[wave] = 0;
   int nfail = 0, fblk = -1;
-  for (int sp2 = lane >> 1; sp2 < splits; sp2 += 32) {
-    const float4 *rec = a.part + ((row * splits + sp2) * 2 + hh) * kRecF4;
-    const int c = __float_as_int(rec[0].x);
+  auto second_pass = [&](const float4(&er)[kRecF4]) {
+    const int c = __float_as_int(er[0].x);
     const int nl = c < kList ? c : kList;
     for (int j = 0; j < nl; ++j) {
-      const float4 e = rec[1 + j];
+      const float4 e = er[1 + j];
       const int base = __float_as_int(e.z);
       if (e.y <= thr) {
         ++nfail;
@@ -1671,6 +1715,15 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
         }
       }
     }
+  };
+  second_pass(rc[0]);
+  second_pass(rc[1]);
+  for (int sp2 = (lane >> 1) + 64; sp2 < splits; sp2 += 32) {
+    const float4 *rec = rec_at(sp2);
+    float4 er[kRecF4];
+#pragma unroll
+    for (int j = 0; j < kRecF4; ++j) er[j] = rec[j];
+    second_pass(er);
   }
   // per half: failing blocks (counts add; any one of them), overflow
   int fb_any = fblk;
@@ -1700,7 +1753,6 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   // (as in the fused kernel: more than kMaxRescore candidates, counting the
   // rescored block's nearest, leave the level to the exact scan)
   if (nc + 1 + (rcode >= 0 ? 1 : 0) > kMaxRescore) rcode = kAuxScan;
-  const float *cb_l = a.cb + (int64_t)level * a.K * a.dp;
   if (rcode >= 0) {
     // a block whose second key is inside the band: its nearest codeword
     // joins the candidates
@@ -1715,11 +1767,17 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
     ++nc;
   }
 
-  // rescoring, two candidates at a time; tw keeps the winner's r - c
+  // rescoring, two candidates at a time; tw keeps the winner's r - c.  A
+  // lone candidate wins without a distance.
   int best = Im;
   float dbest = __builtin_inff();
   float4 tw[NV];
-  for (int j = -1; j < nc; j += 2) {
+  static_for<0, NV>([&](auto V_) {
+    constexpr int v = decltype(V_)::value;
+    tw[v] = make_float4(r[v].x - xim[v].x, r[v].y - xim[v].y, r[v].z - xim[v].z,
+                        r[v].w - xim[v].w);
+  });
+  for (int j = -1; nc > 0 && j < nc; j += 2) {
     const int ua = __builtin_amdgcn_readfirstlane(j < 0 ? Im : cand[wave][j]);
     const int ub = __builtin_amdgcn_readfirstlane(j + 1 < nc ? cand[wave][j + 1] : ua);
     const float4 *p1 = reinterpret_cast<const float4 *>(cb_l + (int64_t)ua * a.dp);
@@ -1729,7 +1787,7 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
       constexpr int v = decltype(V_)::value;
       const int i = lane + 64 * v;
       if (i < dp4) {
-        x1[v] = p1[i];
+        x1[v] = j < 0 ? xim[v] : p1[i];
         x2[v] = p2[i];
       }
     });
@@ -1790,7 +1848,9 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   }
   if (level + 1 < a.L) {
     // bf16 fragment copy for the next level's sweep: the 4 features of a
-    // float4 are half q of lane (h*32 + row%32)'s 16 bytes of k-step ks
+    // float4 are half q of lane (h*32 + row%32)'s 16 bytes of k-step ks.
+    // The same rounding gives the next level's band inputs: every lane puts
+    // b = bf16(t) and u = t - b of its features into this wave's area.
     uint2 *fr = reinterpret_cast<uint2 *>(a.xfrag + (row >> 5) * (a.dp >> 4) * 64);
     const int rl = (int)(row & 31);
     static_for<0, NV>([&](auto V_) {
@@ -1798,39 +1858,40 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
       const int i = lane + 64 * v;
       if (i < dp4) {
         const float4 t = tw[v];
-        const bf16x2 lo = {(__bf16)t.x, (__bf16)t.y};
-        const bf16x2 hi = {(__bf16)t.z, (__bf16)t.w};
+        const uint16_t q0 = f32_to_bf16_bits(t.x), q1 = f32_to_bf16_bits(t.y);
+        const uint16_t q2 = f32_to_bf16_bits(t.z), q3 = f32_to_bf16_bits(t.w);
         const int ks = i >> 2, hq = i & 3;
         fr[((ks * 64 + (hq >> 1) * 32 + rl) << 1) + (hq & 1)] =
-            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-        area[wave][0][i] = t;
+            make_uint2((uint32_t)q0 | ((uint32_t)q1 << 16), (uint32_t)q2 | ((uint32_t)q3 << 16));
+        const float4 b4 = make_float4(bf16_bits_to_f32(q0), bf16_bits_to_f32(q1),
+                                      bf16_bits_to_f32(q2), bf16_bits_to_f32(q3));
+        area[wave][0][i] = b4;
+        area[wave][1][i] = make_float4(t.x - b4.x, t.y - b4.y, t.z - b4.z, t.w - b4.w);
       }
     });
-    // the next level's band inputs, summed as the fused kernel sums them:
-    // lane h over features ks*16 + h*8 + e, in order, then half 0 + half 1
+    // summed as the fused kernel sums them: over features ks*16 + h*8 + e of
+    // half h, in order, with fmaf, then half 0 + half 1; lane 2q + h takes
+    // sum b^2 (q = 0) or sum u^2 (q = 1) of half h, so one instruction
+    // stream runs all four chains
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float srb = 0.f, sdr = 0.f;
-    if (lane < 2) {
-      const float4 *tl = &area[wave][0][lane * 2];
+    float acc = 0.f;
+    if (lane < 4) {
+      const float4 *tl = &area[wave][lane >> 1][(lane & 1) * 2];
       const int kend = a.dp >> 4;
+#pragma unroll 4
       for (int ks = 0; ks < kend; ++ks) {
         const float4 ta = tl[ks * 4], tb = tl[ks * 4 + 1];
         const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float b = bf16_bits_to_f32(f32_to_bf16_bits(tv[e]));
-          const float t = tv[e] - b;
-          srb = fmaf(b, b, srb);
-          sdr = fmaf(t, t, sdr);
-        }
+        for (int e = 0; e < 8; ++e) acc = fmaf(tv[e], tv[e], acc);
       }
     }
-    const float rb0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srb), 0));
-    const float rb1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srb), 1));
-    const float dr0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sdr), 0));
-    const float dr1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sdr), 1));
+    const float rb0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
+    const float rb1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 1));
+    const float dr0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 2));
+    const float dr1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 3));
     if (lane == 0) a.rstat[row] = make_float2(rb0 + rb1, dr0 + dr1);
   }
   if (lane == 0) {
