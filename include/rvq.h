@@ -5,10 +5,11 @@
  * discrete token IDs by residual vector quantization (RVQ): at each level
  * the nearest codeword of that level's codebook is chosen, its index is
  * recorded, and it is subtracted so the residual passes on to the next
- * level ("LongCat-2.5 Native Multimodality for Agentic Tasks", section
+ * level ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型", section
  * "Visual Primitive Modeling", paragraph "Discrete Native Resolution Vision
- * Transformer"; "LongCat-2.5 Open Source Release ...", section "02 Visual
- * Coding and 3D": detail is added level by level).  Token IDs are turned
+ * Transformer"; "LongCat-2.5 Open Source Release: Meituan's 1.6T Multimodal
+ * Agent Model with 1M Context", section "02 Visual Coding and 3D": detail is
+ * added level by level).  Token IDs are turned
  * back into vectors by summing the chosen codewords (same blog, Figure 1:
  * the token sequences are reconstructed).  The tokenizer is fixed and its
  * IDs are precomputed offline (same blog, paragraph "Offline Visual
@@ -248,8 +249,8 @@ rvq_status rvq_decode_level_stats(const int32_t *ids, int64_t n, const float *co
  *
  * Visual signals are multi-level discrete tokens that the backbone takes in
  * the same token format as text, and the visual codebook embeddings are
- * learned jointly with the backbone ("LongCat-2.5 Native Multimodality for
- * Agentic Tasks", section "Visual Primitive Modeling", paragraph "Native
+ * learned jointly with the backbone ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型",
+ * section "Visual Primitive Modeling", paragraph "Native
  * Visual Representation").  Token t of a sequence of T tokens becomes one
  * row of D values:
  *   visual token: out[t] = sum over l of level_tables[l][ids[t][l]], added
@@ -281,7 +282,7 @@ rvq_status rvq_embed_tokens(const int32_t *ids, const uint8_t *is_visual, int64_
  * Resumable ID cache (host files).
  *
  * The visual tokenizer is fixed, so token IDs are computed ahead of time
- * and cached offline ("LongCat-2.5 Native Multimodality for Agentic Tasks",
+ * and cached offline ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型",
  * paragraph "Offline Visual Preprocessing").  An ID cache file holds the
  * IDs [n][L] of n rows in chunks of chunk_rows rows (the last chunk may be
  * shorter), appended in chunk order, each with a CRC-32, so that an
@@ -310,9 +311,8 @@ rvq_status rvq_idcache_read(const char *path, int64_t n, int32_t L, int32_t K,
 /* ------------------------------------------------------------------------
  * Streaming encode of host-resident rows (the offline tokenisation pass).
  *
- * Token IDs are computed ahead of training and cached ("LongCat-2.5 Native
- * Multimodality for Agentic Tasks", paragraph "Offline Visual
- * Preprocessing").  rvq_stream_encode encodes rows [0, n) of a host array
+ * Token IDs are computed ahead of training and cached ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型",
+ * paragraph "Offline Visual Preprocessing").  rvq_stream_encode encodes rows [0, n) of a host array
  * in chunks of chunk_rows rows: while chunk c is encoded on `stream`, chunk
  * c+1 is copied in and the IDs of chunk c-1 are copied out, each on a copy
  * stream of its own that the call creates (default priority) and destroys,

@@ -10,11 +10,12 @@ fp64 exactly (fp32 and bf16 values are all representable in fp64) and takes
 the plain means and roundings that the definitions call for.
 
 Sources (pages' titles and sections):
-  * "LongCat-2.5 Native Multimodality for Agentic Tasks", section "Visual
+  * "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", section "Visual
     Primitive Modeling": RVQ turns native-resolution features into
     multi-level discrete tokens; Figure 1: tokens are reconstructed.
-  * "LongCat-2.5 Open Source Release ...", section "02 Visual Coding and
-    3D": residual quantization adds detail level by level.
+  * "LongCat-2.5 Open Source Release: Meituan's 1.6T Multimodal Agent Model
+    with 1M Context", section "02 Visual Coding and 3D": residual
+    quantization adds detail level by level.
   * same blog, "Offline Visual Preprocessing": a fixed tokenizer.
 
 Per-function pins live in ``tests/test_oracle.py``, and

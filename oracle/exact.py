@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY.  Used to pin the fp64 oracle's per-level choices
 and gaps: every fp32 / fp64 input is a dyadic rational, so the distances,
 argmins and residuals below carry no rounding at all.
 
-Definition (greedy residual quantization, "LongCat-2.5 Open Source Release
-...", section "02 Visual Coding and 3D": detail is added level by level):
+Definition (greedy residual quantization, "LongCat-2.5 Open Source Release:
+Meituan's 1.6T Multimodal Agent Model with 1M Context", section "02 Visual
+Coding and 3D": detail is added level by level):
 at each level the residual's squared Euclidean distance to every codeword of
 that level's codebook is taken, the first index of the minimum is chosen,
 the gap is the smallest distance over the other indices minus the minimum,

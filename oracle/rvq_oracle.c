@@ -8,12 +8,13 @@
  *
  * What is computed (the method as the pages describe it, written out as
  * its plain definition):
- *   - "LongCat-2.5 Native Multimodality for Agentic Tasks", section
+ *   - "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", section
  *     "Visual Primitive Modeling", paragraph "Discrete Native Resolution
  *     Vision Transformer": visual features become multi-level discrete
  *     tokens by residual vector quantization (RVQ).
- *   - "LongCat-2.5 Open Source Release ...", section "02 Visual Coding and
- *     3D": the quantizer adds detail level by level.  Read as greedy RVQ:
+ *   - "LongCat-2.5 Open Source Release: Meituan's 1.6T Multimodal Agent
+ *     Model with 1M Context", section "02 Visual Coding and 3D": the
+ *     quantizer adds detail level by level.  Read as greedy RVQ:
  *     at level l pick the codeword of codebook l nearest to the current
  *     residual, record its index, subtract it, pass the residual on.
  *   - Same blog, Figure 1: token sequences are reconstructed; the plainest
@@ -157,8 +158,8 @@ int rvq_oracle_decode(const int32_t *ids, int64_t n, const double *cb,
 }
 
 /*
- * Unified token embedding of a mixed sequence ("LongCat-2.5 Native
- * Multimodality for Agentic Tasks", section "Visual Primitive Modeling":
+ * Unified token embedding of a mixed sequence ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型",
+ * section "Visual Primitive Modeling":
  * visual tokens are multi-level discrete tokens handled in one token format
  * with text, and the visual codebook embeddings are learned with the
  * backbone).  A visual token t takes the sum over levels, in level order,

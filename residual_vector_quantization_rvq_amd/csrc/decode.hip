@@ -1,10 +1,11 @@
 // decode.hip -- token IDs back to vectors by summing the chosen codewords.
 //
-// "LongCat-2.5 Native Multimodality for Agentic Tasks", Figure 1: the
+// "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", Figure 1: the
 // discrete token sequences are reconstructed; with residual quantization
 // the reconstruction from levels 0..levels-1 is the sum of the chosen
 // codewords (prefix sums give the coarse-to-fine reconstructions of "02
-// Visual Coding and 3D" in "LongCat-2.5 Open Source Release ...").
+// Visual Coding and 3D" in "LongCat-2.5 Open Source Release: Meituan's 1.6T
+// Multimodal Agent Model with 1M Context").
 //
 // HBM/MALL-bound gather-sum.  One wave per row (per part of a row when the
 // rows are too few to fill the GPU): the row's IDs are read as

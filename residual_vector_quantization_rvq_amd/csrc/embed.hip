@@ -1,6 +1,6 @@
 // embed.hip -- one embedding row per token of a mixed text / visual sequence.
 //
-// "LongCat-2.5 Native Multimodality for Agentic Tasks", section "Visual
+// "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", section "Visual
 // Primitive Modeling": visual signals become multi-level discrete tokens
 // that the backbone takes in the same token format as text, and (paragraph
 // "Native Visual Representation") the visual codebook embeddings are learned

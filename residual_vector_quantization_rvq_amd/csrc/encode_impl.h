@@ -2,7 +2,7 @@
 // in the encode_s*.hip units).
 #pragma once
 //
-// Method: "LongCat-2.5 Native Multimodality for Agentic Tasks", section
+// Method: "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", section
 // "Visual Primitive Modeling", paragraph "Discrete Native Resolution Vision
 // Transformer" (RVQ on native-resolution features), and "LongCat-2.5 Open
 // Source Release ...", section "02 Visual Coding and 3D" (detail added level

@@ -1,6 +1,6 @@
 // idcache.hip -- resumable on-disk cache of token IDs, written chunk by chunk.
 //
-// "LongCat-2.5 Native Multimodality for Agentic Tasks", paragraph "Offline
+// "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", paragraph "Offline
 // Visual Preprocessing": the visual tokenizer is fixed, so the visual token
 // IDs are computed ahead of training and cached offline.  This file holds
 // such a cache: IDs [n][L] of n rows, produced in chunks of chunk_rows rows,

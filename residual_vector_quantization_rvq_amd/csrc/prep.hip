@@ -1,10 +1,10 @@
 // prep.hip -- codebook preparation (one pass over the fp32 codebooks).
 //
-// The tokenizer is fixed ("LongCat-2.5 Native Multimodality for Agentic
-// Tasks", "Visual Primitive Modeling", paragraph "Offline Visual
-// Preprocessing"), so the data the distance sweep streams is derived once
-// per codebook set: ||c||^2 in fp32 and the fragment-ordered bf16 stream of
-// -2c with the norm k-step (layout in common.h).
+// The tokenizer is fixed ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型",
+// "Visual Primitive Modeling", paragraph "Offline Visual Preprocessing"), so
+// the data the distance sweep streams is derived once per codebook set:
+// ||c||^2 in fp32 and the fragment-ordered bf16 stream of -2c with the norm
+// k-step (layout in common.h).
 #include "common.h"
 
 namespace rvq {

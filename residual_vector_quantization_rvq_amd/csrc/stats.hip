@@ -1,11 +1,11 @@
 // stats.hip -- per-level codeword usage counts and mean squared residual.
 //
 // Visual token counts and codeword usage matter for the pages' offline
-// preprocessing and load balancing ("LongCat-2.5 Native Multimodality for
-// Agentic Tasks", "Visual Primitive Modeling", paragraph "Offline Visual
-// Preprocessing"); the mean squared residual after each level measures how
-// much detail each level adds ("LongCat-2.5 Open Source Release ...", "02
-// Visual Coding and 3D").  Both are exact or fixed-order reductions: counts
+// preprocessing and load balancing ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型",
+// "Visual Primitive Modeling", paragraph "Offline Visual Preprocessing");
+// the mean squared residual after each level measures how much detail each
+// level adds ("LongCat-2.5 Open Source Release: Meituan's 1.6T Multimodal
+// Agent Model with 1M Context", "02 Visual Coding and 3D").  Both are exact or fixed-order reductions: counts
 // are integers, and the fp64 sums are reduced in an order that depends only
 // on n, so results are bitwise reproducible.
 //

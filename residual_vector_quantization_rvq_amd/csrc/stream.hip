@@ -1,7 +1,7 @@
 // stream.hip -- encode host-resident rows chunk by chunk, overlapping the
 // copies with the encoder: the offline tokenisation pass.
 //
-// "LongCat-2.5 Native Multimodality for Agentic Tasks", paragraph "Offline
+// "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", paragraph "Offline
 // Visual Preprocessing": the visual tokenizer is fixed, so the token IDs are
 // computed ahead of training and cached.  The rows of such a pass live in
 // host memory and are far larger than one encoder call needs, so they go

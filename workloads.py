@@ -13,8 +13,8 @@ rounded to fp32; bf16 inputs are the fp32 values rounded to nearest-even on
 the upper 16 bits.  bf16 arrays are stored as ``uint16`` bit patterns.
 
 Shapes follow the pages' setting: native-resolution visual features turned
-into multi-level discrete tokens ("LongCat-2.5 Native Multimodality for
-Agentic Tasks", section "Visual Primitive Modeling", paragraph "Discrete
+into multi-level discrete tokens ("LongCat-2.5 发布：面向智能体任务的原生多模态大模型",
+section "Visual Primitive Modeling", paragraph "Discrete
 Native Resolution Vision Transformer" and Figure 1: images of different
 resolutions, so token counts per image are ragged).  The pages give no D, K,
 L or value distributions; the five workloads below are synthetic stand-ins
