@@ -1044,7 +1044,30 @@ __device__ __forceinline__ int rescore_block(RG &&rget, int nks, const float *cb
   const float *c0 = cb_l + (int64_t)(k0 < K ? k0 : K - 1) * dp;
   const float *c1 = cb_l + (int64_t)(k1 < K ? k1 : K - 1) * dp;
   float p0 = 0.f, p1 = 0.f;
-  for (int ks = 0; ks < nks; ++ks) {
+  // k-steps four at a time, every load of a group issued before its sums
+  // (one round trip per group instead of one per k-step); the sums keep
+  // their order
+  constexpr int G = 4;
+  int ks = 0;
+  for (; ks + G <= nks; ks += G) {
+    float r[G][8], x0[G][8], x1[G][8];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      rget(ks + u, h, r[u]);
+      read8(c0, 0, dp, (ks + u) * 16 + h * 8, true, x0[u]);
+      read8(c1, 0, dp, (ks + u) * 16 + h * 8, true, x1[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = r[u][e] - x0[u][e], v = r[u][e] - x1[u][e];
+        p0 = fmaf(t, t, p0);
+        p1 = fmaf(v, v, p1);
+      }
+    }
+  }
+  for (; ks < nks; ++ks) {
     float r[8], x0[8], x1[8];
     rget(ks, h, r);
     read8(c0, 0, dp, ks * 16 + h * 8, true, x0);
