@@ -16,12 +16,14 @@ Sources (pages' titles and sections):
   * "LongCat-2.5 Open Source Release: Meituan's 1.6T Multimodal Agent Model
     with 1M Context", section "02 Visual Coding and 3D": residual
     quantization adds detail level by level.
-  * same blog, "Offline Visual Preprocessing": a fixed tokenizer.
+  * "LongCat-2.5 发布：面向智能体任务的原生多模态大模型", paragraph "Offline Visual
+    Preprocessing": a fixed tokenizer.
 
 Per-function pins live in ``tests/test_oracle.py``, and
 ``tests/test_oracle_mutants.py`` plants mistakes in the C source that those
-pins must catch; every function here is pinned (no "parity unpinned"
-entry).
+pins must catch; ``packing.py`` (the packing objective and its exhaustive
+search) is pinned by ``tests/test_oracle_packing.py``.  Every function is
+pinned (no "parity unpinned" entry).
 """
 from __future__ import annotations
 
