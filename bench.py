@@ -445,6 +445,15 @@ def main() -> int:
         "encode_vectors_per_s": round(N / (float(np.median(enc_ms)) * 1e-3), 1),
         "decode_level_stats_ms": round(float(np.median(dec_ms)), 4),
     }
+    # the decode stage against HBM: rvq_decode_level_stats reads each row's
+    # bf16 x and IDs, gathers its L codeword rows (fp32) and writes the bf16
+    # decode; the counts read the IDs once more
+    dec_bytes = float(N) * (2 * D + 4 * L + 4 * L * D + 2 * D) + float(N) * 4 * L
+    dec_s = float(np.median(dec_ms)) * 1e-3
+    rec["decode_stage"] = {"call": "rvq_decode_level_stats (decode to bf16 + counts + msr)",
+                           "gather_counted_bytes": dec_bytes,
+                           "gather_counted_GBps": round(dec_bytes / dec_s / 1e9, 1),
+                           "frac_8TBps": round(dec_bytes / dec_s / 8e12, 4)}
     if not args.no_secondary:
         del x, cb, prepared, ws, ws2, ids, out
         torch.cuda.empty_cache()
