@@ -111,107 +111,362 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float *__restrict_
   if (lane == 0) rstat[row] = make_float2(rb0 + rb1, dr0 + dr1);
 }
 
-// Levels whose candidate band could not be shown complete (repair code
-// kAuxScan, rare: a band list overflowed, or two blocks each held two keys
-// inside the band) are taken again by an exact scan: the nearest codeword
-// under the rescoring's own fp32 distance (two half sums in feature order,
-// half 0 + half 1) over all K, the lower index on a tie.  One workgroup per
-// 256 rows finds its rows with such a level and redoes each one: the
-// residual is rebuilt from the row and its IDs with the encoder's fp32
-// subtractions, and once an ID changes every later level is scanned too.
-// Changed IDs, and the final residual when the caller asked for it, are
-// rewritten.
-__global__ __launch_bounds__(256) void repair_kernel(EncodeArgs a) {
-  __shared__ float res[kMaxStages * kStageCols];
-  __shared__ int rows[256];
-  __shared__ int nrows;
-  __shared__ float wd[4];
-  __shared__ int wi[4];
+// ---- exact scans of the levels the sweep could not show complete ----
+//
+// A level with repair code kAuxScan (rare: a band list overflowed, or two
+// blocks each held two keys inside the band) is taken again by an exact
+// scan: the nearest codeword under the rescoring's own fp32 distance (two
+// half sums in feature order, half 0 + half 1) over all K, the lower index
+// on a tie.  The residual a scan needs is rebuilt from the row and its IDs
+// with the encoder's fp32 subtractions.  Two kernels:
+//   repair_list_kernel, one workgroup per 256 rows, lists the block's
+//     flagged (row, level) entries in row, then level order (a block with
+//     more than kRepairList entries is redone there, row by row);
+//   repair_scan_kernel, a fixed grid, scans every listed entry in slices of
+//     kRepairSlice codewords, one item per (entry, slice) spread over the
+//     grid.  Each item's nearest goes into the entry's 64-bit key (distance
+//     bits, then index: distances are not negative, so the unsigned minimum
+//     is the lexicographic one).  The workgroup that finishes a block's last
+//     item then redoes the block's rows: a flagged level takes its key's
+//     index unless an earlier ID of the row changed; once an ID changes,
+//     every later level is scanned whole, since its residual is no longer
+//     the one the sweep and the keys saw.
+// Changed IDs are rewritten, and so is the final residual of a row with a
+// changed ID when the caller asked for it.
+//
+// Both kernels run after the sweep and the residual conversion, when the
+// two residual buffers hold nothing live, and keep their lists there:
+// rbuf[1] the listed count of each block, rbuf[0] an area of
+// kRepairAreaBytes per block (ticket, keys, entries).  Each buffer holds
+// round_up(n, 128) rows of at least 16 floats, at least 8 KiB per block.
+constexpr int kRepairList = 448;
+constexpr int kRepairSlice = 256;
+constexpr int kRepairAreaBytes = 8192;
+constexpr int kRepairKeysOff = 64;
+constexpr int kRepairRowOff = kRepairKeysOff + kRepairList * 8;
+constexpr int kRepairLevOff = kRepairRowOff + kRepairList * 4;
+static_assert(kRepairLevOff + kRepairList * 4 <= kRepairAreaBytes, "repair area too small");
+constexpr int kRepairChunk = 4096;  // block counts the scan kernel reads per pass, 16 a thread
+constexpr unsigned kRepairGrid = 512;
+
+struct RepairArea {
+  unsigned *ticket;          // items of the block finished
+  unsigned long long *keys;  // per entry: (distance bits << 32) | index
+  int *row;                  // per entry: row within the block
+  int *lev;                  // per entry: level
+};
+
+__device__ __forceinline__ RepairArea repair_area(const EncodeArgs &a, int64_t b) {
+  char *p = (char *)a.rbuf[0] + b * kRepairAreaBytes;
+  return {(unsigned *)p, (unsigned long long *)(p + kRepairKeysOff), (int *)(p + kRepairRowOff),
+          (int *)(p + kRepairLevOff)};
+}
+
+// Exact fp32 distance of codeword c to the row res (in LDS): half 0
+// (features ks*16 + e) and half 1 (ks*16 + 8 + e), each summed in feature
+// order with fmaf, then half 0 + half 1, the rescoring's order.  Loads go
+// eight k-steps at a time, all issued before their sums.
+__device__ __forceinline__ float exact_dist(const float *c, const float *res, int nks) {
+  float p0 = 0.f, p1 = 0.f;
+  constexpr int G = 8;
+  int ks = 0;
+  for (; ks + G <= nks; ks += G) {
+    float x0[G][8], x1[G][8];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      read8(c, 0, 0, (ks + u) * 16, true, x0[u]);
+      read8(c, 0, 0, (ks + u) * 16 + 8, true, x1[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = res[(ks + u) * 16 + e] - x0[u][e];
+        const float v = res[(ks + u) * 16 + 8 + e] - x1[u][e];
+        p0 = fmaf(t, t, p0);
+        p1 = fmaf(v, v, p1);
+      }
+    }
+  }
+  for (; ks < nks; ++ks) {
+    float x0[8], x1[8];
+    read8(c, 0, 0, ks * 16, true, x0);
+    read8(c, 0, 0, ks * 16 + 8, true, x1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = res[ks * 16 + e] - x0[e];
+      const float v = res[ks * 16 + 8 + e] - x1[e];
+      p0 = fmaf(t, t, p0);
+      p1 = fmaf(v, v, p1);
+    }
+  }
+  return p0 + p1;
+}
+
+// The nearest to res of codewords k0 + tid, k0 + tid + 256, ... below k1 of
+// one level (the lower index on a tie), over the workgroup: every thread
+// returns it.  Called by all 256 threads.
+__device__ void wg_nearest(const float *cb_l, int dp, const float *res, int k0, int k1,
+                           float *wd, int *wi, float &bd, int &bi) {
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 256;
-  if (tid == 0) nrows = 0;
-  __syncthreads();
-  {
-    const int64_t row = r0 + tid;
-    bool f = false;
-    if (row < a.n)
-      for (int l = 0; l < a.L; ++l) f |= a.aux[row * a.L + l] == kAuxScan;
-    if (f) rows[atomicAdd(&nrows, 1)] = tid;
+  const int nks = dp >> 4;
+  bd = __builtin_inff();
+  bi = kNoIndex;
+  for (int k = k0 + tid; k < k1; k += 256) {
+    const float dk = exact_dist(cb_l + (int64_t)k * dp, res, nks);
+    if (lex_lt(dk, k, bd, bi)) {
+      bd = dk;
+      bi = k;
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float od = __shfl_xor(bd, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (lex_lt(od, oi, bd, bi)) {
+      bd = od;
+      bi = oi;
+    }
+  }
+  if ((tid & 63) == 0) {
+    wd[tid >> 6] = bd;
+    wi[tid >> 6] = bi;
   }
   __syncthreads();
-  const int nr = nrows;
-  const int nks = a.dp >> 4;
-  for (int q = 0; q < nr; ++q) {
-    const int64_t row = r0 + rows[q];
-    for (int i = tid; i < a.dp; i += 256) {
-      float v = 0.f;
-      if (i < a.d)
-        v = a.x_bf16 ? bf16_bits_to_f32(((const uint16_t *)a.x)[row * a.d + i])
-                     : ((const float *)a.x)[row * a.d + i];
-      res[i] = v;
+  bd = wd[0];
+  bi = wi[0];
+  for (int w = 1; w < 4; ++w)
+    if (lex_lt(wd[w], wi[w], bd, bi)) {
+      bd = wd[w];
+      bi = wi[w];
     }
+  __syncthreads();
+}
+
+// res (LDS, dp floats) = the residual of a row entering level l: the row
+// (zero past d) minus the chosen codewords of levels 0 .. l-1, in level
+// order.  Each thread builds its own features; a barrier follows.
+__device__ void row_residual(const EncodeArgs &a, int64_t row, int l, float *res) {
+  const int32_t *id = a.ids + row * a.L;
+  for (int i = threadIdx.x; i < a.dp; i += 256) {
+    float v = 0.f;
+    if (i < a.d)
+      v = a.x_bf16 ? bf16_bits_to_f32(((const uint16_t *)a.x)[row * a.d + i])
+                   : ((const float *)a.x)[row * a.d + i];
+    int j = 0;
+    for (; j + 4 <= l; j += 4) {
+      float c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[u] = a.cb[((int64_t)(j + u) * a.K + id[j + u]) * a.dp + i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v = v - c[u];
+    }
+    for (; j < l; ++j) v = v - a.cb[((int64_t)j * a.K + id[j]) * a.dp + i];
+    res[i] = v;
+  }
+  __syncthreads();
+}
+
+// Redo one row level by level.  keys: the nearest of each flagged level of
+// the row from the parallel scan, in level order, or null to scan every
+// flagged level here.  The residual (res, LDS) is built only once a scan
+// or a changed ID needs it, and then kept level by level.  A result outside
+// [0, K) (only NaN distances give one) leaves the ID as the sweep chose it.
+// flags: 256 ints of LDS for the row's repair codes.
+__device__ void fix_row(const EncodeArgs &a, int64_t row, const unsigned long long *keys,
+                        float *res, int *flags, float *wd, int *wi) {
+  const int tid = threadIdx.x;
+  bool changed = false, have = false;
+  int q = 0;
+  for (int l0 = 0; l0 < a.L; l0 += 256) {
+    const int nl = a.L - l0 < 256 ? a.L - l0 : 256;
     __syncthreads();
-    bool changed = false;
-    for (int l = 0; l < a.L; ++l) {
+    if (tid < nl) flags[tid] = a.aux[row * a.L + l0 + tid] == kAuxScan ? 1 : 0;
+    __syncthreads();
+    for (int t = 0; t < nl; ++t) {
+      const int l = l0 + t;
+      const bool flagged = flags[t] != 0;
       const float *cb_l = a.cb + (int64_t)l * a.K * a.dp;
-      int id = a.ids[row * a.L + l];
-      if (changed || a.aux[row * a.L + l] == kAuxScan) {
-        float bd = __builtin_inff();
-        int bi = kNoIndex;
-        for (int k = tid; k < a.K; k += 256) {
-          const float *c = cb_l + (int64_t)k * a.dp;
-          float p0 = 0.f, p1 = 0.f;
-          for (int ks = 0; ks < nks; ++ks) {
-            float x0[8], x1[8];
-            read8(c, 0, a.dp, ks * 16, true, x0);
-            read8(c, 0, a.dp, ks * 16 + 8, true, x1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float t = res[ks * 16 + e] - x0[e];
-              const float u = res[ks * 16 + 8 + e] - x1[e];
-              p0 = fmaf(t, t, p0);
-              p1 = fmaf(u, u, p1);
-            }
+      int id = -1;
+      if (changed || flagged) {
+        id = a.ids[row * a.L + l];
+        int bi;
+        if (!changed && keys) {
+          bi = (int)(unsigned)__hip_atomic_load(keys + q, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          if (!have) {
+            row_residual(a, row, l, res);
+            have = true;
           }
-          const float dk = p0 + p1;
-          if (lex_lt(dk, k, bd, bi)) {
-            bd = dk;
-            bi = k;
-          }
+          float bd;
+          wg_nearest(cb_l, a.dp, res, 0, a.K, wd, wi, bd, bi);
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float od = __shfl_xor(bd, off, 64);
-          const int oi = __shfl_xor(bi, off, 64);
-          if (lex_lt(od, oi, bd, bi)) {
-            bd = od;
-            bi = oi;
+        q += flagged ? 1 : 0;
+        if (bi >= 0 && bi < a.K && bi != id) {
+          if (!have) {
+            row_residual(a, row, l, res);
+            have = true;
           }
-        }
-        if ((tid & 63) == 0) {
-          wd[tid >> 6] = bd;
-          wi[tid >> 6] = bi;
-        }
-        __syncthreads();
-        bd = wd[0];
-        bi = wi[0];
-        for (int w = 1; w < 4; ++w)
-          if (lex_lt(wd[w], wi[w], bd, bi)) {
-            bd = wd[w];
-            bi = wi[w];
-          }
-        if (bi != id) {
           changed = true;
           if (tid == 0) a.ids[row * a.L + l] = bi;
           id = bi;
         }
       }
-      for (int i = tid; i < a.dp; i += 256) res[i] = res[i] - cb_l[(int64_t)id * a.dp + i];
+      if (have) {
+        if (id < 0) id = a.ids[row * a.L + l];
+        for (int i = tid; i < a.dp; i += 256) res[i] = res[i] - cb_l[(int64_t)id * a.dp + i];
+        __syncthreads();
+      }
+    }
+  }
+  if (changed && a.residual_out)
+    for (int i = tid; i < a.d; i += 256) a.residual_out[row * a.d + i] = res[i];
+  __syncthreads();
+}
+
+// Exclusive prefix of v over the 256 threads, and the total.
+__device__ __forceinline__ int wg_exclusive_sum(int v, int *wsum, int &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = incl - v;
+  total = 0;
+  for (int w = 0; w < 4; ++w) {
+    base += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  __syncthreads();
+  return base;
+}
+
+__global__ __launch_bounds__(256) void repair_list_kernel(EncodeArgs a) {
+  __shared__ float res[kMaxStages * kStageCols];
+  __shared__ int flagged[256];
+  __shared__ int lvflags[256];
+  __shared__ int wsum[4];
+  __shared__ float wd[4];
+  __shared__ int wi[4];
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int64_t row = b * 256 + tid;
+  // flagged levels per row, from the block's codes read as one contiguous
+  // run (16-byte loads: the run starts 1 KiB-aligned)
+  flagged[tid] = 0;
+  __syncthreads();
+  {
+    const int64_t rows = a.n - b * 256 < 256 ? a.n - b * 256 : 256;
+    const int64_t m = rows * a.L;
+    const int32_t *ax = a.aux + b * 256 * a.L;
+    for (int64_t i = tid; i < (m >> 2); i += 256) {
+      const int4 v = reinterpret_cast<const int4 *>(ax)[i];
+      const int e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e[u] == kAuxScan) atomicAdd(&flagged[(int)((i * 4 + u) / a.L)], 1);
+    }
+    for (int64_t i = (m & ~(int64_t)3) + tid; i < m; i += 256)
+      if (ax[i] == kAuxScan) atomicAdd(&flagged[(int)(i / a.L)], 1);
+  }
+  __syncthreads();
+  const int c = flagged[tid];
+  int total;
+  const int base = wg_exclusive_sum(c, wsum, total);
+  if (tid == 0) ((int *)a.rbuf[1])[b] = total <= kRepairList ? total : 0;
+  if (total == 0) return;
+  if (total <= kRepairList) {
+    const RepairArea ar = repair_area(a, b);
+    if (tid == 0) *ar.ticket = 0u;
+    if (c > 0)
+      for (int l = 0, q = base; l < a.L; ++l)
+        if (a.aux[row * a.L + l] == kAuxScan) {
+          ar.keys[q] = ~0ull;
+          ar.row[q] = tid;
+          ar.lev[q] = l;
+          ++q;
+        }
+    return;
+  }
+  // more entries than a block lists: this workgroup redoes its rows
+  for (int r = 0; r < 256; ++r)
+    if (flagged[r] > 0) fix_row(a, b * 256 + r, nullptr, res, lvflags, wd, wi);
+}
+
+__global__ __launch_bounds__(256) void repair_scan_kernel(EncodeArgs a, int64_t nb, int slices) {
+  __shared__ float res[kMaxStages * kStageCols];
+  __shared__ int pre[kRepairChunk + 1];
+  __shared__ int lvflags[256];
+  __shared__ int wsum[4];
+  __shared__ float wd[4];
+  __shared__ int wi[4];
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int *bcnt = (const int *)a.rbuf[1];
+  const int64_t G = gridDim.x;
+  int64_t E = 0;  // entries listed by the blocks before this pass's
+  for (int64_t c0 = 0; c0 < nb; c0 += kRepairChunk) {
+    // pre[i]: entries of blocks c0 .. c0+i-1; pre[kRepairChunk]: the pass's
+    int v[16], t = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t b = c0 + tid * 16 + u;
+      v[u] = b < nb ? bcnt[b] : 0;
+      t += v[u];
+    }
+    int total;
+    int acc = wg_exclusive_sum(t, wsum, total);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      pre[tid * 16 + u] = acc;
+      acc += v[u];
+    }
+    if (tid == 0) pre[kRepairChunk] = total;
+    __syncthreads();
+    // items (entry, slice) of this pass, entry-major, dealt round robin
+    const int64_t lo = E * slices, hi = (E + total) * slices;
+    for (int64_t it = lo + (((int64_t)blockIdx.x - lo % G) + G) % G; it < hi; it += G) {
+      const int e = (int)(it / slices - E);
+      const int s = (int)(it % slices);
+      // the block of entry e: the last bl with pre[bl] <= e
+      int bl = 0;
+#pragma unroll
+      for (int step = kRepairChunk / 2; step > 0; step >>= 1)
+        if (pre[bl + step] <= e) bl += step;
+      const int64_t b = c0 + bl;
+      const int j = e - pre[bl];
+      const int cnt = pre[bl + 1] - pre[bl];
+      const RepairArea ar = repair_area(a, b);
+      const int l = ar.lev[j];
+      row_residual(a, b * 256 + ar.row[j], l, res);
+      float bd;
+      int bi;
+      const int k0 = s * kRepairSlice;
+      const int k1 = a.K - k0 < kRepairSlice ? a.K : k0 + kRepairSlice;
+      wg_nearest(a.cb + (int64_t)l * a.K * a.dp, a.dp, res, k0, k1, wd, wi, bd, bi);
+      if (tid == 0) {
+        atomicMin(ar.keys + j, ((unsigned long long)__float_as_uint(bd) << 32) | (unsigned)bi);
+        __threadfence();
+        last = atomicAdd(ar.ticket, 1u) + 1u == (unsigned)cnt * (unsigned)slices;
+      }
+      __syncthreads();
+      if (last) {
+        // every item of block b is in: redo its rows
+        __threadfence();
+        for (int q = 0; q < cnt;) {
+          const int r = ar.row[q];
+          fix_row(a, b * 256 + r, ar.keys + q, res, lvflags, wd, wi);
+          while (q < cnt && ar.row[q] == r) ++q;
+        }
+      }
       __syncthreads();
     }
-    if (changed && a.residual_out)
-      for (int i = tid; i < a.d; i += 256) a.residual_out[row * a.d + i] = res[i];
-    __syncthreads();
+    E += total;
   }
 }
 
@@ -319,7 +574,10 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
       unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(final_buf, a.n, a.d, a.dp,
                                                          a.residual_out);
   }
-  repair_kernel<<<dim3((unsigned)ceil_div(a.n, 256)), dim3(256), 0, s>>>(a);
+  const int64_t nb = ceil_div(a.n, 256);
+  repair_list_kernel<<<dim3((unsigned)nb), dim3(256), 0, s>>>(a);
+  repair_scan_kernel<<<dim3(kRepairGrid), dim3(256), 0, s>>>(a, nb,
+                                                            (int)ceil_div(a.K, kRepairSlice));
   return hipGetLastError();
 }
 

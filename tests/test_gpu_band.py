@@ -154,3 +154,45 @@ def test_crowded_bands(rvq, dev, kind, n):
     assert (ids_h == ids_h[0]).all()
     parity.check_ids(ids_h[:1], x[:1], "f32", cb, ref=ref)
     parity.check_residual(res_h[:1], x[:1], "f32", ids_h[:1], cb)
+
+
+def _crowd_every_level(d, K, L, members, spacing, seed, duplicates):
+    """Like _crowd, at every level: level l holds `members` codewords near
+    the residual entering it (the row minus the nearest codewords of the
+    levels before, subtracted in fp32 as the encoder does)."""
+    g = np.random.default_rng(seed)
+    x = (1.0 + 0.25 * g.standard_normal(d)).astype(np.float32)
+    cb = (3.0 * g.standard_normal((L, K, d))).astype(np.float32)
+    r = x.copy()
+    for l in range(L):
+        nr2 = float((r.astype(np.float64) ** 2).sum())
+        for j, k in enumerate(members):
+            u = g.standard_normal(d)
+            u /= np.linalg.norm(u)
+            cb[l, k] = (r + np.sqrt(spacing * (j + 1) * nr2) * u).astype(np.float32)
+        if duplicates:
+            for k in members[1:]:
+                cb[l, k] = cb[l, members[0]]
+        r = r - cb[l, members[0]]
+    return x[None], cb
+
+
+@pytest.mark.parametrize("n", [300, 20000], ids=["split", "fused"])
+@pytest.mark.parametrize("kind", ["many_blocks", "duplicates"])
+def test_crowded_every_level(rvq, dev, kind, n):
+    # Every row is left to the exact scan at all three levels: 768 scans in
+    # a full block of 256 rows, more than a block lists for the parallel
+    # scan, so full blocks are redone row by row, and the last, partial
+    # block (44 or 32 rows) goes through the parallel scan.
+    d, K, L = 64, 1000, 3
+    members = [40, 140, 240, 340, 440, 540, 640, 740, 840]
+    x, cb = _crowd_every_level(d, K, L, members, 3e-4, seed=7, duplicates=kind == "duplicates")
+    ref = oracle.encode(x, cb)
+    assert (ref["ids"][0] == members[0]).all()
+    x = np.repeat(x, n, axis=0)
+    ids_h, res_h = _run(rvq, dev, x, cb)
+    print(f"[crowd every level {kind} n={n}] gpu {ids_h[0]} {ids_h[-1]} oracle {ref['ids'][0]}")
+    assert (ids_h == members[0]).all()
+    assert (res_h == res_h[0]).all()
+    parity.check_ids(ids_h[:1], x[:1], "f32", cb, ref=ref)
+    parity.check_residual(res_h[:1], x[:1], "f32", ids_h[:1], cb)
