@@ -196,3 +196,26 @@ def test_crowded_every_level(rvq, dev, kind, n):
     assert (res_h == res_h[0]).all()
     parity.check_ids(ids_h[:1], x[:1], "f32", cb, ref=ref)
     parity.check_residual(res_h[:1], x[:1], "f32", ids_h[:1], cb)
+
+
+def test_crowded_rows_past_one_count_pass(rvq, dev):
+    # 1,100,000 copies of a crowded row: every row goes to the exact scan at
+    # level 0, so all 4,297 blocks of 256 rows list entries, more blocks
+    # than the scan kernel reads in one pass of their counts (4,096).
+    d, K, L = 64, 1000, 3
+    members = [40, 140, 240, 340, 440, 540, 640, 740, 840]
+    x, cb = _crowd(d, K, L, members, 3e-4, seed=len("many_blocks"))
+    ref = oracle.encode(x, cb)
+    assert ref["ids"][0, 0] == members[0]
+    n = 1_100_000
+    xd = torch.from_numpy(x).to(dev).expand(n, d).contiguous()
+    cbd = torch.from_numpy(cb).to(dev)
+    ids, res = rvq.rvq_encode(xd, cbd, rvq.rvq_prepare_codebooks(cbd), residual=True)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    print(f"[crowd past one pass n={n}] gpu {ids_h[0]} {ids_h[-1]} oracle {ref['ids'][0]}")
+    assert (ids_h == ids_h[0]).all()
+    assert ids_h[0, 0] == members[0]
+    assert bool((res == res[0]).all())
+    parity.check_ids(ids_h[:1], x, "f32", cb, ref=ref)
+    parity.check_residual(res[:1].cpu().numpy(), x, "f32", ids_h[:1], cb)
