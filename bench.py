@@ -314,6 +314,45 @@ def secondary(torch, rvq, workloads, dev) -> dict:
     return out
 
 
+def vendor_gemm(torch, dev, N: int, D: int, K: int) -> dict:
+    """Context for the distance stage: the vendor bf16 GEMM (torch.mm, which
+    calls hipBLASLt) of one level's contraction [N, D] x [D, K] with a bf16
+    output and no argmin, on random N(0, 1) operands and on zero operands.
+    The gap between the two is the data-dependent power limit of the matrix
+    cores; the encoder's launch does this contraction for all levels plus
+    the argmin, the exact rescoring and the residual update."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    x = torch.randn(N, D, generator=g).to(torch.bfloat16).to(dev)
+    c = torch.randn(K, D, generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * N * D * K
+    rec = {"op": f"torch.mm bf16 [{N},{D}] x [{D},{K}] -> bf16 (one level, no argmin)"}
+    for name in ("random", "zero"):
+        if name == "zero":
+            x.zero_()
+            c.zero_()
+        ms = _time_ms(torch, lambda: torch.mm(x, c.t(), out=out), 40)
+        rec[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del x, c, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+def mfma_achievable(torch, rvq, dev) -> dict:
+    """Context for the distance stage: the matrix cores' achievable bf16 rate
+    on this chip (rvq_mfma_rate: a register-only v_mfma_f32_32x32x16_bf16
+    loop, one wave per SIMD, about 30 ms per run) on random and on zero
+    operands, with the shader clock each run held."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rec = {"call": f"rvq_mfma_rate({cus} workgroups, one wave per SIMD, register operands)"}
+    for name, zero in (("random", False), ("zero", True)):
+        tf, ghz = rvq.rvq_mfma_rate(cus, 200_000, zero, dev)
+        rec[name] = {"tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "clock_ghz": round(ghz, 3)}
+    return rec
+
+
 def copy_calibration(torch, dev, mib: int) -> None:
     """One plain elementwise copy that reads and writes mib MiB: the dispatch
     that calibrates the HBM byte counters."""
@@ -457,6 +496,10 @@ def main() -> int:
     if not args.no_secondary:
         del x, cb, prepared, ws, ws2, ids, out
         torch.cuda.empty_cache()
+        rec["mfma_achievable"] = mfma_achievable(torch, rvq, dev)
+        rec["roofline"]["frac_of_achievable"] = round(
+            achieved / rec["mfma_achievable"]["random"]["tflops"], 4)
+        rec["vendor_gemm"] = vendor_gemm(torch, dev, N, D, K)
         rec["secondary"] = secondary(torch, rvq, workloads, dev)
     if args.copy_mib > 0:
         copy_calibration(torch, dev, args.copy_mib)

@@ -422,6 +422,35 @@ rvq_status rvq_pack_ranks(const int64_t *text_tokens, const int64_t *image_token
                           int64_t samples, int32_t ranks, int64_t capacity, int32_t exact_max,
                           int32_t *rank_of, int64_t *summary);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid: the matrix cores' achievable bf16 rate.
+ *
+ * Not a step of the path.  The published dense bf16 peak assumes the
+ * nominal clock; under a full matrix load the chip holds a clock that
+ * depends on how much the operands switch.  rvq_mfma_rate runs a
+ * register-only loop of v_mfma_f32_32x32x16_bf16 (the instruction of the
+ * encoder's distance stage) on `blocks` workgroups of four waves (use one
+ * per compute unit: one wave per SIMD), four independent accumulator chains
+ * per wave, `iters` iterations of eight instructions, no memory traffic in
+ * the loop.  zero_operands != 0 uses all-zero operands, otherwise random
+ * bf16 values (random sign, magnitude in [0.25, 4), random mantissa).
+ * A short untimed run precedes the timed one.
+ *
+ * workspace: device memory of at least rvq_mfma_rate_workspace_size(blocks)
+ * bytes, 8-byte aligned (per-workgroup clock readings and a result sink).
+ * tflops (host) receives the timed launch's rate from HIP events; clock_ghz
+ * (host) the shader clock over the loop (s_memtime ticks over
+ * s_memrealtime's 100 MHz, averaged over workgroups).  Unlike the other
+ * device entry points this call waits for its work and copies the clock
+ * readings to the host.  Returns RVQ_ERR_INVALID_ARGUMENT for blocks
+ * outside 1 .. 65536, iters outside 10 .. 10^7 or a null or misaligned
+ * pointer, RVQ_ERR_WORKSPACE_TOO_SMALL, or RVQ_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+size_t rvq_mfma_rate_workspace_size(int32_t blocks);
+rvq_status rvq_mfma_rate(int32_t blocks, int32_t iters, int32_t zero_operands, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream, double *tflops,
+                         double *clock_ghz);
+
 #ifdef __cplusplus
 }
 #endif

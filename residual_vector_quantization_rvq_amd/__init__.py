@@ -28,7 +28,7 @@ __all__ = [
     "rvq_decode_level_stats",
     "rvq_embed_tokens", "rvq_idcache_resume", "rvq_idcache_append", "rvq_idcache_read",
     "rvq_stream_workspace_size", "rvq_stream_encode", "rvq_stream_encode_to_cache",
-    "rvq_pack_ranks", "rvq_status_string",
+    "rvq_pack_ranks", "rvq_mfma_rate", "rvq_status_string",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -89,7 +89,11 @@ _lib.rvq_stream_encode.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p, _i32, _
                                    _i64, _i64, _p, _p, _p, _sz, _p, _pi64]
 _lib.rvq_stream_encode_to_cache.argtypes = [ctypes.c_char_p, _p, ctypes.c_int, _i64, _i32, _p,
                                             _p, _i32, _i32, _p, _i64, _i64, _p, _sz, _p, _pi64]
-for _f in ("rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size",
+_lib.rvq_mfma_rate_workspace_size.argtypes = [_i32]
+_lib.rvq_mfma_rate_workspace_size.restype = ctypes.c_size_t
+_lib.rvq_mfma_rate.argtypes = [_i32, _i32, _i32, _p, _sz, _p, ctypes.POINTER(ctypes.c_double),
+                               ctypes.POINTER(ctypes.c_double)]
+for _f in ("rvq_mfma_rate", "rvq_prepared_size", "rvq_prepare_codebooks", "rvq_encode_workspace_size",
            "rvq_encode", "rvq_encode_noalloc", "rvq_encode_profiled", "rvq_decode",
            "rvq_level_stats_workspace_size", "rvq_level_stats", "rvq_decode_level_stats", "rvq_embed_tokens", "rvq_idcache_resume",
            "rvq_idcache_append", "rvq_idcache_read", "rvq_stream_workspace_size",
@@ -521,3 +525,17 @@ def rvq_decode_level_stats(ids: torch.Tensor, x: torch.Tensor, codebooks: torch.
                                        _dtype_code(x.dtype), _ptr(msr), _ptr(bad_ids),
                                        _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, hist, msr
+
+
+def rvq_mfma_rate(blocks: int, iters: int, zero_operands: bool = False,
+                  device: Optional[torch.device] = None):
+    """The matrix cores' achievable bf16 rate: a register-only loop of
+    v_mfma_f32_32x32x16_bf16 on `blocks` four-wave workgroups (one per
+    compute unit for one wave per SIMD), on random or all-zero operands.
+    Waits for the run.  Returns (TFLOP/s, shader clock in GHz)."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    ws = torch.empty(int(_lib.rvq_mfma_rate_workspace_size(blocks)), dtype=torch.uint8, device=dev)
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    _check(_lib.rvq_mfma_rate(blocks, iters, 1 if zero_operands else 0, _ptr(ws), ws.numel(),
+                              _stream(dev), ctypes.byref(tf), ctypes.byref(ghz)))
+    return tf.value, ghz.value

@@ -253,3 +253,22 @@ def test_decode_level_stats_rejects_bad_arguments(rvq):
     assert call(a9=p(1), a10=1) == 1       # bf16 x not 2-byte aligned
     assert call(a14=1) == 3                # workspace too small
     assert call(a3=65) == 2                # L above the gather limit
+
+
+def test_mfma_rate_rejects_bad_arguments(rvq):
+    lib = rvq.raw_library()
+    p = ctypes.c_void_p
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    need = int(lib.rvq_mfma_rate_workspace_size(4))
+    assert need == 4 * (16 + 256 * 4)
+    assert lib.rvq_mfma_rate_workspace_size(0) == 0
+    # fake, never-dereferenced addresses: validation fails before any HIP call
+    call = lambda blocks, iters, ws, nbytes: lib.rvq_mfma_rate(
+        blocks, iters, 0, p(ws) if ws else None, nbytes, None, ctypes.byref(tf), ctypes.byref(ghz))
+    assert call(0, 100, 256, need) == 1
+    assert call(70000, 100, 256, need) == 1
+    assert call(4, 5, 256, need) == 1
+    assert call(4, 100, 0, need) == 1
+    assert call(4, 100, 260, need) == 1      # not 8-byte aligned
+    assert call(4, 100, 256, need - 1) == 3
+    assert lib.rvq_mfma_rate(4, 100, 0, p(256), need, None, None, ctypes.byref(ghz)) == 1
