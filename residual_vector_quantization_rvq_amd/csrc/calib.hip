@@ -7,6 +7,8 @@
 // instruction) on register operands, one wave per SIMD, four independent
 // accumulator chains per wave and no memory traffic inside the timed loop,
 // on random or on all-zero operands.
+#include <vector>
+
 #include "rvq.h"
 #include "common.h"
 
@@ -125,24 +127,20 @@ extern "C" rvq_status rvq_mfma_rate(int32_t blocks, int32_t iters, int32_t zero_
   if (e == hipSuccess) e = hipEventSynchronize(e1);
   float ms = 0.f;
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
-  uint64_t *host = nullptr;
+  std::vector<uint64_t> host;
   if (e == hipSuccess) {
-    host = new uint64_t[2 * (size_t)blocks];
-    e = hipMemcpy(host, clocks, 2 * (size_t)blocks * sizeof(uint64_t), hipMemcpyDeviceToHost);
+    host.resize(2 * (size_t)blocks);
+    e = hipMemcpy(host.data(), clocks, host.size() * sizeof(uint64_t), hipMemcpyDeviceToHost);
   }
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
-  if (e != hipSuccess) {
-    delete[] host;
-    return rvq::fail(RVQ_ERR_HIP, "mfma rate: %s", hipGetErrorString(e));
-  }
+  if (e != hipSuccess) return rvq::fail(RVQ_ERR_HIP, "mfma rate: %s", hipGetErrorString(e));
   // s_memtime counts shader clocks, s_memrealtime a constant 100 MHz
   double ticks = 0.0, real = 0.0;
   for (int i = 0; i < blocks; ++i) {
     ticks += (double)host[2 * i];
     real += (double)host[2 * i + 1];
   }
-  delete[] host;
   const double waves = (double)blocks * (kThreads / 64);
   const double flops = waves * (double)iters * kMfmaPerIter * kFlopsPerMfma;
   *tflops = ms > 0.f ? flops / ((double)ms * 1e-3) / 1e12 : 0.0;
