@@ -1627,7 +1627,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // both; four accumulating lanes read these back from this wave's area of
 // LDS, and the winner's r - c is written from the registers.
 template <int S>
-__global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int level, int splits) {
+__global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int level, int splits,
+                                                          int rec_f4) {
   constexpr int kRow4 = S * kStageCols / 4;  // float4 capacity of a row (dp <= 64 S)
   constexpr int NV = (kRow4 + 63) / 64;      // float4 of a row per lane
   constexpr int kMaxCand = 64;
@@ -1659,18 +1660,21 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   const int hh = lane & 1;
   float R1 = __builtin_inff();
   int I1 = kNoIndex, ovf = 0;
-  // (a record is read whole, count and entries at once: its unused entries
-  // are allocated, only never looked at; the lane's first two records stay
-  // in registers for the second pass)
+  // (a record is read at once, count and entries: the first rec_f4 float4,
+  // which hold every entry a split of this many tiles can list (one per
+  // 64-codeword block); the lane's first two records stay in registers for
+  // the second pass, and a lane past the last split reads nothing)
   auto rec_at = [&](int sp2) { return a.part + ((row * splits + sp2) * 2 + hh) * kRecF4; };
+  auto read_rec = [&](const float4 *rec, float4(&e)[kRecF4], bool have) {
+#pragma unroll
+    for (int j = 0; j < kRecF4; ++j)
+      e[j] = (have && j < rec_f4) ? rec[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
   float4 rc[2][kRecF4];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int sp2 = (lane >> 1) + 32 * q;
-    const float4 *rec = rec_at(sp2 < splits ? sp2 : 0);
-#pragma unroll
-    for (int j = 0; j < kRecF4; ++j) rc[q][j] = rec[j];
-    if (sp2 >= splits) rc[q][0].x = __int_as_float(0);
+    read_rec(rec_at(sp2 < splits ? sp2 : 0), rc[q], sp2 < splits);
   }
   auto first_pass = [&](const float4(&e)[kRecF4]) {
     const int c = __float_as_int(e[0].x);
@@ -1687,10 +1691,8 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   first_pass(rc[0]);
   first_pass(rc[1]);
   for (int sp2 = (lane >> 1) + 64; sp2 < splits; sp2 += 32) {
-    const float4 *rec = rec_at(sp2);
     float4 e[kRecF4];
-#pragma unroll
-    for (int j = 0; j < kRecF4; ++j) e[j] = rec[j];
+    read_rec(rec_at(sp2), e, true);
     first_pass(e);
   }
 #pragma unroll
@@ -1742,10 +1744,8 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   second_pass(rc[0]);
   second_pass(rc[1]);
   for (int sp2 = (lane >> 1) + 64; sp2 < splits; sp2 += 32) {
-    const float4 *rec = rec_at(sp2);
     float4 er[kRecF4];
-#pragma unroll
-    for (int j = 0; j < kRecF4; ++j) er[j] = rec[j];
+    read_rec(rec_at(sp2), er, true);
     second_pass(er);
   }
   // per half: failing blocks (counts add; any one of them), overflow
@@ -1939,7 +1939,10 @@ hipError_t launch_stage_count(const EncodePlan &p, const EncodeArgs &a, hipEvent
         a, p.tiles, l, p.splits, p.tiles_per_split);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[2 * l + 1], s)) != hipSuccess) return e;
-    split_update_kernel<S><<<dim3((unsigned)ceil_div(a.n, 4)), dim3(NT), 0, s>>>(a, l, p.splits);
+    // a split's list has at most one entry per 64-codeword block it swept
+    const int rec_f4 = 1 + (2 * p.tiles_per_split < kList ? 2 * p.tiles_per_split : kList);
+    split_update_kernel<S><<<dim3((unsigned)ceil_div(a.n, 4)), dim3(NT), 0, s>>>(a, l, p.splits,
+                                                                                rec_f4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
