@@ -1,5 +1,7 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
 the same seeded inputs."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -100,20 +102,32 @@ def test_single_image(rvq, dev):
 
 def test_native_batch(rvq, dev):
     # The benchmark workload in the configuration the benchmark times: 2,048
-    # sampled rows (every image's first, middle and last row among them)
-    # against the fp64 oracle, the decode, counts and msr of the step's
-    # one-pass kernel against the oracle on every row, and batch invariance.
+    # sampled rows (every image's first, middle and last row among them;
+    # RVQ_NATIVE_ROWS sets another count, "all" every row) against the fp64
+    # oracle, the decode, counts and msr of the step's one-pass kernel
+    # against the oracle on every row, and batch invariance.
     w = workloads.native_batch()
     ids, res, x, cb, prepared = _encode(rvq, w, dev)
     ids_h = ids.cpu().numpy()
     off = w.offsets
+    want = os.environ.get("RVQ_NATIVE_ROWS", "2048")
+    nsel = w.N if want == "all" else min(w.N, int(want))
     ends = np.concatenate([[off[i], (off[i] + off[i + 1]) // 2, off[i + 1] - 1] for i in range(16)])
-    rest = np.random.default_rng(7).choice(w.N, 2048 - len(np.unique(ends)), replace=False)
-    sel = np.unique(np.concatenate([ends, rest]))
-    while len(sel) < 2048:
-        sel = np.unique(np.concatenate([sel, np.random.default_rng(len(sel)).choice(w.N, 2048 - len(sel))]))
+    if nsel == w.N:
+        sel = np.arange(w.N)
+    else:
+        rest = np.random.default_rng(7).choice(w.N, max(0, nsel - len(np.unique(ends))),
+                                               replace=False)
+        sel = np.unique(np.concatenate([ends, rest]))
+        while len(sel) < nsel:
+            sel = np.unique(np.concatenate(
+                [sel, np.random.default_rng(len(sel)).choice(w.N, nsel - len(sel))]))
+    # (in chunks of 4,096 rows, each reported as it is checked)
+    for c0 in range(0, len(sel), 4096):
+        cs = sel[c0:c0 + 4096]
+        print(f"[native_batch] rows {c0}..{c0 + len(cs) - 1} of {len(sel)}",
+              parity.check_ids(ids_h[cs], w.rows(cs).x, "bf16", w.codebooks), flush=True)
     sub = w.rows(sel)
-    print("[native_batch]", len(sel), "rows", parity.check_ids(ids_h[sel], sub.x, "bf16", w.codebooks))
     res_sel = res[torch.from_numpy(sel).to(dev)].cpu().numpy()
     parity.check_residual(res_sel, sub.x, "bf16", ids_h[sel], w.codebooks)
     # the step's decode + statistics pass, against the oracle
