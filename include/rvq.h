@@ -19,10 +19,8 @@
  *
  * Readings taken where the pages are silent: the distance is the squared
  * Euclidean distance; there is one [K][d] codebook per level; search is
- * greedy level by level.  On an exact tie (e.g. duplicated codewords) the
- * encoder returns one of the tied codewords: the lower index when two tie,
- * and a fixed (input-determined, batch-independent) one of them when more
- * than two tie.
+ * greedy level by level; among codewords at the same distance the lower
+ * index wins.
  *
  * Conventions for every entry point:
  *   - Pointers named as device pointers are device memory owned by the
@@ -102,28 +100,34 @@ rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t L, int32_t K, i
 /* ------------------------------------------------------------------------
  * Encode: greedy multi-level nearest-codeword search with residual update.
  *
- * Per level l and row r: the squared distance ||r - c||^2 =
- * ||r||^2 - 2 r.c + ||c||^2 is ranked over all K codewords by the score
+ * Per level l and row r the nearest codeword under ||r - c||^2 is chosen,
+ * its index recorded, and it is subtracted from the fp32 residual, which
+ * feeds the next level.
+ *
+ * Rows of at most 1280 features: the codewords are ranked by the score
  * ||c||^2 - 2 r.c (||r||^2 is the same for every codeword), with the dot
  * products taken on the matrix cores from bf16 copies of r and c with fp32
- * accumulation; the two best-scoring codewords are then rescored exactly in
- * fp32 as sum_i (r_i - c_i)^2 and the smaller wins (lower index on a tie).
- * Which two codewords are rescored is decided by that bf16 screening: each
- * dot product carries the rounding of bf16 operands (each score is then
- * kept to 2^-19 relative in the ranking).  When three or more codewords lie
- * within the screening error of one another, the nearest may not be among
- * the two rescored.  This is not confined to small widths: random sweeps
- * over about 520 shapes (widths 1 to 1280) found five such decisions, at
- * d = 50, 149, 206, 450 and 1057, about 1 in 100,000; each time the missed
- * codeword was nearer than the one returned by 1.1e-4 to 2.3e-4 ||r||^2.
- * At d = 1152 none was found in 32,000 sampled decisions.  The IDs are those of this
- * procedure.  Only two things in it are unspecified: the order in which
- * the dot products are accumulated in fp32, and the tag bits in the low
- * mantissa of the ranking keys.  So a decision, and the fp32 residual it
- * leaves, is fixed whenever the two best scores lie farther from the third
- * than those two effects can move a score.
- * The chosen codeword is subtracted from the fp32 residual, which feeds the
- * next level.
+ * accumulation.  Per row and level the encoder bounds how far this
+ * screening can move a score (from the row's and the level's rounding
+ * terms: the residual's and the codewords' bf16 rounding, the fp32
+ * accumulation, the hi/lo split of ||c||^2 and the tag bits of the ranking
+ * keys), and every codeword whose key lies within the resulting band of the
+ * smallest key is rescored exactly in fp32 as sum_i (r_i - c_i)^2; the
+ * smallest distance wins.  A level whose candidates cannot all be kept
+ * (a crowded band) is rescanned exactly over all K codewords after the
+ * distance launch.  So the nearest codeword is returned wherever it beats
+ * every other by more than 1e-4 ||r||^2.  (The bound treats the rounding
+ * errors of different features as independent, a reading of the typical
+ * case; its Cauchy-Schwarz worst case is used where it is smaller, at
+ * widths below about 25.)
+ *
+ * Rows of 1281 to 8192 features: every distance sum_i (r_i - c_i)^2 is
+ * computed exactly in fp32 on the vector ALUs, with no screening (slower).
+ *
+ * On both paths, among codewords at the same fp32 distance the lower index
+ * wins (duplicated codewords return the lowest index), and a row's IDs and
+ * fp32 residual depend only on the row and the codebooks, not on the other
+ * rows of the call or on its position.
  * ---------------------------------------------------------------------- */
 
 /* Workspace bytes needed by rvq_encode for n rows. */
@@ -141,10 +145,11 @@ rvq_status rvq_encode_workspace_size(int64_t n, int32_t d, int32_t L, int32_t K,
  * residual_out : device, [n][d] fp32 output x - sum_l codebooks[l][ids[l]],
  *                or NULL when not wanted.  4-byte aligned (16-byte alignment
  *                can save a final copy).
- * d            : 1..1280 (RVQ_ERR_UNSUPPORTED above: a row's features stay
- *                resident in registers during the sweep).  One level of
+ * d            : 1..8192 (RVQ_ERR_UNSUPPORTED above).  Up to 1280 a row's
+ *                features stay resident in registers during the matrix-core
+ *                sweep; wider rows take the exact fp32 path.  One level of
  *                codewords, K x (d rounded up to 16) fp32, must be below
- *                4 GiB (RVQ_ERR_UNSUPPORTED otherwise; the same check applies
+ *                4 GiB (RVQ_ERR_UNSUPPORTED otherwise; the same checks apply
  *                to rvq_prepared_size, rvq_prepare_codebooks and
  *                rvq_encode_workspace_size).
  * workspace    : device, >= rvq_encode_workspace_size bytes, 256-byte

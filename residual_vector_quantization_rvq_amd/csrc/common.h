@@ -9,7 +9,7 @@ namespace rvq {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Sentinel index of an empty top-2 slot; never a valid codeword index.
+// Sentinel index of an empty (key, index) slot; never a valid codeword index.
 constexpr int kNoIndex = 0x7fffffff;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
@@ -22,8 +22,8 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 }
 
 // Lexicographic order on (score, index): smaller score first, lower index
-// on equal scores.  A total order on finite scores, so every merge of top-2
-// lists below gives the same result whatever the merge order.
+// on equal scores.  A total order on finite scores, so every merge of
+// (key, index) minima gives the same result whatever the merge order.
 __device__ __forceinline__ bool lex_lt(float sa, int ia, float sb, int ib) {
   return sa < sb || (sa == sb && ia < ib);
 }
@@ -81,6 +81,8 @@ constexpr int kStageBytes = 16 * kBlockBytes;
 constexpr int kNormBytes = 4 * kBlockBytes;
 constexpr int kRowsPerWG = 128;      // 4 waves x 32 rows
 constexpr int kMaxStages = 20;       // features <= 1280
+// Wider rows (up to this many features) take the exact fp32 encoder (wide.hip).
+constexpr int kWideMaxD = 8192;
 constexpr float kPadNorm = 3.0e38f;
 
 // Stage counts (features / 64) with an instantiated encoder; a width is
@@ -218,6 +220,9 @@ struct EncodeArgs {
   const uint16_t *x16;  // fused mode with bf16 rows of stride dp: level 0 reads them directly
   float *res_final;     // where the last level writes its residual (or null)
 };
+// The exact fp32 encoder of rows wider than the sweep holds: one launch per
+// level (events: 2 L, around each), rows of stride dp in rbuf.
+hipError_t launch_wide(const EncodeArgs &a, hipEvent_t *events, hipStream_t s);
 hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a, hipEvent_t *events,
                          hipStream_t s);
 

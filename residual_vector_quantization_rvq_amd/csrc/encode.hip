@@ -495,8 +495,9 @@ EncodePlan plan_encode(int64_t n, int d, int K, int num_cus) {
   p.row_blocks = (int)ceil_div(n, kRowsPerWG);
   int cus = num_cus > 0 ? num_cus : 256;
   cus = cus < kPlanMaxCus ? cus : kPlanMaxCus;
-  p.fused = (int64_t)p.row_blocks * 10 >= (int64_t)cus * 6;
-  if (p.fused) {
+  // (stages == 0: rows wider than the sweep holds, for the exact fp32 encoder)
+  p.fused = p.stages > 0 && (int64_t)p.row_blocks * 10 >= (int64_t)cus * 6;
+  if (p.fused || p.stages == 0) {
     p.splits = 1;
     p.tiles_per_split = p.tiles;
   } else {
@@ -555,6 +556,18 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
   const bool out_al = ((uintptr_t)a.residual_out & 15) == 0;
   const bool convert = a.residual_out && (p.fused || a.dp != a.d || !out_al);
   a.res_final = convert ? final_buf : a.residual_out;
+  if (p.stages == 0) {
+    // rows wider than the sweep holds: exact fp32 distances, nothing to
+    // rescan afterwards
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_wide(a, events, s);
+    if (e != hipSuccess) return e;
+    if (convert)
+      unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(final_buf, a.n, a.d, a.dp,
+                                                         a.residual_out);
+    return hipGetLastError();
+  }
   if (!p.fused) {
     // every block a sweep workgroup reads (4 per 128 rows)
     const int64_t pieces = ceil_div(a.n, kRowsPerWG) * 4 * (a.dp >> 4) * 64;

@@ -25,17 +25,23 @@
 //    accumulator holds the score.  The epilogue packs each score with a
 //    5-bit lane-local codeword tag into a key (score bits 0..4 replaced) and
 //    keeps the two smallest keys per 64-codeword block with v_min / v_med3
-//    (3 VALU ops per score); block winners are merged exactly under the
+//    (3 VALU ops per score); a block whose smallest key lies within the
+//    row's screening band (common.h, screen_band) of the running minimum
+//    goes on the lane's list.  Minima are merged exactly under the
 //    (key, index) order.
 //  * Fused mode (enough rows to fill the GPU): all levels run in one launch;
-//    after a level's sweep, lanes L and L+32 of a wave rescore their row's
-//    two candidates exactly in fp32 (sum of squared differences, each lane
-//    one half of the features in a fixed order), pick the smaller (lower
-//    index on a tie), subtract it from the fp32 residual and rebuild the
-//    B-fragments for the next level in registers.
+//    after a level's sweep the row's smallest key fixes the band, and lanes
+//    L and L+32 of a wave rescore every candidate inside it exactly in fp32
+//    (sum of squared differences, each lane one half of the features in a
+//    fixed order); a block whose second key is inside the band too is
+//    rescored whole, and a level whose candidates could not all be kept is
+//    flagged for the exact scan after the launch.  The smallest distance
+//    wins (lower index on a tie); it is subtracted from the fp32 residual
+//    and the B-fragments for the next level are rebuilt in registers.
 //  * Split mode (few rows): a level's codeword tiles are split over
-//    several workgroups per row block, each writing its top-2 list; a second
-//    kernel merges the lists and runs the same rescoring and update.
+//    several workgroups per row block, each writing its band list as a
+//    record; a second kernel merges the records and runs the same
+//    rescoring and update.
 // Every score depends only on (row, codeword): one MFMA shape, one k-step
 // order, one key rule and a total order for merging, so the IDs and
 // residuals are bitwise independent of batch size, row position and mode.

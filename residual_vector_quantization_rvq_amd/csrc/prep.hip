@@ -150,6 +150,9 @@ hipError_t launch_prepare(const float *cb, int L, int K, int d, float *norms, ui
                                                                                       dp, cbpad);
   }
   const int Kp = (int)padded_k(K), S = (int)(padded_d(d) / kStageCols);
+  // rows wider than the sweep holds are encoded in exact fp32: the padded
+  // copy is all they use
+  if (S == 0) return hipGetLastError();
   const int64_t tiles = (int64_t)L * (Kp / kTileCw);
   prepare_tile_kernel<<<dim3((unsigned)tiles), dim3(256), 0, s>>>(
       cb, L, K, d, Kp, S, norms, reinterpret_cast<uint4 *>(stream), tstat);

@@ -155,9 +155,9 @@ const char *rvq_last_error(void) { return g_err; }
 
 namespace {
 rvq_status check_encode_width(int32_t d, int32_t K) {
-  if (stages_for(d) == 0)
-    return fail(RVQ_ERR_UNSUPPORTED, "encode supports d <= %d (got %d)", kMaxStages * kStageCols,
-                d);
+  // d <= 1280: the matrix-core sweep; up to kWideMaxD: the exact fp32 encoder
+  if (stages_for(d) == 0 && d > kWideMaxD)
+    return fail(RVQ_ERR_UNSUPPORTED, "encode supports d <= %d (got %d)", kWideMaxD, d);
   // the fused update addresses a level's codewords with 32-bit lane offsets
   if ((int64_t)K * row_stride(d) * (int64_t)sizeof(float) > (int64_t)UINT32_MAX)
     return fail(RVQ_ERR_UNSUPPORTED, "encode supports K * d below 2^30 per level (got K=%d, d=%d)",

@@ -76,8 +76,15 @@ def test_prepared_size_layout(rvq):
                                               + al(L * 3 * 8) + al(L * 16) + al(L * K * 80 * 4))
     # d = 640 needs 10 stages, padded to the next instantiated count (12)
     assert rvq.rvq_prepared_size(1, 128, 640) == al(128 * 4) + al(4096 + 12 * 16384) + al(8) + al(16)
+    # rows wider than 1280 features take the exact fp32 encoder: no stages
+    # (a norm block per tile is still reserved), the padded fp32 copy when
+    # d is not a multiple of 16; up to 8192 features
+    assert rvq.rvq_prepared_size(2, 300, 1281) == (al(2 * 384 * 4) + al(2 * 3 * 4096)
+                                                   + al(2 * 3 * 8) + al(2 * 16)
+                                                   + al(2 * 300 * 1296 * 4))
+    assert rvq.rvq_prepared_size(1, 128, 8192) == al(128 * 4) + al(4096) + al(8) + al(16)
     with pytest.raises(rvq.RVQError) as e:
-        rvq.rvq_prepared_size(1, 128, 1281)
+        rvq.rvq_prepared_size(1, 128, 8193)
     assert e.value.status == 2
 
 
