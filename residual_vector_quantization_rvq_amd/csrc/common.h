@@ -220,9 +220,11 @@ struct EncodeArgs {
   const uint16_t *x16;  // fused mode with bf16 rows of stride dp: level 0 reads them directly
   float *res_final;     // where the last level writes its residual (or null)
 };
-// The exact fp32 encoder of rows wider than the sweep holds: one launch per
-// level (events: 2 L, around each), rows of stride dp in rbuf.
-hipError_t launch_wide(const EncodeArgs &a, hipEvent_t *events, hipStream_t s);
+// The exact fp32 encoder of rows wider than the sweep holds: per level one
+// distance launch (events: 2 L, around each) over `slices` codeword slices,
+// then (slices > 1) a merge launch; rows of stride dp in rbuf.
+int wide_slices(int64_t n, int K, int num_cus);
+hipError_t launch_wide(const EncodeArgs &a, int slices, hipEvent_t *events, hipStream_t s);
 hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a, hipEvent_t *events,
                          hipStream_t s);
 

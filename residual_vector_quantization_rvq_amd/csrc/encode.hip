@@ -497,7 +497,11 @@ EncodePlan plan_encode(int64_t n, int d, int K, int num_cus) {
   cus = cus < kPlanMaxCus ? cus : kPlanMaxCus;
   // (stages == 0: rows wider than the sweep holds, for the exact fp32 encoder)
   p.fused = p.stages > 0 && (int64_t)p.row_blocks * 10 >= (int64_t)cus * 6;
-  if (p.fused || p.stages == 0) {
+  if (p.stages == 0) {
+    // wide rows: codeword slices of the exact fp32 encoder
+    p.splits = wide_slices(n, K, cus);
+    p.tiles_per_split = p.tiles;
+  } else if (p.fused) {
     p.splits = 1;
     p.tiles_per_split = p.tiles;
   } else {
@@ -561,7 +565,7 @@ hipError_t launch_encode(const EncodePlan &p, const EncodeArgs &a_in, hipEvent_t
     // rescan afterwards
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_wide(a, events, s);
+    e = launch_wide(a, p.splits, events, s);
     if (e != hipSuccess) return e;
     if (convert)
       unpad_kernel<<<dim3(row_waves), dim3(256), 0, s>>>(final_buf, a.n, a.d, a.dp,

@@ -36,7 +36,14 @@ __device__ __forceinline__ bool lex_less(float d, int i, float bd, int bi) {
   return d < bd || (d == bd && i < bi);
 }
 
-__global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level) {
+__device__ void wide_update(const EncodeArgs &a, int level, int64_t row0, const int *win);
+
+// With slices > 1 the level's codewords are split over `slices`
+// workgroups per 64-row block (slice sl takes codewords sl * slice_cw ..
+// +slice_cw - 1) and each writes its rows' (distance, index) minimum to the
+// split plan's records; wide_merge_kernel then picks each row's winner.
+__global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level, int slices,
+                                                         int slice_cw) {
   __shared__ __align__(16) float rs[kWChunk][kWRows + kWPad];  // [feature][row]
   __shared__ __align__(16) float cs[kWChunk][kWCw + kWPad];    // [feature][codeword]
   __shared__ float red_d[kWRows][16];
@@ -45,7 +52,10 @@ __global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level
 
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
-  const int64_t row0 = (int64_t)blockIdx.x * kWRows;
+  const int64_t row0 = (int64_t)(blockIdx.x / slices) * kWRows;
+  const int sl = blockIdx.x % slices;
+  const int k_begin = sl * slice_cw;
+  const int k_end = min(a.K, k_begin + slice_cw);
   const int dp = a.dp;
   const float *src = level == 0 ? a.src0 : (level & 1) ? a.rbuf[1] : a.rbuf[0];
   const float *cb_l = a.cb + (int64_t)level * a.K * dp;
@@ -63,9 +73,9 @@ __global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level
     bd[i] = __builtin_inff();
     bi[i] = 0x7fffffff;
   }
-  for (int c0 = 0; c0 < a.K; c0 += kWCw) {
+  for (int c0 = k_begin; c0 < k_end; c0 += kWCw) {
     const int lcw = c0 + lr;
-    const bool lcw_ok = lcw < a.K;
+    const bool lcw_ok = lcw < k_end;
     const float *csrc = cb_l + (int64_t)(lcw_ok ? lcw : 0) * dp + lq * 4;
     float acc[4][4];
 #pragma unroll
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = c0 + tx * 4 + j;
-      if (k < a.K) {
+      if (k < k_end) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (lex_less(acc[i][j], k, bd[i], bi[i])) {
@@ -139,16 +149,61 @@ __global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level
         d = red_d[tid][t];
         k = red_i[tid][t];
       }
-    // finite inputs always give a valid codeword
+    const int64_t row = row0 + tid;
+    if (slices > 1) {
+      if (row < a.n)
+        reinterpret_cast<int2 *>(a.part)[row * slices + sl] = make_int2(__float_as_int(d), k);
+    } else {
+      // finite inputs always give a valid codeword
+      k = (k >= 0 && k < a.K) ? k : 0;
+      win[tid] = k;
+      if (row < a.n) {
+        a.ids[row * a.L + level] = k;
+        a.aux[row * a.L + level] = kAuxOk;
+      }
+    }
+  }
+  if (slices > 1) return;
+  __syncthreads();
+  wide_update(a, level, row0, win);
+}
+
+// Each row's winner over the slices' minima ((distance, index) order), its
+// ID, and the next level's residual.
+__global__ __launch_bounds__(256) void wide_merge_kernel(EncodeArgs a, int level, int slices) {
+  __shared__ int win[kWRows];
+  const int tid = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.x * kWRows;
+  if (tid < kWRows) {
+    const int64_t row = row0 + tid;
+    float d = __builtin_inff();
+    int k = 0x7fffffff;
+    if (row < a.n) {
+      const int2 *pm = reinterpret_cast<const int2 *>(a.part) + row * slices;
+      for (int t = 0; t < slices; ++t) {
+        const int2 e = pm[t];
+        if (lex_less(__int_as_float(e.x), e.y, d, k)) {
+          d = __int_as_float(e.x);
+          k = e.y;
+        }
+      }
+    }
     k = (k >= 0 && k < a.K) ? k : 0;
     win[tid] = k;
-    const int64_t row = row0 + tid;
     if (row < a.n) {
       a.ids[row * a.L + level] = k;
       a.aux[row * a.L + level] = kAuxOk;
     }
   }
   __syncthreads();
+  wide_update(a, level, row0, win);
+}
+
+__device__ void wide_update(const EncodeArgs &a, int level, int64_t row0, const int *win) {
+  const int tid = threadIdx.x;
+  const int dp = a.dp;
+  const float *src = level == 0 ? a.src0 : (level & 1) ? a.rbuf[1] : a.rbuf[0];
+  const float *cb_l = a.cb + (int64_t)level * a.K * dp;
   // r - c of the winner, the next level's residual (rows of stride dp)
   float *dst = level == a.L - 1 ? a.res_final : (level & 1) ? a.rbuf[0] : a.rbuf[1];
   if (dst == nullptr) return;
@@ -166,14 +221,37 @@ __global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level
 
 }  // namespace
 
-hipError_t launch_wide(const EncodeArgs &a, hipEvent_t *ev, hipStream_t s) {
+int wide_slices(int64_t n, int K, int num_cus) {
+  // enough workgroups to fill the GPU twice over, in whole 64-codeword
+  // tiles, within the split plan's records (int2 per row and slice), which
+  // the workspace holds only for row counts that some device may split
+  if (n <= 0 || !split_possible(n)) return 1;
+  const int64_t blocks = ceil_div(n, kWRows);
+  const int64_t units = ceil_div((int64_t)K, kWCw);
+  int64_t want = ceil_div(2 * (int64_t)num_cus, blocks);
+  const int64_t room = split_records(n, K) * kRecF4 * 16 / (n * (int64_t)sizeof(int2));
+  want = want < units ? want : units;
+  want = want < room ? want : room;
+  if (want <= 1) return 1;
+  const int64_t per = ceil_div(units, want);
+  return (int)ceil_div(units, per);
+}
+
+hipError_t launch_wide(const EncodeArgs &a, int slices, hipEvent_t *ev, hipStream_t s) {
   hipError_t e;
-  const unsigned grid = (unsigned)ceil_div(a.n, kWRows);
+  const int64_t blocks = ceil_div(a.n, kWRows);
+  const int units = (int)ceil_div((int64_t)a.K, kWCw);
+  const int slice_cw = (int)ceil_div(units, slices) * kWCw;
   for (int l = 0; l < a.L; ++l) {
     if (ev && (e = hipEventRecord(ev[2 * l], s)) != hipSuccess) return e;
-    wide_level_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, l);
+    wide_level_kernel<<<dim3((unsigned)(blocks * slices)), dim3(256), 0, s>>>(a, l, slices,
+                                                                             slice_cw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[2 * l + 1], s)) != hipSuccess) return e;
+    if (slices > 1) {
+      wide_merge_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a, l, slices);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
