@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "RVQ-encoded vectors/sec (all levels) at D=1152,K=8192,L=8; % MFMA peak"
+PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
@@ -172,7 +173,8 @@ def secondary(torch, rvq, workloads, dev) -> dict:
     65,536-row fp32 subset encoded at L=8), the unified token embedding of a
     mixed text / visual sequence (about 40K tokens, bf16 tables of width
     4096), and the offline bulk tokenisation (1,048,576 bf16 rows of width
-    1280, L=16, K=16384; encode only)."""
+    1280, L=16, K=16384; encode only), and rows of width 2048, which the
+    exact fp32 encoder takes."""
     import numpy as np
     out = {}
     w = workloads.single_image()
@@ -311,6 +313,27 @@ def secondary(torch, rvq, workloads, dev) -> dict:
         "N": w.N, "chunk_rows": chunk, "host_rows": "pinned bf16", "ms": round(sms, 2),
         "vectors_per_s": round(w.N / (sms * 1e-3), 1),
         "device_resident_fraction": round(ms / sms, 4)}
+    # rows wider than the matrix-core sweep holds (the exact fp32 encoder,
+    # vector ALUs): a batch of the native batch's size and one image, at
+    # width 2048, random N(0, 1) bf16 rows and codebooks with 0.7^l std
+    for name, n, K in (("wide_rows_encode", 30834, 8192), ("wide_single_image_encode", 1024, 4096)):
+        d, L = 2048, 8
+        g = torch.Generator(device=dev).manual_seed(11)
+        xw = torch.randn(n, d, device=dev, generator=g).to(torch.bfloat16)
+        cbw = torch.randn(L, K, d, device=dev, generator=g)
+        cbw *= (0.7 ** torch.arange(L, device=dev, dtype=torch.float32)).view(L, 1, 1)
+        prepw = rvq.rvq_prepare_codebooks(cbw)
+        wsw = torch.empty(rvq.rvq_encode_workspace_size(n, d, L, K), dtype=torch.uint8, device=dev)
+        idw = rvq.rvq_encode(xw, cbw, prepw, workspace=wsw)
+        torch.cuda.synchronize(dev)
+        ms = _time_ms(torch, lambda: rvq.rvq_encode(xw, cbw, prepw, workspace=wsw, ids_out=idw), 3)
+        fl = 3.0 * n * K * d * L  # subtract and fused multiply-add per element
+        out[name] = {"N": n, "D": d, "K": K, "L": L, "x_dtype": "bf16", "ms": round(ms, 3),
+                     "vectors_per_s": round(n / (ms * 1e-3), 1),
+                     "fp32_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac_fp32_vector_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+        del xw, cbw, prepw, wsw, idw
+        torch.cuda.empty_cache()
     return out
 
 
