@@ -8,7 +8,8 @@ L=8 levels of K=8192 fp32 codewords):
   per-level usage counts and mean squared residual.
 Inputs are resident in HBM before the timed region.  `value` is encoded
 vectors per second for the whole step.  The distance kernel (the dense
-contraction with its top-2 epilogue) is timed per launch with HIP events
+contraction with its candidate-band epilogue, exact rescoring and residual
+update, all levels in one launch) is timed per launch with HIP events
 recorded on the library's stream, and reported against the bf16 MFMA peak.
 The fp64 oracle is timed on the host's cores on a bounded row sample.
 

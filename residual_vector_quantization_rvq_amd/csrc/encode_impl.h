@@ -1638,7 +1638,7 @@ __global__ __launch_bounds__(NT) void split_update_kernel(EncodeArgs a, int leve
   constexpr int kRow4 = S * kStageCols / 4;  // float4 capacity of a row (dp <= 64 S)
   constexpr int NV = (kRow4 + 63) / 64;      // float4 of a row per lane
   constexpr int kMaxCand = 64;
-  __shared__ float4 area[4][2][kRow4];       // per wave: r - c of two candidates
+  __shared__ float4 area[4][2][kRow4];       // per wave: r - c of the pair of candidates rescored
   __shared__ int cand[4][kMaxCand + 1];
   __shared__ int ncand[4];
   const int lane = threadIdx.x & 63;
