@@ -89,3 +89,31 @@ def test_wide_random_shapes(rvq, dev):
         except AssertionError as e:
             raise AssertionError(f"{tag}: {e}") from None
         print(f"[wide sweep] {tag}: {st['decisions']} decisions ok", flush=True)
+
+
+def test_wide_rows_through_the_streaming_and_no_allocation_encoders(rvq, dev):
+    # the streaming tokeniser (host rows in chunks) and rvq_encode_noalloc
+    # (the library's own scratch) take wide rows too, bit for bit as
+    # rvq_encode
+    import ctypes
+    n, d, L, K = 700, 2000, 3, 300
+    w = workloads.random_problem(69, n, d, L, K, x_dtype="bf16")
+    x = parity.x_to_device(w, dev)
+    cb = torch.from_numpy(w.codebooks).to(dev)
+    prep = rvq.rvq_prepare_codebooks(cb)
+    ids, res = rvq.rvq_encode(x, cb, prep, residual=True)
+    torch.cuda.synchronize()
+    host = x.cpu()
+    sids, done = rvq.rvq_stream_encode(host, cb, prep, chunk_rows=256)
+    assert done == 3
+    assert torch.equal(sids, ids.cpu())
+    ids_b = torch.full((n, L), -1, dtype=torch.int32, device=dev)
+    res_b = torch.full((n, d), float("nan"), dtype=torch.float32, device=dev)
+    st = rvq.raw_library().rvq_encode_noalloc(
+        ctypes.c_void_p(x.data_ptr()), 1, n, d, ctypes.c_void_p(cb.data_ptr()),
+        ctypes.c_void_p(prep.data_ptr()), L, K, ctypes.c_void_p(ids_b.data_ptr()),
+        ctypes.c_void_p(res_b.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0, rvq.raw_library().rvq_last_error().decode()
+    assert torch.equal(ids_b, ids)
+    assert torch.equal(res_b.view(torch.int32), res.view(torch.int32))
