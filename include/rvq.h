@@ -89,8 +89,11 @@ rvq_status rvq_prepared_size(int32_t L, int32_t K, int32_t d, size_t *bytes);
 
 /*
  * codebooks : device, [L][K][d] fp32, 16-byte aligned.
- * prepared  : device, >= rvq_prepared_size bytes, 256-byte aligned; fully
- *             overwritten.  Owned by the caller; pass it to rvq_encode with
+ * prepared  : device, >= rvq_prepared_size bytes, 256-byte aligned.  For
+ *             d <= 1280 fully overwritten; for wider rows only an fp32 copy
+ *             of the codebooks with rows padded to a multiple of 16 is
+ *             written (when d is not one), the only part the exact fp32
+ *             encoder reads.  Owned by the caller; pass it to rvq_encode with
  *             the same codebooks, L, K and d (not checked: a buffer prepared
  *             from other codebooks gives wrong IDs, never a fault).
  */
@@ -165,7 +168,7 @@ rvq_status rvq_encode(const void *x, rvq_dtype x_dtype, int64_t n, int32_t d,
  * caller-created events (hipEventCreate).  The encoder runs either one
  * launch for all levels (enough rows to fill the GPU: the launch includes
  * each level's rescoring and residual update) or one distance launch per
- * level (few rows).  events[2*i] is recorded on `stream` immediately before
+ * level (few rows, or rows wider than 1280 features).  events[2*i] is recorded on `stream` immediately before
  * and events[2*i + 1] immediately after distance launch i; `events` must
  * hold 2*L events, or be NULL to record nothing.  *launches (may be NULL)
  * receives the number of launches recorded (1 or L; 0 when n == 0).
