@@ -36,7 +36,8 @@ __device__ __forceinline__ bool lex_less(float d, int i, float bd, int bi) {
   return d < bd || (d == bd && i < bi);
 }
 
-__device__ void wide_update(const EncodeArgs &a, int level, int64_t row0, const int *win);
+__device__ void wide_update(const EncodeArgs &a, int level, int64_t row0, const int *win, int f4b,
+                            int f4e);
 
 // With slices > 1 the level's codewords are split over `slices`
 // workgroups per 64-row block (slice sl takes codewords sl * slice_cw ..
@@ -165,41 +166,60 @@ __global__ __launch_bounds__(256) void wide_level_kernel(EncodeArgs a, int level
   }
   if (slices > 1) return;
   __syncthreads();
-  wide_update(a, level, row0, win);
+  wide_update(a, level, row0, win, 0, a.dp >> 2);
 }
 
 // Each row's winner over the slices' minima ((distance, index) order), its
-// ID, and the next level's residual.
-__global__ __launch_bounds__(256) void wide_merge_kernel(EncodeArgs a, int level, int slices) {
+// ID, and the next level's residual.  Workgroup b takes the rows of block
+// b / fsplit and features (in float4) [f4b, f4e) of part b % fsplit of the
+// row; four threads share a row's minima, and part 0 writes the IDs.
+__global__ __launch_bounds__(256) void wide_merge_kernel(EncodeArgs a, int level, int slices,
+                                                         int fsplit) {
   __shared__ int win[kWRows];
   const int tid = threadIdx.x;
-  const int64_t row0 = (int64_t)blockIdx.x * kWRows;
-  if (tid < kWRows) {
-    const int64_t row = row0 + tid;
-    float d = __builtin_inff();
-    int k = 0x7fffffff;
-    if (row < a.n) {
-      const int2 *pm = reinterpret_cast<const int2 *>(a.part) + row * slices;
-      for (int t = 0; t < slices; ++t) {
-        const int2 e = pm[t];
-        if (lex_less(__int_as_float(e.x), e.y, d, k)) {
-          d = __int_as_float(e.x);
-          k = e.y;
-        }
+  const int64_t row0 = (int64_t)(blockIdx.x / fsplit) * kWRows;
+  const int fs = blockIdx.x % fsplit;
+  const int r = tid >> 2, q = tid & 3;
+  const int64_t row = row0 + r;
+  float d = __builtin_inff();
+  int k = 0x7fffffff;
+  if (row < a.n) {
+    const int2 *pm = reinterpret_cast<const int2 *>(a.part) + row * slices;
+    for (int t = q; t < slices; t += 4) {
+      const int2 e = pm[t];
+      if (lex_less(__int_as_float(e.x), e.y, d, k)) {
+        d = __int_as_float(e.x);
+        k = e.y;
       }
     }
+  }
+  // (a total order: the minimum does not depend on how it is reduced)
+#pragma unroll
+  for (int off = 1; off < 4; off <<= 1) {
+    const float od = __shfl_xor(d, off, 64);
+    const int ok = __shfl_xor(k, off, 64);
+    if (lex_less(od, ok, d, k)) {
+      d = od;
+      k = ok;
+    }
+  }
+  if (q == 0) {
     k = (k >= 0 && k < a.K) ? k : 0;
-    win[tid] = k;
-    if (row < a.n) {
+    win[r] = k;
+    if (row < a.n && fs == 0) {
       a.ids[row * a.L + level] = k;
       a.aux[row * a.L + level] = kAuxOk;
     }
   }
   __syncthreads();
-  wide_update(a, level, row0, win);
+  const int dp4 = a.dp >> 2;
+  const int per = (dp4 + fsplit - 1) / fsplit;
+  const int f4b = fs * per;
+  wide_update(a, level, row0, win, f4b, min(dp4, f4b + per));
 }
 
-__device__ void wide_update(const EncodeArgs &a, int level, int64_t row0, const int *win) {
+__device__ void wide_update(const EncodeArgs &a, int level, int64_t row0, const int *win, int f4b,
+                            int f4e) {
   const int tid = threadIdx.x;
   const int dp = a.dp;
   const float *src = level == 0 ? a.src0 : (level & 1) ? a.rbuf[1] : a.rbuf[0];
@@ -207,9 +227,9 @@ __device__ void wide_update(const EncodeArgs &a, int level, int64_t row0, const 
   // r - c of the winner, the next level's residual (rows of stride dp)
   float *dst = level == a.L - 1 ? a.res_final : (level & 1) ? a.rbuf[0] : a.rbuf[1];
   if (dst == nullptr) return;
-  const int dp4 = dp >> 2;
-  for (int e = tid; e < kWRows * dp4; e += 256) {
-    const int rr = e / dp4, f4 = e % dp4;
+  const int w4 = f4e - f4b;
+  for (int e = tid; e < kWRows * w4; e += 256) {
+    const int rr = e / w4, f4 = f4b + e % w4;
     const int64_t row = row0 + rr;
     if (row >= a.n) continue;
     const float4 r = reinterpret_cast<const float4 *>(src + row * dp)[f4];
@@ -249,7 +269,12 @@ hipError_t launch_wide(const EncodeArgs &a, int slices, hipEvent_t *ev, hipStrea
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[2 * l + 1], s)) != hipSuccess) return e;
     if (slices > 1) {
-      wide_merge_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a, l, slices);
+      // about 512 workgroups for the merge and the residual update
+      const int64_t dp4 = a.dp >> 2;
+      int64_t fsplit = ceil_div(512, blocks);
+      fsplit = fsplit < dp4 ? fsplit : dp4;
+      wide_merge_kernel<<<dim3((unsigned)(blocks * fsplit)), dim3(256), 0, s>>>(a, l, slices,
+                                                                              (int)fsplit);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
