@@ -68,9 +68,11 @@ def test_wide_duplicate_codewords_pick_the_lowest_index(rvq, dev):
 
 
 def test_wide_random_shapes(rvq, dev):
-    # random wide shapes, every row against the oracle
+    # random wide shapes, every row against the oracle (RVQ_WIDE_SHAPES sets
+    # the count, default 12)
+    import os
     g = np.random.default_rng(68)
-    for i in range(12):
+    for i in range(int(os.environ.get("RVQ_WIDE_SHAPES", "12"))):
         d = int(g.integers(1281, 4097))
         n = int(g.integers(1, 200))
         L = int(g.integers(1, 5))
