@@ -148,7 +148,8 @@ def test_native_batch(rvq, dev):
 
 def test_bulk_tokenisation_sampled(rvq, dev):
     # full size (1,048,576 x 1280 bf16, L = 16, K = 16384); 256 sampled rows
-    # (the first and last among them) against the fp64 oracle
+    # (the first and last among them; RVQ_BULK_ROWS sets another count)
+    # against the fp64 oracle
     w = workloads.bulk_tokenisation()
     x = parity.x_to_device(w, dev)
     cb = torch.from_numpy(w.codebooks).to(dev)
@@ -157,11 +158,14 @@ def test_bulk_tokenisation_sampled(rvq, dev):
     torch.cuda.synchronize()
     ids_h = ids.cpu().numpy()
     assert ids_h.min() >= 0 and ids_h.max() < w.K
+    nsel = int(os.environ.get("RVQ_BULK_ROWS", "256"))
     sel = np.unique(np.concatenate([[0, w.N - 1],
-                                    np.random.default_rng(1).choice(w.N, 254, replace=False)]))
-    sub = w.rows(sel)
-    print("[bulk_tokenisation]", len(sel), "rows",
-          parity.check_ids(ids_h[sel], sub.x, "bf16", w.codebooks))
+                                    np.random.default_rng(1).choice(w.N, nsel - 2, replace=False)]))
+    # (in chunks of 512 rows, each reported as it is checked)
+    for c0 in range(0, len(sel), 512):
+        cs = sel[c0:c0 + 512]
+        print(f"[bulk_tokenisation] rows {c0}..{c0 + len(cs) - 1} of {len(sel)}",
+              parity.check_ids(ids_h[cs], w.rows(cs).x, "bf16", w.codebooks), flush=True)
 
 
 def test_decode_heavy(rvq, dev):
