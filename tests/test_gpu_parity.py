@@ -169,6 +169,8 @@ def test_bulk_tokenisation_sampled(rvq, dev):
 
 
 def test_decode_heavy(rvq, dev):
+    # 4,000 sampled rows and the hot rows of the 4,194,304-row bf16 decode
+    # (RVQ_DECODE_ROWS=all: every row), the full counts, and the msr subset
     w = workloads.decode_heavy()
     cb = torch.from_numpy(w.codebooks).to(dev)
     ids = torch.from_numpy(w.ids).to(dev)
@@ -178,11 +180,22 @@ def test_decode_heavy(rvq, dev):
     torch.cuda.synchronize()
     assert int(bad.item()) == 0
     np.testing.assert_array_equal(hist.cpu().numpy(), oracle.hist(w.ids, w.K))
-    hot = np.where((w.ids == 0).all(axis=1))[0][:64]
-    sel = np.unique(np.concatenate([hot, np.random.default_rng(2).choice(len(w.ids), 4000, replace=False),
-                                    [len(w.ids) - 1]]))
-    got = parity.bf16_tensor_bits(out[torch.from_numpy(sel).to(dev)])
-    parity.check_decode_bf16(got, w.ids[sel], w.codebooks)
+    if os.environ.get("RVQ_DECODE_ROWS") == "all":
+        # every row, in chunks of 262,144 rows, each reported as it is checked
+        nid = len(w.ids)
+        for r0 in range(0, nid, 1 << 18):
+            r1 = min(nid, r0 + (1 << 18))
+            diffs = parity.check_decode_bf16(parity.bf16_tensor_bits(out[r0:r1]), w.ids[r0:r1],
+                                             w.codebooks)
+            print(f"[decode_heavy] rows {r0}..{r1 - 1} of {nid}: {diffs} elements off the "
+                  f"rounded fp64 sum, all within the bound", flush=True)
+    else:
+        hot = np.where((w.ids == 0).all(axis=1))[0][:64]
+        sel = np.unique(np.concatenate([hot, np.random.default_rng(2).choice(len(w.ids), 4000,
+                                                                             replace=False),
+                                        [len(w.ids) - 1]]))
+        got = parity.bf16_tensor_bits(out[torch.from_numpy(sel).to(dev)])
+        parity.check_decode_bf16(got, w.ids[sel], w.codebooks)
     # statistics subset: encode at L=8, then msr along the GPU's IDs
     x = parity.x_to_device(w, dev)
     sids = rvq.rvq_encode(x, cb)
