@@ -107,6 +107,12 @@ def test_encode_workspace_size(rvq):
     assert rvq.rvq_encode_workspace_size(n, 1152, 8, 8192) == (
         2 * al(30848 * 1152 * 4) + al(n * 8 * 4) + al(n * 9 * 2 * 7 * 16) + al(30848 * 1152 * 2)
         + al(n * 8))
+    # rows wider than 1280 features use the same layout (the exact fp32
+    # encoder keeps its codeword-slice minima in the split plan's records)
+    n, d, L, K = 1000, 2048, 4, 256
+    assert rvq.rvq_encode_workspace_size(n, d, L, K) == (
+        2 * al(1024 * 2048 * 4) + al(n * L * 4) + al(n * 2 * 2 * 7 * 16) + al(1024 * 2048 * 2)
+        + al(n * 8))
     # 80,000 rows fill any device: no split-plan buffers
     assert rvq.rvq_encode_workspace_size(80000, 1280, 16, 16384) == (
         2 * al(80000 * 1280 * 4) + al(80000 * 16 * 4))
